@@ -1,0 +1,350 @@
+/*
+ * gdn_oracle.c - plain C99 CPU oracle (TEST INFRASTRUCTURE ONLY; see
+ * gdn_oracle.h for the sources, the layouts and who may call this).
+ *
+ * Written to be read against the pages, not to be fast: one loop per printed
+ * step, sequential binary32 sums, a separate multiply and add (the build uses
+ * -ffp-contract=off), libm expf/sqrtf.
+ */
+#include "gdn_oracle.h"
+
+#include <math.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+
+/*
+ * One value head, one token, transposed state M[j][i] = S[i][j]
+ * ([dev15c] "Pinned llama.cpp semantics"):
+ *   1. M *= exp(gate)
+ *   2. sk[j]    = dot(M[j], k)            (uses the decayed M)
+ *   3. delta[j] = (v[j] - sk[j]) * beta
+ *   4. M[j][i] += delta[j] * k[i]
+ *   5. out[j]   = dot(M[j], q) / sqrt(dk) (uses the updated M)
+ * The page writes sqrt(128) with 128 the state/key dimension; dk is that
+ * dimension, generalised only so tiny heads can be brute-forced.
+ */
+static void head_step_M(int32_t dk, int32_t dv,
+                        const float *q, const float *k, const float *v,
+                        float beta, float gate, float *M, float *out,
+                        float *delta)
+{
+    const float e = expf(gate);
+    const float scale = sqrtf((float)dk);
+    int32_t i, j;
+
+    /* step 1: decay */
+    for (j = 0; j < dv; ++j)
+        for (i = 0; i < dk; ++i)
+            M[(size_t)j * dk + i] = M[(size_t)j * dk + i] * e;
+
+    for (j = 0; j < dv; ++j) {
+        float *row = M + (size_t)j * dk;
+        float sk = 0.0f;
+        float d;
+        /* step 2: sk[j] = M[j] . k */
+        for (i = 0; i < dk; ++i)
+            sk = sk + row[i] * k[i];
+        /* step 3: delta */
+        d = (v[j] - sk) * beta;
+        if (delta)
+            delta[j] = d;
+        /* step 4: rank-1 update of row j */
+        for (i = 0; i < dk; ++i)
+            row[i] = row[i] + d * k[i];
+    }
+
+    /* step 5: output from the updated state */
+    for (j = 0; j < dv; ++j) {
+        const float *row = M + (size_t)j * dk;
+        float s = 0.0f;
+        for (i = 0; i < dk; ++i)
+            s = s + row[i] * q[i];
+        out[j] = s / scale;
+    }
+}
+
+/* Value head h reads Q/K of key head h % Hk: the page lists the broadcast as
+ * value_head % key_heads, i.e. key heads 0..15 then 0..15 again. */
+static int32_t key_head_of(int32_t h, int32_t Hk) { return h % Hk; }
+
+void oracle_gdn_step_M(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv,
+                       const float *q, const float *k, const float *v,
+                       const float *beta, const float *gate,
+                       float *M, float *out, float *delta)
+{
+    int32_t b, h;
+    for (b = 0; b < B; ++b) {
+        for (h = 0; h < Hv; ++h) {
+            const int32_t kh = key_head_of(h, Hk);
+            const size_t bh = (size_t)b * Hv + h;
+            head_step_M(dk, dv,
+                        q + ((size_t)b * Hk + kh) * dk,
+                        k + ((size_t)b * Hk + kh) * dk,
+                        v + bh * dv,
+                        beta[bh], gate[bh],
+                        M + bh * dv * dk,
+                        out + bh * dv,
+                        delta ? delta + bh * dv : NULL);
+        }
+    }
+}
+
+/*
+ * The same update on the non-transposed state S[i][j] (i = key dim,
+ * j = value dim), which the transposed layout M[j][i] = S[i][j] stores:
+ *   S *= e;  sk = S^T k;  delta = (v - sk) beta;  S += k delta^T;
+ *   out = S^T q / sqrt(dk).
+ */
+static void head_step_S(int32_t dk, int32_t dv,
+                        const float *q, const float *k, const float *v,
+                        float beta, float gate, float *S, float *out,
+                        float *delta)
+{
+    const float e = expf(gate);
+    const float scale = sqrtf((float)dk);
+    float *d = (float *)malloc((size_t)dv * sizeof(float));
+    int32_t i, j;
+
+    for (i = 0; i < dk; ++i)
+        for (j = 0; j < dv; ++j)
+            S[(size_t)i * dv + j] = S[(size_t)i * dv + j] * e;
+
+    for (j = 0; j < dv; ++j) {
+        float sk = 0.0f;
+        for (i = 0; i < dk; ++i)
+            sk = sk + S[(size_t)i * dv + j] * k[i];
+        d[j] = (v[j] - sk) * beta;
+        if (delta)
+            delta[j] = d[j];
+    }
+
+    for (i = 0; i < dk; ++i)
+        for (j = 0; j < dv; ++j)
+            S[(size_t)i * dv + j] = S[(size_t)i * dv + j] + k[i] * d[j];
+
+    for (j = 0; j < dv; ++j) {
+        float s = 0.0f;
+        for (i = 0; i < dk; ++i)
+            s = s + S[(size_t)i * dv + j] * q[i];
+        out[j] = s / scale;
+    }
+    free(d);
+}
+
+void oracle_gdn_step_S(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv,
+                       const float *q, const float *k, const float *v,
+                       const float *beta, const float *gate,
+                       float *S, float *out, float *delta)
+{
+    int32_t b, h;
+    for (b = 0; b < B; ++b) {
+        for (h = 0; h < Hv; ++h) {
+            const int32_t kh = key_head_of(h, Hk);
+            const size_t bh = (size_t)b * Hv + h;
+            head_step_S(dk, dv,
+                        q + ((size_t)b * Hk + kh) * dk,
+                        k + ((size_t)b * Hk + kh) * dk,
+                        v + bh * dv,
+                        beta[bh], gate[bh],
+                        S + bh * dk * dv,
+                        out + bh * dv,
+                        delta ? delta + bh * dv : NULL);
+        }
+    }
+}
+
+/* Binary64 shadow of head_step_M. */
+static void head_step_f64(int32_t dk, int32_t dv,
+                          const float *q, const float *k, const float *v,
+                          float beta, float gate, double *M, double *out)
+{
+    const double e = exp((double)gate);
+    const double scale = sqrt((double)dk);
+    int32_t i, j;
+
+    for (j = 0; j < dv; ++j)
+        for (i = 0; i < dk; ++i)
+            M[(size_t)j * dk + i] = M[(size_t)j * dk + i] * e;
+
+    for (j = 0; j < dv; ++j) {
+        double *row = M + (size_t)j * dk;
+        double sk = 0.0, d;
+        for (i = 0; i < dk; ++i)
+            sk = sk + row[i] * (double)k[i];
+        d = ((double)v[j] - sk) * (double)beta;
+        for (i = 0; i < dk; ++i)
+            row[i] = row[i] + d * (double)k[i];
+    }
+
+    for (j = 0; j < dv; ++j) {
+        const double *row = M + (size_t)j * dk;
+        double s = 0.0;
+        for (i = 0; i < dk; ++i)
+            s = s + row[i] * (double)q[i];
+        out[j] = s / scale;
+    }
+}
+
+void oracle_gdn_step_f64(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv,
+                         const float *q, const float *k, const float *v,
+                         const float *beta, const float *gate,
+                         double *M, double *out)
+{
+    int32_t b, h;
+    for (b = 0; b < B; ++b) {
+        for (h = 0; h < Hv; ++h) {
+            const int32_t kh = key_head_of(h, Hk);
+            const size_t bh = (size_t)b * Hv + h;
+            head_step_f64(dk, dv,
+                          q + ((size_t)b * Hk + kh) * dk,
+                          k + ((size_t)b * Hk + kh) * dk,
+                          v + bh * dv,
+                          beta[bh], gate[bh],
+                          M + bh * dv * dk,
+                          out + bh * dv);
+        }
+    }
+}
+
+/* [linear_core] the batch path walks the positions in order; each position
+ * is one single-token step on the carried state. */
+void oracle_gdn_seq(int32_t B, int32_t T, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv,
+                    const float *q, const float *k, const float *v,
+                    const float *beta, const float *gate,
+                    float *M, float *out)
+{
+    int32_t b, t, h;
+    for (b = 0; b < B; ++b) {
+        for (t = 0; t < T; ++t) {
+            const size_t bt = (size_t)b * T + t;
+            for (h = 0; h < Hv; ++h) {
+                const int32_t kh = key_head_of(h, Hk);
+                head_step_M(dk, dv,
+                            q + (bt * Hk + kh) * dk,
+                            k + (bt * Hk + kh) * dk,
+                            v + (bt * Hv + h) * dv,
+                            beta[bt * Hv + h], gate[bt * Hv + h],
+                            M + ((size_t)b * Hv + h) * dv * dk,
+                            out + (bt * Hv + h) * dv,
+                            NULL);
+            }
+        }
+    }
+}
+
+static float silu(float x) { return x / (1.0f + expf(-x)); }
+
+/*
+ * [dev15a] conv-state shift + causal conv1d + SiLU, one token.  The window
+ * of channel c is [cache slot 0 .. slot K-2, x] (oldest first); tap t of the
+ * weight multiplies window element t; there is no bias.  Afterwards the
+ * cache holds the last K-1 raw inputs (the new x in the last slot).
+ */
+void oracle_conv_silu(int32_t B, int32_t C, int32_t K,
+                      const float *x, const float *conv_w, float *conv_state,
+                      float *act)
+{
+    float *win = (float *)malloc((size_t)K * sizeof(float));
+    int32_t b, c, t;
+    for (b = 0; b < B; ++b) {
+        float *cs = conv_state + (size_t)b * (K - 1) * C;
+        for (c = 0; c < C; ++c) {
+            float acc = 0.0f;
+            for (t = 0; t < K - 1; ++t)
+                win[t] = cs[(size_t)t * C + c];
+            win[K - 1] = x[(size_t)b * C + c];
+            for (t = 0; t < K; ++t)
+                acc = acc + conv_w[(size_t)c * K + t] * win[t];
+            for (t = 0; t < K - 1; ++t)
+                cs[(size_t)t * C + c] = win[t + 1];
+            act[(size_t)b * C + c] = silu(acc);
+        }
+    }
+    free(win);
+}
+
+void oracle_l2norm_rows(int32_t n, int32_t d, float *u)
+{
+    int32_t r, i;
+    for (r = 0; r < n; ++r) {
+        float *row = u + (size_t)r * d;
+        float ss = 0.0f, nrm;
+        for (i = 0; i < d; ++i)
+            ss = ss + row[i] * row[i];
+        nrm = sqrtf(ss);
+        if (nrm < 1e-6f)
+            nrm = 1e-6f;
+        for (i = 0; i < d; ++i)
+            row[i] = row[i] / nrm;
+    }
+}
+
+void oracle_gated_rmsnorm(int32_t rows, int32_t n, int32_t group, float eps,
+                          const float *o, const float *z, const float *w,
+                          float *y)
+{
+    int32_t r, g, i;
+    for (r = 0; r < rows; ++r) {
+        for (g = 0; g < n; g += group) {
+            const size_t base = (size_t)r * n + g;
+            float ss = 0.0f, rms;
+            for (i = 0; i < group; ++i)
+                ss = ss + o[base + i] * o[base + i];
+            rms = sqrtf(ss / (float)group + eps);
+            for (i = 0; i < group; ++i)
+                y[base + i] = (o[base + i] / rms) * w[i] * silu(z[base + i]);
+        }
+    }
+}
+
+void oracle_layer_tail(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv,
+                       int32_t K, int32_t group, float eps,
+                       const float *x, const float *conv_w, float *conv_state,
+                       const float *beta, const float *gate, float *M,
+                       const float *z, const float *norm_w, float *y,
+                       float *qkv_out, float *core_out)
+{
+    const int32_t nq = Hk * dk, nv = Hv * dv;
+    const int32_t C = 2 * nq + nv;
+    float *act = (float *)malloc((size_t)B * C * sizeof(float));
+    float *q = (float *)malloc((size_t)B * nq * sizeof(float));
+    float *k = (float *)malloc((size_t)B * nq * sizeof(float));
+    float *v = (float *)malloc((size_t)B * nv * sizeof(float));
+    float *o = (float *)malloc((size_t)B * nv * sizeof(float));
+    int32_t b;
+
+    /* conv-state shift, conv1d, SiLU */
+    oracle_conv_silu(B, C, K, x, conv_w, conv_state, act);
+
+    /* Q/K/V split, [Q | K | V], then per-head L2 of Q and K */
+    for (b = 0; b < B; ++b) {
+        memcpy(q + (size_t)b * nq, act + (size_t)b * C, (size_t)nq * sizeof(float));
+        memcpy(k + (size_t)b * nq, act + (size_t)b * C + nq, (size_t)nq * sizeof(float));
+        memcpy(v + (size_t)b * nv, act + (size_t)b * C + 2 * nq, (size_t)nv * sizeof(float));
+    }
+    oracle_l2norm_rows(B * Hk, dk, q);
+    oracle_l2norm_rows(B * Hk, dk, k);
+
+    if (qkv_out) {
+        for (b = 0; b < B; ++b) {
+            memcpy(qkv_out + (size_t)b * C, q + (size_t)b * nq, (size_t)nq * sizeof(float));
+            memcpy(qkv_out + (size_t)b * C + nq, k + (size_t)b * nq, (size_t)nq * sizeof(float));
+            memcpy(qkv_out + (size_t)b * C + 2 * nq, v + (size_t)b * nv, (size_t)nv * sizeof(float));
+        }
+    }
+
+    /* the recurrent state step */
+    oracle_gdn_step_M(B, Hv, Hk, dk, dv, q, k, v, beta, gate, M, o, NULL);
+    if (core_out)
+        memcpy(core_out, o, (size_t)B * nv * sizeof(float));
+
+    /* gated RMSNorm x SiLU(z) */
+    oracle_gated_rmsnorm(B, nv, group, eps, o, z, norm_w, y);
+
+    free(act);
+    free(q);
+    free(k);
+    free(v);
+    free(o);
+}

@@ -1,0 +1,82 @@
+"""CPU: plausible mistakes planted in a copy of the oracle source must each
+trip at least one pin.  This shows the pins are strong enough to catch a
+dropped term, a wrong sign, index, order or operand in the oracle.
+
+Mistakes are planted in a temporary copy only; the real oracle is untouched.
+Each mutant runs in its own process so a bad mutant cannot take pytest down.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+# (name, original text, planted text): the first occurrence is replaced.
+MUTANTS = [
+    ("delta_sign", "d = (v[j] - sk) * beta;", "d = (sk - v[j]) * beta;"),
+    ("beta_dropped", "d = (v[j] - sk) * beta;", "d = (v[j] - sk);"),
+    ("rank1_update_dropped", "row[i] = row[i] + d * k[i];", "row[i] = row[i] + 0.0f * d * k[i];"),
+    ("decay_dropped", "M[(size_t)j * dk + i] = M[(size_t)j * dk + i] * e;",
+     "M[(size_t)j * dk + i] = M[(size_t)j * dk + i];"),
+    ("decay_squared", "const float e = expf(gate);", "const float e = expf(2.0f * gate);"),
+    ("sk_transposed_operand", "sk = sk + row[i] * k[i];", "sk = sk + M[(size_t)i * dk + j] * k[i];"),
+    ("out_uses_k", "s = s + row[i] * q[i];", "s = s + row[i] * k[i];"),
+    ("out_unscaled", "out[j] = s / scale;", "out[j] = s;"),
+    ("out_scale_dv", "const float scale = sqrtf((float)dk);", "const float scale = sqrtf((float)(dk + 1));"),
+    ("head_map_interleaved", "static int32_t key_head_of(int32_t h, int32_t Hk) { return h % Hk; }",
+     "static int32_t key_head_of(int32_t h, int32_t Hk) { return (h / 2) % Hk; }"),
+    ("seq_wrong_token_stride", "q + (bt * Hk + kh) * dk,", "q + ((size_t)b * Hk + kh) * dk,"),
+    ("conv_taps_reversed", "acc = acc + conv_w[(size_t)c * K + t] * win[t];",
+     "acc = acc + conv_w[(size_t)c * K + (K - 1 - t)] * win[t];"),
+    ("conv_cache_not_shifted", "cs[(size_t)t * C + c] = win[t + 1];", "cs[(size_t)t * C + c] = win[t];"),
+    ("silu_sign", "return x / (1.0f + expf(-x));", "return x / (1.0f + expf(x));"),
+    ("l2_without_sqrt", "nrm = sqrtf(ss);", "nrm = ss;"),
+    ("rms_weight_index", "* w[i] *", "* w[0] *"),
+    ("rms_eps_outside_sqrt", "rms = sqrtf(ss / (float)group + eps);", "rms = sqrtf(ss / (float)group) + eps;"),
+    ("rms_mean_over_wrong_n", "rms = sqrtf(ss / (float)group + eps);", "rms = sqrtf(ss / (float)n + eps);"),
+    ("tail_split_q_from_k", "memcpy(q + (size_t)b * nq, act + (size_t)b * C, ",
+     "memcpy(q + (size_t)b * nq, act + (size_t)b * C + nq, "),
+    ("tail_k_not_normalized", "oracle_l2norm_rows(B * Hk, dk, k);", ";"),
+]
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle.SOURCE) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, source, name, old, new):
+    assert old in source, f"mutation site for {name} not found"
+    src = tmp_path / "gdn_oracle.c"
+    src.write_text(source.replace(old, new, 1))
+    hdr = os.path.join(os.path.dirname(oracle.SOURCE), "gdn_oracle.h")
+    (tmp_path / "gdn_oracle.h").write_text(open(hdr).read())
+    lib = str(tmp_path / "liboracle_mutant.so")
+    subprocess.run(["gcc", *oracle.CFLAGS, "-w", str(src), "-o", lib, "-lm"], check=True)
+    here = os.path.dirname(os.path.abspath(__file__))
+    r = subprocess.run([sys.executable, os.path.join(here, "pins.py"), lib],
+                       capture_output=True, text=True, timeout=300,
+                       env={**os.environ, "PYTHONPATH": os.pathsep.join(
+                           [os.path.dirname(here), here, os.environ.get("PYTHONPATH", "")])})
+    assert r.returncode == 1 and "FAIL" in r.stdout, \
+        f"planted mistake {name} not caught (rc={r.returncode}):\n{r.stdout}\n{r.stderr}"
+
+
+def test_unmodified_copy_passes(tmp_path, source):
+    """Control: the same harness on an unmodified copy reports no failure."""
+    src = tmp_path / "gdn_oracle.c"
+    src.write_text(source)
+    hdr = os.path.join(os.path.dirname(oracle.SOURCE), "gdn_oracle.h")
+    (tmp_path / "gdn_oracle.h").write_text(open(hdr).read())
+    lib = str(tmp_path / "liboracle_copy.so")
+    subprocess.run(["gcc", *oracle.CFLAGS, str(src), "-o", lib, "-lm"], check=True)
+    here = os.path.dirname(os.path.abspath(__file__))
+    r = subprocess.run([sys.executable, os.path.join(here, "pins.py"), lib],
+                       capture_output=True, text=True, timeout=300,
+                       env={**os.environ, "PYTHONPATH": os.pathsep.join(
+                           [os.path.dirname(here), here, os.environ.get("PYTHONPATH", "")])})
+    assert r.returncode == 0, r.stdout + r.stderr
