@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet decode step on one MI355X.
+
+Workload (one "step"): B=256 sequences x 36 recurrent layers, one token per
+layer: 36 gdn_step calls in layer order on one stream, each on its own
+[256][32][128][128] float32 state (512 MiB; 18 GiB in all), with fresh seeded
+inputs per layer.  Inputs and states are resident in HBM before timing starts.
+
+Printed: ONE JSON line with the headline metric (state-updates/s, one update =
+one 128x128 head state advanced by one token), the roofline of the gdn_step
+kernel (algorithmic bytes per launch / mean launch time from HIP events on the
+launch stream), the plain C oracle timed on the host on a bounded sample, and
+secondary measurements of the other entry points.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+import gdn_inputs as gi  # noqa: E402
+
+HV, HK, D = gi.HV, gi.HK, gi.D
+# Algorithmic bytes of one state-update of gdn_step: the 64 KiB state read and
+# written, v and out (512 B each), half of the shared q and k of the key head
+# (512 B), beta and gate (8 B).
+STATE_UPDATE_BYTES = 2 * D * D * 4 + 2 * D * 4 + (2 * D * 4) // 2 + 8   # 132616
+HBM_PEAK_GBPS = 8000.0
+METRIC = "GDN state-updates/s (seq·head·token) and achieved HBM GB/s, B=256 decode"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true", help="skip the secondary entry points")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def setup_config2(torch, g):
+    c = gi.CONFIGS[2]
+    B, L, seed = c["B"], c["layers"], c["seed"]
+    log(f"[bench] generating {L} x {B} x {HV} x {D}x{D} f32 states (seeded) ...")
+    states = torch.empty((L, B, HV, D, D), device="cuda")
+    stage = torch.empty((B, HV, D, D), pin_memory=True)
+    sn = stage.numpy()
+    ins = []
+    for l in range(L):
+        gi.state_into(sn, seed, l)
+        states[l].copy_(stage)
+        si = gi.step_inputs(seed, l, B)
+        ins.append({n: torch.from_numpy(x).cuda() for n, x in si.items()})
+        torch.cuda.synchronize()
+    outs = torch.empty((L, B, HV, D), device="cuda")
+    return dict(B=B, L=L, states=states, ins=ins, outs=outs)
+
+
+def run_step36(g, w, stream, evs=None):
+    for l in range(w["L"]):
+        t = w["ins"][l]
+        if evs is not None:
+            evs[l][0].record(stream)
+        g.step(t["q"], t["k"], t["v"], t["beta"], t["gate"], w["states"][l], w["outs"][l],
+               stream=stream)
+        if evs is not None:
+            evs[l][1].record(stream)
+
+
+def cpu_baseline(seconds):
+    """The oracle as it is, on the host cores, over config-2 layers (B=256)
+    stepped round-robin until `seconds` have passed."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    o = oracle.get()
+    c = gi.CONFIGS[2]
+    B, seed, n_layers = c["B"], c["seed"], 4
+    threads = max(1, min(16, os.cpu_count() or 1))
+    states = [gi.state(seed, l, B) for l in range(n_layers)]
+    ins = [gi.step_inputs(seed, l, B) for l in range(n_layers)]
+    bounds = np.linspace(0, B, threads + 1).astype(int)
+
+    def layer(l):
+        def part(i):
+            a, b = bounds[i], bounds[i + 1]
+            si = {n: np.ascontiguousarray(x[a:b]) for n, x in ins[l].items()}
+            M = np.ascontiguousarray(states[l][a:b])
+            o.step_M(si["q"], si["k"], si["v"], si["beta"], si["gate"], M)
+            states[l][a:b] = M
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(part, range(threads)))
+
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        layer(done % n_layers)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or done >= 360:
+            break
+    updates = done * B * HV
+    return {"value": updates / el, "unit": "state-updates/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} layer-steps of configuration 2 (B=256, 32 heads; layers 0-"
+                      f"{n_layers - 1} stepped round-robin), oracle_gdn_step_M split over "
+                      f"{threads} host threads by sequence, {el:.1f} s",
+            "GBps": updates * STATE_UPDATE_BYTES / el / 1e9}
+
+
+def extra_measurements(torch, g, stream):
+    """Secondary entry points, timed with events on the launch stream."""
+    res = {}
+
+    def timeit(fn, reps):
+        for _ in range(2):
+            fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record(stream)
+        for _ in range(reps):
+            fn()
+        e.record(stream)
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+
+    # config 0: B=1 single step (latency-bound)
+    si = {n: torch.from_numpy(x).cuda() for n, x in gi.step_inputs(1000, 0, 1).items()}
+    M = torch.from_numpy(gi.state(1000, 0, 1)).cuda()
+    o = torch.empty((1, HV, D), device="cuda")
+    ms = timeit(lambda: g.step(si["q"], si["k"], si["v"], si["beta"], si["gate"], M, o,
+                               stream=stream), 1000)
+    res["config0_step_b1"] = {"us_per_call": ms * 1e3, "state_updates_per_s": 32 / (ms / 1e3)}
+
+    # config 1: B=64 decode, 100 calls with fresh inputs
+    c1 = gi.CONFIGS[1]
+    M = torch.from_numpy(gi.state(c1["seed"], 0, 64)).cuda()
+    ins = [{n: torch.from_numpy(x).cuda() for n, x in gi.step_inputs(c1["seed"], i, 64).items()}
+           for i in range(100)]
+    o = torch.empty((64, HV, D), device="cuda")
+
+    def c1run():
+        for t in ins:
+            g.step(t["q"], t["k"], t["v"], t["beta"], t["gate"], M, o, stream=stream)
+    ms = timeit(c1run, 3)
+    upd = 100 * 64 * HV
+    res["config1_step_b64_x100"] = {"ms": ms, "state_updates_per_s": upd / (ms / 1e3),
+                                    "GBps": upd * STATE_UPDATE_BYTES / (ms / 1e3) / 1e9,
+                                    "note": "128 MiB state fits the 256 MB Infinity Cache"}
+
+    # config 3: gdn_seq B=8 x T=4096 from a zero state
+    c3 = gi.CONFIGS[3]
+    si = {n: torch.from_numpy(x).cuda() for n, x in gi.step_inputs(c3["seed"], 0, 8, T=4096).items()}
+    M = torch.zeros((8, HV, D, D), device="cuda")
+    o = torch.empty((8, 4096, HV, D), device="cuda")
+    ms = timeit(lambda: g.seq(si["q"], si["k"], si["v"], si["beta"], si["gate"], M, o,
+                              stream=stream), 5)
+    upd = 8 * 4096 * HV
+    flops = upd * D * D * 7  # decay mul + 3 FMA per element
+    res["config3_seq_b8_t4096"] = {"ms": ms, "state_updates_per_s": upd / (ms / 1e3),
+                                   "TFLOPs": flops / (ms / 1e3) / 1e12,
+                                   "frac_fp32_vector_nonpacked_78.6": flops / (ms / 1e3) / 78.6e12}
+
+    # config 4: layer tail B=32
+    c4 = gi.CONFIGS[4]
+    ti = {n: torch.from_numpy(x).cuda() for n, x in gi.tail_inputs(c4["seed"], 32).items()}
+    M = torch.from_numpy(gi.state(c4["seed"], 0, 32)).cuda()
+    y = torch.empty((32, HV * D), device="cuda")
+    ws = torch.empty(g.layer_tail_workspace_bytes(32), dtype=torch.uint8, device="cuda")
+    ms = timeit(lambda: g.layer_tail(ti["x"], ti["conv_w"], ti["conv_state"], ti["beta"],
+                                     ti["gate"], M, ti["z"], ti["norm_w"], y, workspace=ws,
+                                     stream=stream), 200)
+    res["config4_layer_tail_b32"] = {"us_per_call": ms * 1e3,
+                                     "state_updates_per_s": 32 * HV / (ms / 1e3)}
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+              "the decode step has no cross-GPU exchange and shards by sequence", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gated_deltanet_decode_amd as g
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    w = setup_config2(torch, g)
+    stream = torch.cuda.current_stream()
+    L, B = w["L"], w["B"]
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        run_step36(g, w, stream)
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps x {L} gdn_step launches")
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in range(L)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(args.steps):
+        run_step36(g, w, stream, evs[s])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    launch_ms = [evs[s][l][0].elapsed_time(evs[s][l][1]) for s in range(args.steps) for l in range(L)]
+    avg_launch_ms = float(np.mean(launch_ms))
+
+    updates_per_step = L * B * HV
+    ms_per_step = ms_total / args.steps
+    value = updates_per_step / (ms_per_step / 1e3)
+    bytes_per_launch = B * HV * STATE_UPDATE_BYTES
+    achieved = bytes_per_launch / (avg_launch_ms / 1e3) / 1e9
+    log(f"[bench] {ms_per_step:.3f} ms/step (wall {wall / args.steps * 1e3:.3f}), "
+        f"launch mean {avg_launch_ms * 1e3:.1f} us min {min(launch_ms) * 1e3:.1f} "
+        f"max {max(launch_ms) * 1e3:.1f}; {achieved:.0f} GB/s")
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "state-updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "gdn_step decode, B=256 sequences x 36 layers (one 512 MiB "
+                               "state per layer, 18 GiB), 32 value / 16 key heads, d=128, "
+                               "one token per layer",
+                   "global_batch": B, "layers": L, "launches_per_step": L,
+                   "seed": gi.CONFIGS[2]["seed"]},
+        "achieved_GBps_step": updates_per_step * STATE_UPDATE_BYTES / (ms_per_step / 1e3) / 1e9,
+        "roofline": {"bound": "hbm", "kernel": "k_step (gdn_step)", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None,
+                     "bytes_per_launch": bytes_per_launch,
+                     "avg_launch_us": avg_launch_ms * 1e3},
+    }
+    if not args.no_extra:
+        log("[bench] secondary entry points")
+        del w
+        torch.cuda.empty_cache()
+        line["extra"] = extra_measurements(torch, g, stream)
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU baseline (oracle, ~{args.cpu_seconds:.0f} s)")
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,179 @@
+"""Python binding of libgdn.so (the C ABI in include/gdn.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  PyTorch provides device memory and streams.  The names mirror the
+C entry points:
+
+    step(q, k, v, beta, gate, state, out)        -> gdn_step
+    seq(q, k, v, beta, gate, state, out)         -> gdn_seq
+    layer_tail(x, conv_w, conv_state, beta, gate, state, z, norm_w, y, ...)
+                                                 -> gdn_layer_tail
+    layer_tail_workspace_bytes(B)                -> gdn_layer_tail_workspace_bytes
+    last_error(), version()
+
+If the library has not been built, importing this package raises: there is
+no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from ._build import LIBRARY
+
+__all__ = ["GdnError", "Dims", "TailParams", "lib", "step", "seq", "layer_tail",
+           "layer_tail_workspace_bytes", "last_error", "version", "PAGE_DIMS",
+           "PAGE_TAIL", "ERRORS"]
+
+if not os.path.exists(LIBRARY):
+    raise ImportError(f"{LIBRARY} is not built; run __graft_entry__.build() "
+                      "(hipcc --offload-arch=gfx950) first")
+
+
+class Dims(ctypes.Structure):
+    """gdn_dims"""
+    _fields_ = [("n_v_heads", ctypes.c_int32), ("n_k_heads", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32)]
+
+
+class TailParams(ctypes.Structure):
+    """gdn_tail_params"""
+    _fields_ = [("conv_kernel", ctypes.c_int32), ("norm_group", ctypes.c_int32),
+                ("norm_eps", ctypes.c_float)]
+
+
+PAGE_DIMS = Dims(32, 16, 128, 128)
+PAGE_TAIL = TailParams(4, 128, 1e-6)
+
+ERRORS = {0: "GDN_OK", -1: "GDN_ERR_NULL", -2: "GDN_ERR_SHAPE", -3: "GDN_ERR_ALIGN",
+          -4: "GDN_ERR_ALIAS", -5: "GDN_ERR_WORKSPACE", -6: "GDN_ERR_HIP"}
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_DP = ctypes.POINTER(Dims)
+_TP = ctypes.POINTER(TailParams)
+
+lib = ctypes.CDLL(LIBRARY)
+lib.gdn_version.restype = ctypes.c_int
+lib.gdn_version.argtypes = []
+lib.gdn_last_error.restype = ctypes.c_char_p
+lib.gdn_last_error.argtypes = []
+lib.gdn_step.restype = ctypes.c_int
+lib.gdn_step.argtypes = [_DP, _i32] + [_vp] * 7 + [_vp]
+lib.gdn_seq.restype = ctypes.c_int
+lib.gdn_seq.argtypes = [_DP, _i32, _i32] + [_vp] * 7 + [_vp]
+lib.gdn_layer_tail.restype = ctypes.c_int
+lib.gdn_layer_tail.argtypes = [_DP, _TP, _i32] + [_vp] * 11 + [_vp, ctypes.c_size_t, _vp]
+lib.gdn_layer_tail_workspace_bytes.restype = ctypes.c_size_t
+lib.gdn_layer_tail_workspace_bytes.argtypes = [_DP, _i32]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {message}")
+        self.code = code
+
+
+def version() -> int:
+    return lib.gdn_version()
+
+
+def last_error() -> str:
+    return lib.gdn_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise GdnError(rc, last_error())
+
+
+def _ptr(t, name, shape=None, optional=False):
+    import torch
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dims_of(q, v):
+    Hk, dk = q.shape[-2], q.shape[-1]
+    Hv, dv = v.shape[-2], v.shape[-1]
+    return Dims(Hv, Hk, dk, dv)
+
+
+def step(q, k, v, beta, gate, state, out, stream=None) -> None:
+    """gdn_step: q,k [B][Hk][dk], v [B][Hv][dv], beta/gate [B][Hv],
+    state [B][Hv][dv][dk] (updated in place), out [B][Hv][dv]."""
+    B = q.shape[0]
+    d = _dims_of(q, v)
+    _check(lib.gdn_step(
+        ctypes.byref(d), B,
+        _ptr(q, "q", (B, d.n_k_heads, d.d_k)), _ptr(k, "k", (B, d.n_k_heads, d.d_k)),
+        _ptr(v, "v", (B, d.n_v_heads, d.d_v)),
+        _ptr(beta, "beta", (B, d.n_v_heads)), _ptr(gate, "gate", (B, d.n_v_heads)),
+        _ptr(state, "state", (B, d.n_v_heads, d.d_v, d.d_k)),
+        _ptr(out, "out", (B, d.n_v_heads, d.d_v)), _stream(stream)))
+
+
+def seq(q, k, v, beta, gate, state, out, stream=None) -> None:
+    """gdn_seq: q,k [B][T][Hk][dk], v [B][T][Hv][dv], beta/gate [B][T][Hv],
+    state [B][Hv][dv][dk] (in/out), out [B][T][Hv][dv]."""
+    B, T = q.shape[0], q.shape[1]
+    d = _dims_of(q, v)
+    _check(lib.gdn_seq(
+        ctypes.byref(d), B, T,
+        _ptr(q, "q", (B, T, d.n_k_heads, d.d_k)), _ptr(k, "k", (B, T, d.n_k_heads, d.d_k)),
+        _ptr(v, "v", (B, T, d.n_v_heads, d.d_v)),
+        _ptr(beta, "beta", (B, T, d.n_v_heads)), _ptr(gate, "gate", (B, T, d.n_v_heads)),
+        _ptr(state, "state", (B, d.n_v_heads, d.d_v, d.d_k)),
+        _ptr(out, "out", (B, T, d.n_v_heads, d.d_v)), _stream(stream)))
+
+
+def layer_tail_workspace_bytes(B: int, dims: Dims = PAGE_DIMS) -> int:
+    return int(lib.gdn_layer_tail_workspace_bytes(ctypes.byref(dims), B))
+
+
+def layer_tail(x, conv_w, conv_state, beta, gate, state, z, norm_w, y,
+               dbg_qkv=None, dbg_core=None, workspace=None,
+               dims: Dims = PAGE_DIMS, params: TailParams = PAGE_TAIL, stream=None) -> None:
+    """gdn_layer_tail.  workspace: a GPU tensor of at least
+    layer_tail_workspace_bytes(B) bytes (any dtype), or None when both dbg
+    buffers are given."""
+    import torch
+    B, C = x.shape
+    K = params.conv_kernel
+    nv = dims.n_v_heads * dims.d_v
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if not (isinstance(workspace, torch.Tensor) and workspace.is_cuda and workspace.is_contiguous()):
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(lib.gdn_layer_tail(
+        ctypes.byref(dims), ctypes.byref(params), B,
+        _ptr(x, "x", (B, C)), _ptr(conv_w, "conv_w", (C, K)),
+        _ptr(conv_state, "conv_state", (B, K - 1, C)),
+        _ptr(beta, "beta", (B, dims.n_v_heads)), _ptr(gate, "gate", (B, dims.n_v_heads)),
+        _ptr(state, "state", (B, dims.n_v_heads, dims.d_v, dims.d_k)),
+        _ptr(z, "z", (B, nv)), _ptr(norm_w, "norm_w", (params.norm_group,)),
+        _ptr(y, "y", (B, nv)),
+        _ptr(dbg_qkv, "dbg_qkv", (B, C), optional=True),
+        _ptr(dbg_core, "dbg_core", (B, dims.n_v_heads, dims.d_v), optional=True),
+        ws_ptr, ws_bytes, _stream(stream)))

@@ -1,0 +1,292 @@
+// gdn_api.cpp - the C ABI declared in include/gdn.h: argument validation,
+// error reporting and kernel dispatch.  All validation happens on the host
+// before anything is enqueued, so a rejected call leaves every buffer as it
+// was and never touches the GPU.
+
+#include "gdn.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "gdn_launch.hpp"
+
+namespace {
+
+thread_local char g_error[512];
+
+void clear_error() { g_error[0] = '\0'; }
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_error, sizeof g_error, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Do [a, a+na) and [b, b+nb) share a byte?
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+struct Buf {
+    const char *name;
+    const void *p;
+    size_t bytes;
+};
+
+// Every output must be disjoint from every other listed buffer.
+int check_alias(const Buf *outs, int n_out, const Buf *all, int n_all) {
+    for (int i = 0; i < n_out; ++i)
+        for (int j = 0; j < n_all; ++j) {
+            if (outs[i].p == all[j].p && outs[i].name == all[j].name) continue;  // itself
+            if (overlap(outs[i].p, outs[i].bytes, all[j].p, all[j].bytes))
+                return fail(GDN_ERR_ALIAS, "%s overlaps %s", outs[i].name, all[j].name);
+        }
+    return GDN_OK;
+}
+
+int check_dims(const gdn_dims *d) {
+    if (!d) return fail(GDN_ERR_NULL, "dims is NULL");
+    if (d->n_v_heads < 1 || d->n_k_heads < 1)
+        return fail(GDN_ERR_SHAPE, "head counts must be >= 1 (n_v_heads=%d, n_k_heads=%d)",
+                    d->n_v_heads, d->n_k_heads);
+    if (d->n_v_heads % d->n_k_heads != 0)
+        return fail(GDN_ERR_SHAPE, "n_v_heads=%d is not a multiple of n_k_heads=%d",
+                    d->n_v_heads, d->n_k_heads);
+    if (d->d_k != gdn::kHeadDim || d->d_v != gdn::kHeadDim)
+        return fail(GDN_ERR_SHAPE, "only d_k = d_v = %d is supported (got d_k=%d, d_v=%d)",
+                    gdn::kHeadDim, d->d_k, d->d_v);
+    return GDN_OK;
+}
+
+// Heads of one call map to workgroups along grid x.
+int check_batch(const gdn_dims *d, int64_t B, const char *what) {
+    if (B < 1) return fail(GDN_ERR_SHAPE, "%s must be >= 1 (got %lld)", what, (long long)B);
+    if (B * d->n_v_heads > INT32_MAX)
+        return fail(GDN_ERR_SHAPE, "B * n_v_heads = %lld exceeds %d", (long long)(B * d->n_v_heads),
+                    INT32_MAX);
+    return GDN_OK;
+}
+
+#define GDN_TRY(expr)               \
+    do {                            \
+        const int rc__ = (expr);    \
+        if (rc__ != GDN_OK) return rc__; \
+    } while (0)
+
+int check_ptrs(const Buf *bufs, int n, uintptr_t align) {
+    for (int i = 0; i < n; ++i) {
+        if (!bufs[i].p) return fail(GDN_ERR_NULL, "%s is NULL", bufs[i].name);
+        if (!aligned(bufs[i].p, align))
+            return fail(GDN_ERR_ALIGN, "%s (%p) is not %u-byte aligned", bufs[i].name, bufs[i].p,
+                        static_cast<unsigned>(align));
+    }
+    return GDN_OK;
+}
+
+int hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess)
+        return fail(GDN_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), static_cast<int>(e));
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_version(void) { return GDN_VERSION; }
+
+const char *gdn_last_error(void) { return g_error; }
+
+int gdn_step(const gdn_dims *dims, int32_t B, const float *q, const float *k, const float *v,
+             const float *beta, const float *gate, float *state, float *out, void *stream) {
+    clear_error();
+    GDN_TRY(check_dims(dims));
+    GDN_TRY(check_batch(dims, B, "B"));
+    const size_t f = sizeof(float);
+    const size_t nqk = static_cast<size_t>(B) * dims->n_k_heads * dims->d_k * f;
+    const size_t nv = static_cast<size_t>(B) * dims->n_v_heads * dims->d_v * f;
+    const size_t nh = static_cast<size_t>(B) * dims->n_v_heads * f;
+    const size_t ns = static_cast<size_t>(B) * dims->n_v_heads * dims->d_v * dims->d_k * f;
+    const Buf vec[] = {{"q", q, nqk}, {"k", k, nqk}, {"v", v, nv}, {"state", state, ns},
+                       {"out", out, nv}};
+    const Buf sc[] = {{"beta", beta, nh}, {"gate", gate, nh}};
+    GDN_TRY(check_ptrs(vec, 5, 16));
+    GDN_TRY(check_ptrs(sc, 2, 4));
+    const Buf all[] = {vec[0], vec[1], vec[2], vec[3], vec[4], sc[0], sc[1]};
+    const Buf outs[] = {vec[3], vec[4]};  // state and out are written
+    GDN_TRY(check_alias(outs, 2, all, 7));
+
+    gdn::StepArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.gate = gate;
+    a.state = state;
+    a.out = out;
+    a.qk_bstride = static_cast<int64_t>(dims->n_k_heads) * dims->d_k;
+    a.v_bstride = static_cast<int64_t>(dims->n_v_heads) * dims->d_v;
+    a.B = B;
+    a.Hv = dims->n_v_heads;
+    a.Hk = dims->n_k_heads;
+    (void)hipGetLastError();  // do not report an earlier, unrelated error
+    return hip_status(gdn::launch_step(a, static_cast<hipStream_t>(stream)), "gdn_step launch");
+}
+
+int gdn_seq(const gdn_dims *dims, int32_t B, int32_t T, const float *q, const float *k,
+            const float *v, const float *beta, const float *gate, float *state, float *out,
+            void *stream) {
+    clear_error();
+    GDN_TRY(check_dims(dims));
+    GDN_TRY(check_batch(dims, B, "B"));
+    if (T < 1) return fail(GDN_ERR_SHAPE, "T must be >= 1 (got %d)", T);
+    const size_t f = sizeof(float);
+    const size_t BT = static_cast<size_t>(B) * T;
+    const size_t nqk = BT * dims->n_k_heads * dims->d_k * f;
+    const size_t nv = BT * dims->n_v_heads * dims->d_v * f;
+    const size_t nh = BT * dims->n_v_heads * f;
+    const size_t ns = static_cast<size_t>(B) * dims->n_v_heads * dims->d_v * dims->d_k * f;
+    const Buf vec[] = {{"q", q, nqk}, {"k", k, nqk}, {"v", v, nv}, {"state", state, ns},
+                       {"out", out, nv}};
+    const Buf sc[] = {{"beta", beta, nh}, {"gate", gate, nh}};
+    GDN_TRY(check_ptrs(vec, 5, 16));
+    GDN_TRY(check_ptrs(sc, 2, 4));
+    const Buf all[] = {vec[0], vec[1], vec[2], vec[3], vec[4], sc[0], sc[1]};
+    const Buf outs[] = {vec[3], vec[4]};
+    GDN_TRY(check_alias(outs, 2, all, 7));
+
+    gdn::SeqArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.gate = gate;
+    a.state = state;
+    a.out = out;
+    a.B = B;
+    a.T = T;
+    a.Hv = dims->n_v_heads;
+    a.Hk = dims->n_k_heads;
+    (void)hipGetLastError();
+    return hip_status(gdn::launch_seq(a, static_cast<hipStream_t>(stream)), "gdn_seq launch");
+}
+
+size_t gdn_layer_tail_workspace_bytes(const gdn_dims *dims, int32_t B) {
+    if (!dims || B < 1 || dims->n_v_heads < 1 || dims->n_k_heads < 1 || dims->d_k < 1 ||
+        dims->d_v < 1)
+        return 0;
+    const size_t C = 2 * static_cast<size_t>(dims->n_k_heads) * dims->d_k +
+                     static_cast<size_t>(dims->n_v_heads) * dims->d_v;
+    const size_t qkv = static_cast<size_t>(B) * C * sizeof(float);
+    const size_t core = static_cast<size_t>(B) * dims->n_v_heads * dims->d_v * sizeof(float);
+    return qkv + core;  // both parts are multiples of 16 bytes (d_k = d_v = 128)
+}
+
+int gdn_layer_tail(const gdn_dims *dims, const gdn_tail_params *params, int32_t B,
+                   const float *x, const float *conv_w, float *conv_state, const float *beta,
+                   const float *gate, float *state, const float *z, const float *norm_w, float *y,
+                   float *dbg_qkv, float *dbg_core, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+    clear_error();
+    GDN_TRY(check_dims(dims));
+    if (!params) return fail(GDN_ERR_NULL, "params is NULL");
+    GDN_TRY(check_batch(dims, B, "B"));
+    const int K = params->conv_kernel;
+    if (K < 2 || K > 8) return fail(GDN_ERR_SHAPE, "conv_kernel must be in 2..8 (got %d)", K);
+    const int64_t nvw = static_cast<int64_t>(dims->n_v_heads) * dims->d_v;
+    if (params->norm_group < 1 || nvw % params->norm_group != 0)
+        return fail(GDN_ERR_SHAPE, "norm_group=%d must be >= 1 and divide n_v_heads*d_v=%lld",
+                    params->norm_group, (long long)nvw);
+    if (!(params->norm_eps >= 0.0f) || params->norm_eps > 3.0e38f)
+        return fail(GDN_ERR_SHAPE, "norm_eps must be finite and >= 0");
+    const int64_t C = 2 * static_cast<int64_t>(dims->n_k_heads) * dims->d_k + nvw;
+    if (C * B > INT32_MAX / 2)
+        return fail(GDN_ERR_SHAPE, "B * channels = %lld too large", (long long)(C * B));
+
+    const size_t f = sizeof(float);
+    const size_t nx = static_cast<size_t>(B) * C * f;
+    const size_t nw = static_cast<size_t>(C) * K * f;
+    const size_t ncs = static_cast<size_t>(B) * (K - 1) * C * f;
+    const size_t nh = static_cast<size_t>(B) * dims->n_v_heads * f;
+    const size_t ns = static_cast<size_t>(B) * dims->n_v_heads * dims->d_v * dims->d_k * f;
+    const size_t nz = static_cast<size_t>(B) * nvw * f;
+    const size_t nnw = static_cast<size_t>(params->norm_group) * f;
+
+    const Buf vec[] = {{"x", x, nx}, {"conv_state", conv_state, ncs}, {"state", state, ns},
+                       {"z", z, nz}, {"y", y, nz}};
+    const Buf sc[] = {{"conv_w", conv_w, nw}, {"beta", beta, nh}, {"gate", gate, nh},
+                      {"norm_w", norm_w, nnw}};
+    GDN_TRY(check_ptrs(vec, 5, 16));
+    GDN_TRY(check_ptrs(sc, 4, 4));
+    if (dbg_qkv && !aligned(dbg_qkv, 16)) return fail(GDN_ERR_ALIGN, "dbg_qkv is not 16-byte aligned");
+    if (dbg_core && !aligned(dbg_core, 16))
+        return fail(GDN_ERR_ALIGN, "dbg_core is not 16-byte aligned");
+
+    const size_t need = (dbg_qkv ? 0 : nx) + (dbg_core ? 0 : nz);
+    if (need > 0) {
+        if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+        if (!aligned(workspace, 16)) return fail(GDN_ERR_ALIGN, "workspace is not 16-byte aligned");
+        if (workspace_bytes < need)
+            return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
+                        need);
+    }
+    float *qkv = dbg_qkv ? dbg_qkv : static_cast<float *>(workspace);
+    float *core = dbg_core ? dbg_core
+                           : static_cast<float *>(workspace) + (dbg_qkv ? 0 : nx / f);
+
+    const Buf all[] = {vec[0], vec[1], vec[2], vec[3], vec[4], sc[0],
+                       sc[1],  sc[2],  sc[3],  {"qkv buffer", qkv, nx}, {"core buffer", core, nz}};
+    const Buf outs[] = {vec[1], vec[2], vec[4], all[9], all[10]};
+    GDN_TRY(check_alias(outs, 5, all, 11));
+
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+
+    gdn::PrestateArgs pa{};
+    pa.x = x;
+    pa.conv_w = conv_w;
+    pa.conv_state = conv_state;
+    pa.qkv = qkv;
+    pa.B = B;
+    pa.C = static_cast<int32_t>(C);
+    pa.K = K;
+    pa.n_qk = 2 * dims->n_k_heads * dims->d_k;
+    GDN_TRY(hip_status(gdn::launch_prestate(pa, s), "gdn_layer_tail prestate launch"));
+
+    gdn::StepArgs sa{};
+    sa.q = qkv;
+    sa.k = qkv + static_cast<int64_t>(dims->n_k_heads) * dims->d_k;
+    sa.v = qkv + pa.n_qk;
+    sa.beta = beta;
+    sa.gate = gate;
+    sa.state = state;
+    sa.out = core;
+    sa.qk_bstride = C;
+    sa.v_bstride = C;
+    sa.B = B;
+    sa.Hv = dims->n_v_heads;
+    sa.Hk = dims->n_k_heads;
+    GDN_TRY(hip_status(gdn::launch_step(sa, s), "gdn_layer_tail step launch"));
+
+    gdn::GatedNormArgs na{};
+    na.o = core;
+    na.z = z;
+    na.w = norm_w;
+    na.y = y;
+    na.rows = B;
+    na.n = static_cast<int32_t>(nvw);
+    na.group = params->norm_group;
+    na.eps = params->norm_eps;
+    return hip_status(gdn::launch_gated_norm(na, s), "gdn_layer_tail gated-norm launch");
+}
+
+}  // extern "C"

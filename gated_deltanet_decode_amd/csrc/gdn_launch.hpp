@@ -1,0 +1,73 @@
+// gdn_launch.hpp - internal interface between the C-ABI layer (gdn_api.cpp)
+// and the gfx950 kernels (gdn_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Only head size supported by the kernels: d_k = d_v = 128 (the page's model).
+constexpr int kHeadDim = 128;
+
+// One token of the state step for B sequences.  q/k/v may live inside a larger
+// per-sequence row (the layer tail reads them from its [B][C] buffer), hence
+// the explicit per-sequence strides (in floats).
+struct StepArgs {
+    const float *q;
+    const float *k;
+    const float *v;
+    const float *beta;
+    const float *gate;
+    float *state;
+    float *out;
+    int64_t qk_bstride;  // floats between sequences in q and k
+    int64_t v_bstride;   // floats between sequences in v
+    int32_t B;
+    int32_t Hv;
+    int32_t Hk;
+};
+
+struct SeqArgs {
+    const float *q;
+    const float *k;
+    const float *v;
+    const float *beta;
+    const float *gate;
+    float *state;
+    float *out;
+    int32_t B;
+    int32_t T;
+    int32_t Hv;
+    int32_t Hk;
+};
+
+// conv-state shift + causal conv1d + SiLU + per-head L2 of the Q and K parts.
+struct PrestateArgs {
+    const float *x;
+    const float *conv_w;
+    float *conv_state;
+    float *qkv;        // [B][C] output
+    int32_t B;
+    int32_t C;
+    int32_t K;
+    int32_t n_qk;      // channels of Q plus K (2 * Hk * d_k); these get L2-normalised
+};
+
+struct GatedNormArgs {
+    const float *o;
+    const float *z;
+    const float *w;
+    float *y;
+    int32_t rows;
+    int32_t n;
+    int32_t group;
+    float eps;
+};
+
+hipError_t launch_step(const StepArgs &a, hipStream_t s);
+hipError_t launch_seq(const SeqArgs &a, hipStream_t s);
+hipError_t launch_prestate(const PrestateArgs &a, hipStream_t s);
+hipError_t launch_gated_norm(const GatedNormArgs &a, hipStream_t s);
+
+}  // namespace gdn

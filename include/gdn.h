@@ -1,0 +1,155 @@
+/*
+ * gdn.h - C ABI of libgdn.so, the MI355X (gfx950) Gated DeltaNet decode path.
+ *
+ * Operation (Red Lite dev15c "Gated DeltaNet recurrent-state parity",
+ * section "Pinned llama.cpp semantics"): for every sequence b and value head
+ * h, with key head kh = h % n_k_heads, e = exp(gate[b][h]) and the transposed
+ * state M[j][i] = S[i][j] (j = value dim, i = key dim):
+ *   1. M *= e
+ *   2. sk[j]    = sum_i M[j][i] * k[kh][i]        (decayed M)
+ *   3. delta[j] = (v[h][j] - sk[j]) * beta[b][h]
+ *   4. M[j][i] += delta[j] * k[kh][i]
+ *   5. out[j]   = sum_i M[j][i] * q[kh][i] / sqrt(d_k)   (updated M)
+ * The page's geometry is d_k = d_v = 128, 16 key heads, 32 value heads,
+ * a 2 MiB F32 state per sequence and layer.
+ *
+ * Conventions shared by every call
+ *   - All tensors are float32 (IEEE binary32), row-major and contiguous.
+ *   - Every pointer is a device pointer (hipMalloc'd or torch CUDA memory)
+ *     that the caller owns; the library keeps no reference after the call.
+ *   - Tensor pointers must be 16-byte aligned; beta and gate 4-byte aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls enqueue their kernels on it and return without synchronising.
+ *   - Inputs are read-only; `state` and `conv_state` are updated in place.
+ *     Outputs must not overlap any input or state buffer.
+ *   - Supported on the GPU path: d_k = d_v = 128, n_k_heads >= 1,
+ *     n_v_heads a multiple of n_k_heads, B >= 1, T >= 1.
+ *   - Results are bitwise deterministic for identical inputs, independent of
+ *     B and of the other sequences in the batch.  gdn_seq over T tokens is
+ *     bitwise equal to T calls of gdn_step.
+ *   - NaN and Inf inputs are not checked; they propagate.
+ *
+ * Errors: every call returns GDN_OK (0) or a negative code.  Argument errors
+ * are detected before anything is enqueued and leave every buffer untouched;
+ * gdn_last_error() then returns a message describing the failure (thread
+ * local, valid until the next call on the same thread).  GDN_ERR_HIP reports
+ * a failed kernel launch (hipGetLastError); work already enqueued by that
+ * call may have run.
+ *
+ * Thread safety: every call may be made concurrently from several host
+ * threads.  The library holds no mutable global state apart from the
+ * thread-local error text.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_VERSION 10000 /* 1.0.0 */
+
+#define GDN_OK 0
+#define GDN_ERR_NULL (-1)      /* a required pointer is NULL                  */
+#define GDN_ERR_SHAPE (-2)     /* unsupported sizes (B, T, heads, dims, tail) */
+#define GDN_ERR_ALIGN (-3)     /* a pointer is not suitably aligned           */
+#define GDN_ERR_ALIAS (-4)     /* an output overlaps an input or a state      */
+#define GDN_ERR_WORKSPACE (-5) /* workspace missing or too small              */
+#define GDN_ERR_HIP (-6)       /* the HIP runtime reported a launch error     */
+
+/* Head geometry.  The page's model: {32, 16, 128, 128}. */
+typedef struct gdn_dims {
+    int32_t n_v_heads; /* value / recurrent heads                   */
+    int32_t n_k_heads; /* key / query heads; value head h uses h % n_k_heads */
+    int32_t d_k;       /* key dimension (state row length)          */
+    int32_t d_v;       /* value dimension (state rows per head)     */
+} gdn_dims;
+
+/* Tail parameters.  The page's model: {4, 128, 1e-6f}. */
+typedef struct gdn_tail_params {
+    int32_t conv_kernel; /* causal conv1d taps, 2..8; cache holds conv_kernel-1 inputs */
+    int32_t norm_group;  /* gated RMSNorm group size; must divide n_v_heads*d_v        */
+    float norm_eps;      /* added to mean(o^2) inside the square root, >= 0            */
+} gdn_tail_params;
+
+/*
+ * gdn_step - one token for B sequences (dev15c, steps 1-5 above).
+ *   q, k   [B][n_k_heads][d_k]   (L2-normalised by the caller)
+ *   v      [B][n_v_heads][d_v]
+ *   beta   [B][n_v_heads]        update strength, used as given
+ *   gate   [B][n_v_heads]        log-decay; the step applies exp()
+ *   state  [B][n_v_heads][d_v][d_k]   transposed state M, updated in place
+ *   out    [B][n_v_heads][d_v]
+ * Each state element is read once and written once.
+ */
+int gdn_step(const gdn_dims *dims, int32_t B,
+             const float *q, const float *k, const float *v,
+             const float *beta, const float *gate,
+             float *state, float *out, void *stream);
+
+/*
+ * gdn_seq - T tokens for B sequences, run in order with the state carried
+ * (docs.rs "Module linear_core", gdn_forward_batch: the recurrence runs
+ * sequentially over positions, elementwise identical to single steps).
+ *   q, k   [B][T][n_k_heads][d_k]
+ *   v      [B][T][n_v_heads][d_v]
+ *   beta, gate [B][T][n_v_heads]
+ *   state  [B][n_v_heads][d_v][d_k]   in: state before token 0, out: after T-1
+ *   out    [B][T][n_v_heads][d_v]
+ * The state stays on chip for all T tokens: it is read once and written once
+ * per call.  Splitting T into consecutive calls gives bitwise the same result.
+ */
+int gdn_seq(const gdn_dims *dims, int32_t B, int32_t T,
+            const float *q, const float *k, const float *v,
+            const float *beta, const float *gate,
+            float *state, float *out, void *stream);
+
+/*
+ * gdn_layer_tail - the recurrent branch around the step for one token
+ * (Red Lite dev15e "complete recurrent DeltaNet layer composition", stage
+ * list; dev15a "Validation boundary", prestate order), with C = 2*n_k_heads*d_k
+ * + n_v_heads*d_v channels (8192 for the page's model):
+ *   1. conv-state shift + causal conv1d over the window
+ *      [conv_state slot 0 .. slot K-2, x] (oldest first, tap t on window
+ *      element t, no bias); conv_state then holds the last K-1 raw inputs;
+ *   2. SiLU;  3. split [Q | K | V];  4. per-head L2 norm of Q and K
+ *      (u / max(||u||, 1e-6));  5. gdn_step;
+ *   6. gated RMSNorm: y = o / sqrt(mean_group(o^2) + eps) * norm_w[pos] * SiLU(z).
+ *   x          [B][C]          raw pre-conv channels
+ *   conv_w     [C][conv_kernel]
+ *   conv_state [B][conv_kernel-1][C]   in/out
+ *   beta, gate [B][n_v_heads]
+ *   state      [B][n_v_heads][d_v][d_k] in/out
+ *   z          [B][n_v_heads*d_v]
+ *   norm_w     [norm_group]
+ *   y          [B][n_v_heads*d_v]      output
+ *   dbg_qkv    [B][C] optional (NULL = skip): normalised Q | K | V fed to the step
+ *   dbg_core   [B][n_v_heads][d_v] optional: step output before the gated norm
+ *   workspace  device scratch of gdn_layer_tail_workspace_bytes() bytes
+ *              (16-byte aligned; may be NULL when both dbg buffers are given)
+ */
+int gdn_layer_tail(const gdn_dims *dims, const gdn_tail_params *params, int32_t B,
+                   const float *x, const float *conv_w, float *conv_state,
+                   const float *beta, const float *gate, float *state,
+                   const float *z, const float *norm_w, float *y,
+                   float *dbg_qkv, float *dbg_core,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace gdn_layer_tail needs when no dbg buffer is given
+ * (0 on invalid arguments). */
+size_t gdn_layer_tail_workspace_bytes(const gdn_dims *dims, int32_t B);
+
+/* Message for the last non-zero return on this thread ("" if none). */
+const char *gdn_last_error(void);
+
+/* GDN_VERSION of the loaded library. */
+int gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

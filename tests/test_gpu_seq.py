@@ -1,0 +1,99 @@
+"""GPU: gdn_seq (state resident on chip over T tokens) against the oracle,
+and its contract with gdn_step (docs.rs "Module linear_core",
+gdn_forward_batch: sequential over positions, elementwise identical)."""
+import numpy as np
+import pytest
+
+import gdn_inputs as gi
+import ref
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def g():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import gated_deltanet_decode_amd as g
+    return g
+
+
+def dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run_seq(g, si, M):
+    import torch
+    t = {n: dev(x) for n, x in si.items()}
+    Md = dev(M)
+    out = torch.empty(si["v"].shape, dtype=torch.float32, device="cuda")
+    g.seq(t["q"], t["k"], t["v"], t["beta"], t["gate"], Md, out)
+    torch.cuda.synchronize()
+    return Md.cpu().numpy(), out.cpu().numpy()
+
+
+def token(si, t):
+    return {n: np.ascontiguousarray(x[:, t]) for n, x in si.items()}
+
+
+@pytest.mark.parametrize("B,T,Hv,Hk", [(1, 1, 32, 16), (2, 5, 32, 16), (1, 17, 32, 16),
+                                       (3, 33, 4, 2), (2, 16, 1, 1), (1, 48, 64, 16)])
+def test_seq_matches_oracle(g, orc, B, T, Hv, Hk):
+    print(f"\n  gdn_seq B={B} T={T} Hv={Hv} Hk={Hk}", flush=True)
+    si = gi.step_inputs(3000 + T, 0, B, Hv, Hk, T=T)
+    M = gi.state(3000 + T, 0, B, Hv)
+    Mg, og = run_seq(g, si, M)
+    want = ref.seq_mt(orc, si, M)
+    # The recurrence contracts (0 < exp(gate) < 1, 0 < beta < 1, unit k), so
+    # rounding differences do not build up over short runs: the per-step
+    # tolerances apply.
+    ref.assert_close("state", Mg, M, 1e-6)
+    ref.assert_close("out", og, want, 1e-5)
+
+
+def test_seq_is_bitwise_repeated_step(g):
+    """T tokens in one gdn_seq == T gdn_step calls, bit for bit (both paths
+    share the per-row arithmetic)."""
+    import torch
+    print("\n  gdn_seq == repeated gdn_step", flush=True)
+    B, T = 2, 37
+    si = gi.step_inputs(3100, 0, B, T=T)
+    M = gi.state(3100, 0, B)
+    Ms, os_ = run_seq(g, si, M)
+    Md = dev(M)
+    outs = []
+    for t in range(T):
+        tk = {n: dev(x) for n, x in token(si, t).items()}
+        o = torch.empty((B, 32, 128), device="cuda")
+        g.step(tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], Md, o)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert np.array_equal(Md.cpu().numpy(), Ms), "state differs"
+    assert np.array_equal(torch.stack(outs, 1).cpu().numpy(), os_), "outputs differ"
+
+
+def test_seq_chunked_resume_is_bitwise(g):
+    """Checkpoint/resume: seq(T) == seq(T1) then seq(T - T1) from the saved state."""
+    print("\n  gdn_seq chunked resume", flush=True)
+    B, T, T1 = 3, 40, 13
+    si = gi.step_inputs(3200, 0, B, T=T)
+    M = gi.state(3200, 0, B)
+    Mfull, ofull = run_seq(g, si, M)
+    a = {n: np.ascontiguousarray(x[:, :T1]) for n, x in si.items()}
+    b = {n: np.ascontiguousarray(x[:, T1:]) for n, x in si.items()}
+    M1, o1 = run_seq(g, a, M)
+    M2, o2 = run_seq(g, b, M1)
+    assert np.array_equal(M2, Mfull) and np.array_equal(np.concatenate([o1, o2], 1), ofull)
+
+
+def test_seq_contraction_from_zero_state(g, orc):
+    """Zero initial state (configuration 3's start) over a ragged T."""
+    print("\n  gdn_seq zero state T=70", flush=True)
+    B, T = 2, 70
+    si = gi.step_inputs(3300, 0, B, T=T)
+    M = np.zeros((B, 32, 128, 128), np.float32)
+    Mg, og = run_seq(g, si, M)
+    want = ref.seq_mt(orc, si, M)
+    ref.assert_close("state", Mg, M, 1e-6)
+    ref.assert_close("out", og, want, 1e-5)

@@ -1,0 +1,141 @@
+"""GPU: gdn_step (through the C ABI) against the oracle, element by element,
+plus the properties the pages fix: h % 16 broadcast, the delta-rule
+invariant, batch invariance and run-to-run determinism."""
+import numpy as np
+import pytest
+
+import gdn_inputs as gi
+import ref
+
+pytestmark = pytest.mark.gpu
+
+STATE_TOL = 1e-6   # per-step tolerances (absolute)
+OUT_TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def g():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import gated_deltanet_decode_amd as g
+    return g
+
+
+def dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run_step(g, si, M):
+    import torch
+    t = {n: dev(x) for n, x in si.items()}
+    Md = dev(M)
+    out = torch.empty(si["v"].shape, dtype=torch.float32, device="cuda")
+    g.step(t["q"], t["k"], t["v"], t["beta"], t["gate"], Md, out)
+    torch.cuda.synchronize()
+    return Md.cpu().numpy(), out.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,Hv,Hk", [(1, 32, 16), (3, 32, 16), (5, 4, 2), (2, 1, 1),
+                                     (2, 64, 16), (7, 16, 16), (1, 96, 32)])
+def test_step_matches_oracle(g, orc, B, Hv, Hk):
+    print(f"\n  gdn_step B={B} Hv={Hv} Hk={Hk}", flush=True)
+    si = gi.step_inputs(2000 + B, Hv, B, Hv, Hk)
+    M = gi.state(2000 + B, Hv, B, Hv)
+    Mg, og = run_step(g, si, M)
+    want = ref.step_mt(orc, si, M)
+    ref.assert_close("state", Mg, M, STATE_TOL)
+    ref.assert_close("out", og, want, OUT_TOL)
+
+
+def test_config0_single_sequence(g, orc):
+    """Configuration 0: B=1, the page geometry, seed 1000."""
+    c = gi.CONFIGS[0]
+    print("\n  config 0: gdn_step B=1", flush=True)
+    si = gi.step_inputs(c["seed"], 0, 1)
+    M = gi.state(c["seed"], 0, 1)
+    M64 = M.astype(np.float64)
+    Mg, og = run_step(g, si, M)
+    want = orc.step_M(si["q"], si["k"], si["v"], si["beta"], si["gate"], M)
+    out64 = orc.step_f64(si["q"], si["k"], si["v"], si["beta"], si["gate"], M64)
+    ref.assert_close("state", Mg, M, STATE_TOL)
+    ref.assert_close("out", og, want, OUT_TOL)
+    # diagnostic: GPU and f32-oracle errors against the binary64 shadow
+    print("    vs f64: gpu state %.3e out %.3e | oracle state %.3e out %.3e" % (
+        ref.max_err(Mg, M64)[0], ref.max_err(og, out64)[0],
+        ref.max_err(M, M64)[0], ref.max_err(want, out64)[0]), flush=True)
+
+
+def test_broadcast_and_delta_rule_on_gpu(g):
+    """beta=1, gate=0, unit k: the GPU's updated state satisfies M'k = v with
+    the key head h % 16; heads h and h+16 fed the same v and state agree
+    bitwise."""
+    print("\n  gdn_step broadcast / delta rule", flush=True)
+    si = gi.step_inputs(2100, 0, 2)
+    si["beta"][:] = 1.0
+    si["gate"][:] = 0.0
+    si["v"][:, 16:] = si["v"][:, :16]
+    M = gi.state(2100, 0, 2)
+    M[:, 16:] = M[:, :16]
+    Mg, og = run_step(g, si, M)
+    for b in range(2):
+        for h in range(32):
+            r = Mg[b, h].astype(np.float64) @ si["k"][b, h % 16].astype(np.float64)
+            assert np.max(np.abs(r - si["v"][b, h])) <= 2e-6, (b, h)
+            if h % 16 != h // 2:
+                r2 = Mg[b, h].astype(np.float64) @ si["k"][b, h // 2].astype(np.float64)
+                assert np.max(np.abs(r2 - si["v"][b, h])) > 1e-3, (b, h)
+        assert np.array_equal(Mg[b, :16], Mg[b, 16:]) and np.array_equal(og[b, :16], og[b, 16:])
+
+
+def test_batch_invariance_and_determinism(g):
+    """A sequence's result is bitwise independent of the batch it runs in, and
+    two runs on the same inputs are bitwise equal."""
+    print("\n  gdn_step batch invariance", flush=True)
+    si = gi.step_inputs(2200, 0, 6)
+    M = gi.state(2200, 0, 6)
+    M6, o6 = run_step(g, si, M)
+    M6b, o6b = run_step(g, si, M)
+    assert np.array_equal(M6, M6b) and np.array_equal(o6, o6b), "not deterministic"
+    s1 = gi.step_inputs(2200, 0, 1, b0=4)      # sequence 4 alone, regenerated
+    M1 = gi.state(2200, 0, 1, b0=4)
+    M1g, o1g = run_step(g, s1, M1)
+    assert np.array_equal(M1g[0], M6[4]) and np.array_equal(o1g[0], o6[4]), "batch dependence"
+
+
+def test_special_cases_on_gpu(g, orc):
+    """Full forget (gate=-1e4), pure decay (beta=0), zero state, zero k."""
+    print("\n  gdn_step special cases", flush=True)
+    for case in ("forget", "decay", "zero_state", "zero_k"):
+        si = gi.step_inputs(2300, 0, 2)
+        M = gi.state(2300, 0, 2)
+        if case == "forget":
+            si["gate"][:] = -1e4
+        elif case == "decay":
+            si["beta"][:] = 0
+        elif case == "zero_state":
+            M[:] = 0
+        else:
+            si["k"][:] = 0
+        Mg, og = run_step(g, si, M)
+        want = ref.step_mt(orc, si, M)
+        ref.assert_close(case + " state", Mg, M, STATE_TOL)
+        ref.assert_close(case + " out", og, want, OUT_TOL)
+
+
+def test_rejected_call_leaves_buffers_untouched(g):
+    """An argument error is reported before anything is enqueued."""
+    import ctypes
+    import torch
+    print("\n  gdn_step rejected call", flush=True)
+    si = gi.step_inputs(2400, 0, 2)
+    M = gi.state(2400, 0, 2)
+    t = {n: dev(x) for n, x in si.items()}
+    Md = dev(M)
+    out = torch.full((2, 32, 128), 7.0, device="cuda")
+    rc = g.lib.gdn_step(ctypes.byref(g.PAGE_DIMS), 2, t["q"].data_ptr() + 4, t["k"].data_ptr(),
+                        t["v"].data_ptr(), t["beta"].data_ptr(), t["gate"].data_ptr(),
+                        Md.data_ptr(), out.data_ptr(), None)
+    torch.cuda.synchronize()
+    assert rc == -3 and "q" in g.last_error()
+    assert np.array_equal(Md.cpu().numpy(), M) and bool((out == 7.0).all())

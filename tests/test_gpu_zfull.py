@@ -1,0 +1,139 @@
+"""GPU: the full-size configurations, in the launch configuration the
+benchmark times, checked against the oracle on sampled sequences (config 2)
+or in full (configs 1 and 3).
+
+  config 1: B=64 decode, 100 gdn_step calls with fresh inputs
+  config 2: B=256 x 36 layers (18 GiB of state), one gdn_step per layer,
+            plus the same 36 layers flattened into one B=9216 call
+  config 3: gdn_seq B=8 x T=4096 from a zero state
+"""
+import numpy as np
+import pytest
+
+import gdn_inputs as gi
+import ref
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def g():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import gated_deltanet_decode_amd as g
+    return g
+
+
+def dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+@pytest.mark.timeout(600)
+def test_config1_b64_x100(g, orc):
+    import torch
+    c = gi.CONFIGS[1]
+    B, calls = c["B"], c["calls"]
+    print(f"\n  config 1: gdn_step B={B} x {calls} calls", flush=True)
+    M = gi.state(c["seed"], 0, B)
+    Md = dev(M)
+    inputs = [gi.step_inputs(c["seed"], i, B) for i in range(calls)]
+    dins = [{n: dev(x) for n, x in si.items()} for si in inputs]
+    outs = torch.empty((calls, B, 32, 128), device="cuda")
+    M1 = None
+    for i in range(calls):
+        t = dins[i]
+        g.step(t["q"], t["k"], t["v"], t["beta"], t["gate"], Md, outs[i])
+        if i == 0:
+            M1 = Md.cpu().numpy()
+    torch.cuda.synchronize()
+    Mg, og = Md.cpu().numpy(), outs.cpu().numpy()
+    worst = 0.0
+    for i in range(calls):
+        want = ref.step_mt(orc, inputs[i], M)
+        if i == 0:
+            ref.assert_close("state@1", M1, M, 1e-6)
+        worst = max(worst, ref.max_err(og[i], want)[0])
+        assert worst <= 1e-5, f"call {i}: out error {worst:.3e}"
+    print(f"    all {calls} outputs: max abs {worst:.3e}", flush=True)
+    ref.assert_close("state@100", Mg, M, 1e-6)
+
+
+@pytest.mark.timeout(900)
+def test_config2_b256_x36_layers(g, orc):
+    import torch
+    c = gi.CONFIGS[2]
+    B, L, seed = c["B"], c["layers"], c["seed"]
+    print(f"\n  config 2: gdn_step B={B} x {L} layers (18 GiB state)", flush=True)
+    states = torch.empty((L, B, 32, 128, 128), device="cuda")
+    stage = torch.empty((B, 32, 128, 128), pin_memory=True)
+    sn = stage.numpy()
+    ins = []
+    for l in range(L):
+        gi.state_into(sn, seed, l)
+        states[l].copy_(stage)
+        ins.append(gi.step_inputs(seed, l, B))
+    torch.cuda.synchronize()
+    dins = {n: dev(np.stack([ins[l][n] for l in range(L)])) for n in ins[0]}
+    outs = torch.empty((L, B, 32, 128), device="cuda")
+    print("    inputs resident; running 36 layer calls", flush=True)
+    for l in range(L):
+        g.step(dins["q"][l], dins["k"][l], dins["v"][l], dins["beta"][l], dins["gate"][l],
+               states[l], outs[l])
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(7)
+    picks = {l: np.sort(rng.choice(B, 8, replace=False)) for l in range(L)}
+    picks[0] = np.r_[0, picks[0][1:-1], B - 1]          # first and last sequence
+    post = {}
+    worst_s = worst_o = 0.0
+    og = outs.cpu().numpy()
+    for l in range(L):
+        for b in picks[l]:
+            si = {n: np.ascontiguousarray(ins[l][n][b:b + 1]) for n in ins[l]}
+            M = gi.state(seed, l, 1, b0=int(b))
+            want = orc.step_M(si["q"], si["k"], si["v"], si["beta"], si["gate"], M)
+            Mg = states[l, b].cpu().numpy()
+            worst_s = max(worst_s, ref.max_err(Mg, M[0])[0])
+            worst_o = max(worst_o, ref.max_err(og[l, b], want[0])[0])
+            post[(l, int(b))] = M
+        if l % 6 == 5:
+            print(f"    layers 0..{l} checked: state {worst_s:.3e} out {worst_o:.3e}", flush=True)
+    assert worst_s <= 1e-6 and worst_o <= 1e-5, (worst_s, worst_o)
+
+    # The same memory as one flattened B=9216 call (one more token).
+    print("    flattened B=9216 call", flush=True)
+    flat = states.view(L * B, 32, 128, 128)
+    ins2 = [gi.step_inputs(seed + 100, l, B) for l in range(L)]
+    d2 = {n: dev(np.concatenate([ins2[l][n] for l in range(L)])) for n in ins2[0]}
+    out2 = torch.empty((L * B, 32, 128), device="cuda")
+    g.step(d2["q"], d2["k"], d2["v"], d2["beta"], d2["gate"], flat, out2)
+    torch.cuda.synchronize()
+    o2 = out2.cpu().numpy()
+    worst_s = worst_o = 0.0
+    for (l, b), M in post.items():
+        si = {n: np.ascontiguousarray(ins2[l][n][b:b + 1]) for n in ins2[l]}
+        want = orc.step_M(si["q"], si["k"], si["v"], si["beta"], si["gate"], M)
+        worst_s = max(worst_s, ref.max_err(flat[l * B + b].cpu().numpy(), M[0])[0])
+        worst_o = max(worst_o, ref.max_err(o2[l * B + b], want[0])[0])
+    print(f"    flattened: state {worst_s:.3e} out {worst_o:.3e}", flush=True)
+    assert worst_s <= 1e-6 and worst_o <= 1e-5, (worst_s, worst_o)
+
+
+@pytest.mark.timeout(600)
+def test_config3_seq_b8_t4096(g, orc):
+    import torch
+    c = gi.CONFIGS[3]
+    B, T = c["B"], c["T"]
+    print(f"\n  config 3: gdn_seq B={B} T={T} from zero state", flush=True)
+    si = gi.step_inputs(c["seed"], 0, B, T=T)
+    M = np.zeros((B, 32, 128, 128), np.float32)
+    t = {n: dev(x) for n, x in si.items()}
+    Md = dev(M)
+    out = torch.empty((B, T, 32, 128), device="cuda")
+    g.seq(t["q"], t["k"], t["v"], t["beta"], t["gate"], Md, out)
+    torch.cuda.synchronize()
+    print("    GPU done; oracle running", flush=True)
+    want = ref.seq_mt(orc, si, M)
+    ref.assert_close("state", Md.cpu().numpy(), M, 1e-4)
+    ref.assert_close("out", out.cpu().numpy(), want, 1e-4)
