@@ -35,6 +35,11 @@ HV, HK, D = gi.HV, gi.HK, gi.D
 # (512 B), beta and gate (8 B).
 STATE_UPDATE_BYTES = 2 * D * D * 4 + 2 * D * 4 + (2 * D * 4) // 2 + 8   # 132616
 HBM_PEAK_GBPS = 8000.0
+# HBM traffic of one gdn_step launch from hardware counters (FETCH_SIZE and
+# WRITE_SIZE, calibrated against a copy of known size); only reported while
+# the kernel source is the one the counters were taken on.
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "k_step_b256_traffic.json")
+KERNEL_SOURCE = os.path.join(HERE, "gated_deltanet_decode_amd", "csrc", "gdn_kernels.hip")
 METRIC = "GDN state-updates/s (seq·head·token) and achieved HBM GB/s, B=256 decode"
 
 
@@ -69,6 +74,45 @@ def setup_config2(torch, g):
         torch.cuda.synchronize()
     outs = torch.empty((L, B, HV, D), device="cuda")
     return dict(B=B, L=L, states=states, ins=ins, outs=outs)
+
+
+def measured_traffic():
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(KERNEL_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != sha:
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def copy_probe(torch, stream, nbytes=1 << 30, reps=5):
+    """Bandwidth of a plain device-to-device copy (read + write bytes / s)."""
+    import ctypes
+    from gated_deltanet_decode_amd._build import PROBE_LIBRARY
+    lib = ctypes.CDLL(PROBE_LIBRARY)
+    lib.gdn_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+
+    def once():
+        assert lib.gdn_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, stream.cuda_stream) == 0
+    once()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(reps):
+        once()
+    e.record(stream)
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del src, dst
+    return 2 * nbytes / (ms / 1e3) / 1e9
 
 
 def run_step36(g, w, stream, evs=None):
@@ -111,7 +155,7 @@ def cpu_baseline(seconds):
         layer(done % n_layers)
         done += 1
         el = time.perf_counter() - t0
-        if el >= seconds or done >= 360:
+        if el >= seconds or done >= 4000:
             break
     updates = done * B * HV
     return {"value": updates / el, "unit": "state-updates/s", "cores": threads, "kind": "oracle",
@@ -200,8 +244,10 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
 
-    w = setup_config2(torch, g)
     stream = torch.cuda.current_stream()
+    copy_gbps = copy_probe(torch, stream)
+    log(f"[bench] copy probe: {copy_gbps:.0f} GB/s")
+    w = setup_config2(torch, g)
     L, B = w["L"], w["B"]
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -254,8 +300,9 @@ def main():
         "achieved_GBps_step": updates_per_step * STATE_UPDATE_BYTES / (ms_per_step / 1e3) / 1e9,
         "roofline": {"bound": "hbm", "kernel": "k_step (gdn_step)", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None,
+                     "traffic": measured_traffic(),
                      "bytes_per_launch": bytes_per_launch,
+                     "copy_probe_GBps": copy_gbps,
                      "avg_launch_us": avg_launch_ms * 1e3},
     }
     if not args.no_extra:

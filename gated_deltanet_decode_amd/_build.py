@@ -9,6 +9,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBRARY = os.path.join(CSRC, "libgdn.so")
 SOURCES = [os.path.join(CSRC, "gdn_api.cpp"), os.path.join(CSRC, "gdn_kernels.hip")]
+# Measurement aid (a copy kernel of known size), built as its own library.
+PROBE_LIBRARY = os.path.join(CSRC, "libgdn_probe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "hbm_probe.hip")]
 ARCH = "gfx950"
 
 # Packed FP32 instructions are switched off for the device code; hipcc's host
@@ -26,10 +29,13 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(output: str = LIBRARY, extra=(), verbose: bool = False) -> str:
-    """Compile every HIP source into one shared library; returns its path."""
+def build(output: str = LIBRARY, extra=(), verbose: bool = False, sources=None) -> str:
+    """Compile the decode-path HIP sources into one shared library (and, for
+    the default output, the copy probe into its own); returns the path."""
+    if sources is None and output == LIBRARY:
+        build(PROBE_LIBRARY, extra, verbose, PROBE_SOURCES)
     tmp = output + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, *SOURCES, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, *(sources or SOURCES), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -7,15 +7,15 @@
 // Work decomposition.  Row j of a head's state depends only on that row,
 // on the head's k and q, and on v[j], beta and gate: rows never exchange
 // data, not even across tokens.  Every kernel here therefore gives one state
-// row (128 floats, 512 contiguous bytes) to a quad of four lanes:
-//   lane c (0..3) of the quad owns the float4 chunks 4*i + c, i = 0..7,
-//   i.e. 32 of the 128 columns, interleaved so that one vector-memory
-//   instruction of the quad covers 64 contiguous bytes of the row.
-// A wave64 therefore works on 16 rows at a time (a "tile", 8 KiB of state).
-// The two row dot products (M k and M q) are a 32-term FMA chain per lane
-// followed by a two-step quad reduction over DPP quad_perm; the quad then
-// holds bitwise-identical sums in all four lanes, so delta is identical in
-// every lane that applies it.
+// row (128 floats, 512 contiguous bytes) to a group of eight lanes:
+//   lane c (0..7) of the group owns the float4 chunks 8*i + c, i = 0..3,
+//   i.e. 16 of the 128 columns, interleaved so that one vector-memory
+//   instruction of the group covers one whole 128-byte line of the row.
+// A wave64 therefore works on 8 rows at a time (a "tile", 4 KiB of state).
+// The two row dot products (M k and M q) are a 16-term FMA chain per lane
+// followed by a three-step reduction over the group with DPP
+// (row_half_mirror, then two quad_perm swaps); all eight lanes end with
+// bitwise-identical sums, so delta is the same in every lane that applies it.
 //
 // All kernels share row_token(), so a row's arithmetic is the same in the
 // single-step kernel, the multi-token kernel and the tail: a T-token gdn_seq
@@ -33,54 +33,73 @@
 namespace gdn {
 namespace {
 
-constexpr int D = kHeadDim;            // 128
-constexpr int kLanesPerRow = 4;        // a quad owns a row
-constexpr int kF4PerLane = D / 4 / kLanesPerRow;  // 8 float4 = 32 floats per lane
-constexpr int kRowsPerTile = 64 / kLanesPerRow;    // 16 rows per wave
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int D = kHeadDim;                        // 128
+constexpr int kLanesPerRow = 8;                    // a lane group owns a row
+constexpr int kF4PerLane = D / 4 / kLanesPerRow;   // 4 float4 = 16 floats per lane
+constexpr int kRowsPerTile = 64 / kLanesPerRow;    // 8 rows per wave
+constexpr int kTilesPerHead = D / kRowsPerTile;    // 16
 // 1/sqrt(128) rounded to binary32; the output is scaled by it.
 constexpr float kInvSqrtD = 0.08838834764831845f;
 
 // ----------------------------------------------------------------- helpers
-// DPP move within a quad; CTRL is a quad_perm selector.
+// DPP move; CTRL is a row_half_mirror or quad_perm selector.
 template <int CTRL>
-__device__ __forceinline__ float dpp_quad(float x) {
+__device__ __forceinline__ float dpp(float x) {
     return __builtin_bit_cast(
         float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over the 4 lanes of a quad; every lane of the quad gets the same bits.
-__device__ __forceinline__ float quad_sum(float x) {
-    x = x + dpp_quad<0xB1>(x);  // quad_perm [1,0,3,2]: partner lane c^1
-    x = x + dpp_quad<0x4E>(x);  // quad_perm [2,3,0,1]: partner lane c^2
+// Sum over the 8 lanes of a row group; every lane gets the same bits
+// (each step adds a value to its partner's copy of the same value).
+__device__ __forceinline__ float group_sum(float x) {
+    x = x + dpp<0x141>(x);   // row_half_mirror: lane i <-> 7-i within 8
+    x = x + dpp<0xB1>(x);    // quad_perm [1,0,3,2]: lane c^1
+    x = x + dpp<0x4E>(x);    // quad_perm [2,3,0,1]: lane c^2
     return x;
 }
 
-struct RowSlice {   // the 32 state elements of one row that this lane owns
-    float4 m[kF4PerLane];
+struct RowSlice {   // the 16 state elements of one row that this lane owns
+    f4 m[kF4PerLane];
 };
-struct VecSlice {   // the matching 32 entries of k or q
-    float4 x[kF4PerLane];
+struct VecSlice {   // the matching 16 entries of k or q
+    f4 x[kF4PerLane];
 };
 
+// State rows are streamed with nontemporal loads and stores when NT: they
+// are touched once per call and need not displace other data in the caches.
+template <bool NT>
 __device__ __forceinline__ void load_row(RowSlice &r, const float *row, int c) {
-    const float4 *p = reinterpret_cast<const float4 *>(row);
+    const f4 *p = reinterpret_cast<const f4 *>(row);
 #pragma unroll
-    for (int i = 0; i < kF4PerLane; ++i) r.m[i] = p[4 * i + c];
+    for (int i = 0; i < kF4PerLane; ++i) {
+        if constexpr (NT)
+            r.m[i] = __builtin_nontemporal_load(p + kLanesPerRow * i + c);
+        else
+            r.m[i] = p[kLanesPerRow * i + c];
+    }
 }
 
+template <bool NT>
 __device__ __forceinline__ void store_row(float *row, const RowSlice &r, int c) {
-    float4 *p = reinterpret_cast<float4 *>(row);
+    f4 *p = reinterpret_cast<f4 *>(row);
 #pragma unroll
-    for (int i = 0; i < kF4PerLane; ++i) p[4 * i + c] = r.m[i];
+    for (int i = 0; i < kF4PerLane; ++i) {
+        if constexpr (NT)
+            __builtin_nontemporal_store(r.m[i], p + kLanesPerRow * i + c);
+        else
+            p[kLanesPerRow * i + c] = r.m[i];
+    }
 }
 
 __device__ __forceinline__ void load_vec(VecSlice &v, const float *src, int c) {
-    const float4 *p = reinterpret_cast<const float4 *>(src);
+    const f4 *p = reinterpret_cast<const f4 *>(src);
 #pragma unroll
-    for (int i = 0; i < kF4PerLane; ++i) v.x[i] = p[4 * i + c];
+    for (int i = 0; i < kF4PerLane; ++i) v.x[i] = p[kLanesPerRow * i + c];
 }
 
-// This lane's partial of dot(row, w): a sequential FMA chain over its 32 columns.
+// This lane's partial of dot(row, w): a sequential FMA chain over its 16 columns.
 __device__ __forceinline__ float dot_part(const RowSlice &r, const VecSlice &w) {
     float p = 0.0f;
 #pragma unroll
@@ -104,7 +123,7 @@ __device__ __forceinline__ float row_token(RowSlice &r, const VecSlice &k, const
         r.m[i].z *= e;
         r.m[i].w *= e;
     }
-    const float sk = quad_sum(dot_part(r, k));        // 2. sk = M[j] . k
+    const float sk = group_sum(dot_part(r, k));       // 2. sk = M[j] . k
     const float d = (vj - sk) * beta;                 // 3. delta
 #pragma unroll
     for (int i = 0; i < kF4PerLane; ++i) {           // 4. rank-1 update
@@ -113,71 +132,64 @@ __device__ __forceinline__ float row_token(RowSlice &r, const VecSlice &k, const
         r.m[i].z = fmaf(d, k.x[i].z, r.m[i].z);
         r.m[i].w = fmaf(d, k.x[i].w, r.m[i].w);
     }
-    return quad_sum(dot_part(r, q)) * kInvSqrtD;      // 5. output, updated state
+    return group_sum(dot_part(r, q)) * kInvSqrtD;     // 5. output, updated state
 }
 
 // ------------------------------------------------------------- gdn_step
-// One workgroup = kWaves waves x kTiles tiles x 16 rows.  With kTiles = 2 a
-// workgroup is exactly one head (128 rows, 64 KiB of state): all 16 state
-// loads of a lane are issued before any arithmetic, so a workgroup keeps
-// 64 KiB in flight.
+// HBM-bound: the state is streamed once in and once out.  A persistent grid
+// of kStepWaves-wave workgroups walks the tiles (8 rows = 4 KiB each) of all
+// heads in a grid-stride loop, one tile per wave per iteration, so the
+// addresses in flight at any moment form one contiguous window of a few MiB
+// that advances through the state (this keeps DRAM pages open; measured on
+// MI355X it beats one workgroup per head and deeper per-wave queues).
+// Workgroup g runs on XCD g % 8; the tile order is remapped so that the 16
+// tiles of a head go to workgroups of one XCD and its k and q are fetched
+// into one L2 only.
 constexpr int kStepWaves = 4;
-constexpr int kStepTiles = 2;
-constexpr int kStepRowsPerWG = kStepWaves * kStepTiles * kRowsPerTile;  // 128
-static_assert(kStepRowsPerWG == D, "one head per workgroup");
+constexpr int kXcds = 8;
 
-__global__ __launch_bounds__(kStepWaves * 64) void k_step(StepArgs a) {
+__global__ __launch_bounds__(kStepWaves * 64) void k_step(StepArgs a, int n_tiles) {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int quad = lane >> 2;
-    const int c = lane & 3;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = lane >> 3;
+    const int c = lane & 7;
 
-    // head = b * Hv + h; the host guarantees B * Hv fits in 31 bits
-    const unsigned hd = blockIdx.x;
-    const unsigned bu = hd / static_cast<unsigned>(a.Hv);
-    const int h = static_cast<int>(hd - bu * static_cast<unsigned>(a.Hv));
-    const int kh = h % a.Hk;                      // key-head broadcast
-    const int64_t head = hd;
-    const int64_t b = bu;
+    const int G = gridDim.x;
+    const int g = blockIdx.x;
+    const int lg = (G % kXcds == 0) ? (g % kXcds) * (G / kXcds) + g / kXcds : g;
+    const int stride = G * kStepWaves;
 
-    float *M = a.state + head * (D * D);
-    int rows[kStepTiles];
-    RowSlice r[kStepTiles];
-#pragma unroll
-    for (int t = 0; t < kStepTiles; ++t) {
-        rows[t] = (wave * kStepTiles + t) * kRowsPerTile + quad;
-        load_row(r[t], M + rows[t] * D, c);
-    }
+    for (int u = lg * kStepWaves + wave; u < n_tiles; u += stride) {
+        const int head = u / kTilesPerHead;                   // b * Hv + h
+        const int row = (u % kTilesPerHead) * kRowsPerTile + grp;
+        const int b = head / a.Hv;
+        const int h = head - b * a.Hv;
+        const int kh = h % a.Hk;                              // key-head broadcast
 
-    VecSlice kv, qv;
-    load_vec(kv, a.k + b * a.qk_bstride + kh * D, c);
-    load_vec(qv, a.q + b * a.qk_bstride + kh * D, c);
-    const float e = expf(a.gate[head]);
-    const float bt = a.beta[head];
-    const float *vh = a.v + b * a.v_bstride + static_cast<int64_t>(h) * D;
-    float vj[kStepTiles];
-#pragma unroll
-    for (int t = 0; t < kStepTiles; ++t) vj[t] = vh[rows[t]];
+        float *Mrow = a.state + static_cast<int64_t>(head) * (D * D) + row * D;
+        RowSlice r;
+        load_row<true>(r, Mrow, c);
+        VecSlice kv, qv;
+        load_vec(kv, a.k + b * a.qk_bstride + kh * D, c);
+        load_vec(qv, a.q + b * a.qk_bstride + kh * D, c);
+        const float e = expf(a.gate[head]);
+        const float bt = a.beta[head];
+        const float vj = a.v[b * a.v_bstride + h * D + row];
 
-    float *out = a.out + head * D;
-#pragma unroll
-    for (int t = 0; t < kStepTiles; ++t) {
-        const float o = row_token(r[t], kv, qv, e, bt, vj[t]);
-        store_row(M + rows[t] * D, r[t], c);
-        if (c == 0) out[rows[t]] = o;
+        const float o = row_token(r, kv, qv, e, bt, vj);
+        store_row<true>(Mrow, r, c);
+        if (c == 0) a.out[static_cast<int64_t>(head) * D + row] = o;
     }
 }
 
 // -------------------------------------------------------------- gdn_seq
-// One workgroup per (sequence, value head): 8 waves x one 16-row tile each,
-// so the whole 64 KiB head state lives in VGPRs (32 floats per lane) for all
-// T tokens and is read and written once per call.  The per-token inputs
-// (k, q, v, gate, beta: 1.5 KiB per token) are staged through LDS in chunks
-// of kChunk tokens, double-buffered: the global loads of chunk c+1 are issued
-// before chunk c is computed and written to LDS after it, so their latency
-// hides behind kChunk tokens of arithmetic and there is one barrier per chunk.
-constexpr int kSeqWaves = D / kRowsPerTile;   // 8
-constexpr int kSeqThreads = kSeqWaves * 64;   // 512
+// One workgroup per (sequence, value head): kSeqWaves waves x TPW tiles, so
+// the whole 64 KiB head state lives in VGPRs for all T tokens and is read and
+// written once per call.  The per-token inputs (k, q, v, gate, beta: 1.5 KiB
+// per token) are staged through LDS in chunks of kChunk tokens,
+// double-buffered: the global loads of chunk c+1 are issued before chunk c
+// is computed and written to LDS after it, so their latency hides behind
+// kChunk tokens of arithmetic and there is one barrier per chunk.
 constexpr int kChunk = 16;
 
 struct alignas(16) TokenLds {
@@ -193,24 +205,25 @@ static_assert(sizeof(TokenLds) % 16 == 0, "float4 aligned token slots");
 // float4 loads needed per token: k (32) + q (32) + v (32)
 constexpr int kTokF4 = 3 * D / 4;
 constexpr int kChunkF4 = kChunk * kTokF4;                    // 1536
-constexpr int kF4PerThread = (kChunkF4 + kSeqThreads - 1) / kSeqThreads;  // 3
-static_assert(kChunkF4 % kSeqThreads == 0, "even staging split");
 
+template <int THREADS>
 struct ChunkRegs {
-    float4 f[kF4PerThread];
+    static constexpr int kPer = (kChunkF4 + THREADS - 1) / THREADS;
+    f4 f[kPer];
     float s;   // gate or beta of one token (threads 0 .. 2*kChunk-1)
 };
 
-__device__ __forceinline__ void seq_fetch(ChunkRegs &cr, const SeqArgs &a, int64_t b, int h,
-                                          int kh, int t0, int tid) {
+template <int THREADS>
+__device__ __forceinline__ void seq_fetch(ChunkRegs<THREADS> &cr, const SeqArgs &a, int64_t b,
+                                          int h, int kh, int t0, int tid) {
 #pragma unroll
-    for (int j = 0; j < kF4PerThread; ++j) {
-        const int e = tid + j * kSeqThreads;
+    for (int j = 0; j < ChunkRegs<THREADS>::kPer; ++j) {
+        const int e = tid + j * THREADS;
         const int tt = e / kTokF4;
         const int w = e - tt * kTokF4;
         const int t = t0 + tt;
-        float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (t < a.T) {
+        f4 val = {0.f, 0.f, 0.f, 0.f};
+        if (e < kChunkF4 && t < a.T) {
             const int64_t bt = b * a.T + t;
             const float *src;
             if (w < 32)
@@ -219,7 +232,7 @@ __device__ __forceinline__ void seq_fetch(ChunkRegs &cr, const SeqArgs &a, int64
                 src = a.q + (bt * a.Hk + kh) * D + 4 * (w - 32);
             else
                 src = a.v + (bt * a.Hv + h) * D + 4 * (w - 64);
-            val = *reinterpret_cast<const float4 *>(src);
+            val = *reinterpret_cast<const f4 *>(src);
         }
         cr.f[j] = val;
     }
@@ -234,16 +247,19 @@ __device__ __forceinline__ void seq_fetch(ChunkRegs &cr, const SeqArgs &a, int64
     }
 }
 
-__device__ __forceinline__ void seq_stage(TokenLds *buf, const ChunkRegs &cr, int tid) {
+template <int THREADS>
+__device__ __forceinline__ void seq_stage(TokenLds *buf, const ChunkRegs<THREADS> &cr, int tid) {
 #pragma unroll
-    for (int j = 0; j < kF4PerThread; ++j) {
-        const int e = tid + j * kSeqThreads;
-        const int tt = e / kTokF4;
-        const int w = e - tt * kTokF4;
-        float *dst = w < 32 ? buf[tt].k + 4 * w
-                   : w < 64 ? buf[tt].q + 4 * (w - 32)
-                            : buf[tt].v + 4 * (w - 64);
-        *reinterpret_cast<float4 *>(dst) = cr.f[j];
+    for (int j = 0; j < ChunkRegs<THREADS>::kPer; ++j) {
+        const int e = tid + j * THREADS;
+        if (e < kChunkF4) {
+            const int tt = e / kTokF4;
+            const int w = e - tt * kTokF4;
+            float *dst = w < 32 ? buf[tt].k + 4 * w
+                       : w < 64 ? buf[tt].q + 4 * (w - 32)
+                                : buf[tt].v + 4 * (w - 64);
+            *reinterpret_cast<f4 *>(dst) = cr.f[j];
+        }
     }
     if (tid < kChunk)
         buf[tid].gate = cr.s;
@@ -251,36 +267,41 @@ __device__ __forceinline__ void seq_stage(TokenLds *buf, const ChunkRegs &cr, in
         buf[tid - kChunk].beta = cr.s;
 }
 
-__global__ __launch_bounds__(kSeqThreads) void k_seq(SeqArgs a) {
+template <int TPW>   // tiles (8 rows each) per wave
+__global__ __launch_bounds__((kTilesPerHead / TPW) * 64) void k_seq(SeqArgs a) {
+    constexpr int kWaves = kTilesPerHead / TPW;
+    constexpr int kThreads = kWaves * 64;
     __shared__ TokenLds lds[2][kChunk];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int quad = lane >> 2;
-    const int c = lane & 3;
+    const int grp = lane >> 3;
+    const int c = lane & 7;
 
-    const unsigned hd = blockIdx.x;               // b * Hv + h
-    const unsigned bu = hd / static_cast<unsigned>(a.Hv);
-    const int h = static_cast<int>(hd - bu * static_cast<unsigned>(a.Hv));
+    const int head = blockIdx.x;                  // b * Hv + h
+    const int b = head / a.Hv;
+    const int h = head - b * a.Hv;
     const int kh = h % a.Hk;
-    const int64_t head = hd;
-    const int64_t b = bu;
-    const int row = wave * kRowsPerTile + quad;
 
-    float *Mrow = a.state + head * (D * D) + row * D;
-    RowSlice r;
-    load_row(r, Mrow, c);
+    float *M = a.state + static_cast<int64_t>(head) * (D * D);
+    int rows[TPW];
+    RowSlice r[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        rows[t] = (wave * TPW + t) * kRowsPerTile + grp;
+        load_row<false>(r[t], M + rows[t] * D, c);
+    }
 
-    ChunkRegs cr;
-    seq_fetch(cr, a, b, h, kh, 0, tid);
-    seq_stage(lds[0], cr, tid);
+    ChunkRegs<kThreads> cr;
+    seq_fetch<kThreads>(cr, a, b, h, kh, 0, tid);
+    seq_stage<kThreads>(lds[0], cr, tid);
     __syncthreads();
 
     const int n_chunks = (a.T + kChunk - 1) / kChunk;
     for (int ch = 0; ch < n_chunks; ++ch) {
         const bool more = ch + 1 < n_chunks;
-        if (more) seq_fetch(cr, a, b, h, kh, (ch + 1) * kChunk, tid);
+        if (more) seq_fetch<kThreads>(cr, a, b, h, kh, (ch + 1) * kChunk, tid);
 
         const TokenLds *buf = lds[ch & 1];
         const int t0 = ch * kChunk;
@@ -291,16 +312,21 @@ __global__ __launch_bounds__(kSeqThreads) void k_seq(SeqArgs a) {
             load_vec(kv, tok.k, c);
             load_vec(qv, tok.q, c);
             const float e = expf(tok.gate);
-            const float o = row_token(r, kv, qv, e, tok.beta, tok.v[row]);
-            if (c == 0) a.out[((b * a.T + t0 + tt) * a.Hv + h) * D + row] = o;
+            const int64_t ob = ((static_cast<int64_t>(b) * a.T + t0 + tt) * a.Hv + h) * D;
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const float o = row_token(r[t], kv, qv, e, tok.beta, tok.v[rows[t]]);
+                if (c == 0) a.out[ob + rows[t]] = o;
+            }
         }
 
         if (more) {
-            seq_stage(lds[(ch + 1) & 1], cr, tid);
+            seq_stage<kThreads>(lds[(ch + 1) & 1], cr, tid);
             __syncthreads();
         }
     }
-    store_row(Mrow, r, c);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) store_row<false>(M + rows[t] * D, r[t], c);
 }
 
 // --------------------------------------------------------- tail kernels
@@ -373,15 +399,42 @@ __global__ __launch_bounds__(kNormThreads) void k_gated_norm(GatedNormArgs a) {
 }  // namespace
 
 // ---------------------------------------------------------------- launch
+#ifndef GDN_STEP_WGS_PER_CU
+#define GDN_STEP_WGS_PER_CU 2
+#endif
+#ifndef GDN_SEQ_TILES_PER_WAVE
+#define GDN_SEQ_TILES_PER_WAVE 2
+#endif
+
+// Compute units of the current device (read once per device; a value that
+// never changes, so concurrent first calls race harmlessly).
+static int device_cus() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
 hipError_t launch_step(const StepArgs &a, hipStream_t s) {
-    const int64_t heads = static_cast<int64_t>(a.B) * a.Hv;
-    k_step<<<dim3(static_cast<unsigned>(heads)), dim3(kStepWaves * 64), 0, s>>>(a);
+    const int64_t tiles = static_cast<int64_t>(a.B) * a.Hv * kTilesPerHead;
+    const int64_t full = device_cus() * static_cast<int64_t>(GDN_STEP_WGS_PER_CU);
+    const int64_t need = (tiles + kStepWaves - 1) / kStepWaves;
+    const int grid = static_cast<int>(need < full ? need : full);
+    k_step<<<dim3(grid), dim3(kStepWaves * 64), 0, s>>>(a, static_cast<int>(tiles));
     return hipGetLastError();
 }
 
 hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
+    constexpr int tpw = GDN_SEQ_TILES_PER_WAVE;
     const int64_t heads = static_cast<int64_t>(a.B) * a.Hv;
-    k_seq<<<dim3(static_cast<unsigned>(heads)), dim3(kSeqThreads), 0, s>>>(a);
+    k_seq<tpw><<<dim3(static_cast<unsigned>(heads)), dim3((kTilesPerHead / tpw) * 64), 0, s>>>(a);
     return hipGetLastError();
 }
 
