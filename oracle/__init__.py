@@ -63,13 +63,14 @@ class Oracle:
         L.oracle_gdn_step_S.argtypes = L.oracle_gdn_step_M.argtypes
         L.oracle_gdn_step_f64.argtypes = [_i32, *dims5[1:], *vec5, _f64p, _f64p]
         L.oracle_gdn_seq.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, *vec5, _f32p, _f32p]
+        L.oracle_gdn_pair.argtypes = [_i32, *dims5[1:], *vec5, _f32p, _f32p, _f32p]
         L.oracle_conv_silu.argtypes = [_i32, _i32, _i32, _f32p, _f32p, _f32p, _f32p]
         L.oracle_l2norm_rows.argtypes = [_i32, _i32, _f32p]
         L.oracle_gated_rmsnorm.argtypes = [_i32, _i32, _i32, ctypes.c_float,
                                            _f32p, _f32p, _f32p, _f32p]
         L.oracle_layer_tail.argtypes = [_i32] * 7 + [ctypes.c_float] + [_f32p] * 11
         for name in ("oracle_gdn_step_M", "oracle_gdn_step_S", "oracle_gdn_step_f64",
-                     "oracle_gdn_seq", "oracle_conv_silu", "oracle_l2norm_rows",
+                     "oracle_gdn_seq", "oracle_gdn_pair", "oracle_conv_silu", "oracle_l2norm_rows",
                      "oracle_gated_rmsnorm", "oracle_layer_tail"):
             getattr(L, name).restype = None
         self.lib = L
@@ -125,6 +126,20 @@ class Oracle:
         self.lib.oracle_gdn_seq(B, T, Hv, Hk, dk, dv, _p32(q), _p32(k), _p32(v),
                                 _p32(beta), _p32(gate), _p32(M), _p32(out))
         return out
+
+    def pair(self, q, k, v, beta, gate, M):
+        """[linear_core] gdn_pair: q,k [B][2][Hk][dk], v [B][2][Hv][dv],
+        beta/gate [B][2][Hv].  M is committed in place (position 1); returns
+        (out [B][2][Hv][dv], M_next) with M_next the tentative state."""
+        B, two, Hk, dk = q.shape
+        assert two == 2
+        _, _, Hv, dv = v.shape
+        assert M.shape == (B, Hv, dv, dk)
+        out = np.empty((B, 2, Hv, dv), np.float32)
+        Mn = np.empty_like(M)
+        self.lib.oracle_gdn_pair(B, Hv, Hk, dk, dv, _p32(q), _p32(k), _p32(v),
+                                 _p32(beta), _p32(gate), _p32(M), _p32(Mn), _p32(out))
+        return out, Mn
 
     # -- tail stages ------------------------------------------------------
     def conv_silu(self, x, conv_w, conv_state):

@@ -233,6 +233,36 @@ void oracle_gdn_seq(int32_t B, int32_t T, int32_t Hv, int32_t Hk, int32_t dk, in
     }
 }
 
+/* [linear_core] gdn_pair: position 1 is an ordinary step on the committed
+ * state; position 2 is a step on a copy of the result (the tentative lane). */
+void oracle_gdn_pair(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv,
+                     const float *q, const float *k, const float *v,
+                     const float *beta, const float *gate,
+                     float *M, float *M_next, float *out)
+{
+    int32_t b, h, p;
+    for (b = 0; b < B; ++b) {
+        for (h = 0; h < Hv; ++h) {
+            const int32_t kh = key_head_of(h, Hk);
+            float *Mh = M + ((size_t)b * Hv + h) * dv * dk;
+            float *Nh = M_next + ((size_t)b * Hv + h) * dv * dk;
+            for (p = 0; p < 2; ++p) {
+                const size_t bp = (size_t)b * 2 + p;
+                if (p == 1)
+                    memcpy(Nh, Mh, (size_t)dv * dk * sizeof(float));
+                head_step_M(dk, dv,
+                            q + (bp * Hk + kh) * dk,
+                            k + (bp * Hk + kh) * dk,
+                            v + (bp * Hv + h) * dv,
+                            beta[bp * Hv + h], gate[bp * Hv + h],
+                            p == 0 ? Mh : Nh,
+                            out + (bp * Hv + h) * dv,
+                            NULL);
+            }
+        }
+    }
+}
+
 static float silu(float x) { return x / (1.0f + expf(-x)); }
 
 /*

@@ -76,6 +76,16 @@ void oracle_gdn_seq(int32_t B, int32_t T, int32_t Hv, int32_t Hk, int32_t dk, in
                     const float *beta, const float *gate,
                     float *M, float *out);
 
+/* [linear_core] gdn_pair: two positions fused for speculative verification.
+ * Position 1 commits into M; position 2 starts from that committed state and
+ * its state goes to M_next (tentative), leaving M as after position 1.
+ *   q, k [B][2][Hk][dk]; v [B][2][Hv][dv]; beta, gate [B][2][Hv]
+ *   M [B][Hv][dv][dk] in/out; M_next [B][Hv][dv][dk] out; out [B][2][Hv][dv] */
+void oracle_gdn_pair(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv,
+                     const float *q, const float *k, const float *v,
+                     const float *beta, const float *gate,
+                     float *M, float *M_next, float *out);
+
 /* [dev15a] "conv-state shift, real F32 ssm_conv1d, SiLU" for one token.
  *   x          [B][C]        raw pre-conv channels of this token
  *   conv_w     [C][K]        tap 0 is applied to the oldest input

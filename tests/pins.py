@@ -240,6 +240,41 @@ def pin_seq_is_repeated_step(o):
     assert np.array_equal(Ms, Mr), "seq final state differs from repeated steps"
 
 
+def pin_pair_is_commit_then_tentative_step(o):
+    """linear_core gdn_pair: position 1 commits (the state equals one step),
+    position 2 runs from the committed state into the tentative buffer (it
+    equals the two-position sequence), and the outputs are those of the
+    two-position sequence - bitwise.  With d = 1, k = +-1 both positions also
+    follow the scalar closed form m' = (1 - beta) e m + beta v k."""
+    rng = np.random.default_rng(20)
+    B, Hv, Hk, d = 2, 4, 2, 8
+    steps = [_rand_step(rng, B, Hv, Hk, d) for _ in range(2)]
+    M0 = steps[0][5]
+    st = lambda i: np.ascontiguousarray(np.stack([steps[0][i], steps[1][i]], axis=1))
+    q, k, v, beta, gate = (st(i) for i in range(5))
+    M = M0.copy()
+    out, Mn = o.pair(q, k, v, beta, gate, M)
+    M1 = M0.copy()
+    o1 = o.step_M(*steps[0][:5], M1)
+    M2 = M0.copy()
+    o2 = o.seq(q, k, v, beta, gate, M2)
+    assert np.array_equal(M, M1), "committed state is not one step"
+    assert np.array_equal(Mn, M2), "tentative state is not the two-position sequence"
+    assert np.array_equal(out[:, 0], o1) and np.array_equal(out, o2), "pair outputs"
+    # scalar closed form
+    kk = np.array([1.0, -1.0], np.float32).reshape(1, 2, 1, 1)
+    qq = np.array([-1.0, 1.0], np.float32).reshape(1, 2, 1, 1)
+    vv = np.array([0.7, -1.3], np.float32).reshape(1, 2, 1, 1)
+    bb = np.array([0.25, 0.6], np.float32).reshape(1, 2, 1)
+    gg = np.array([-0.3, -1.1], np.float32).reshape(1, 2, 1)
+    M = np.full((1, 1, 1, 1), 0.4, np.float32)
+    out, Mn = o.pair(qq, kk, vv, bb, gg, M)
+    m1 = (1 - 0.25) * np.exp(np.float64(np.float32(-0.3))) * 0.4 + 0.25 * float(np.float32(0.7))
+    m2 = (1 - 0.6) * np.exp(np.float64(np.float32(-1.1))) * m1 + 0.6 * float(np.float32(-1.3)) * -1
+    assert abs(M[0, 0, 0, 0] - m1) <= 1e-6 and abs(Mn[0, 0, 0, 0] - m2) <= 1e-6, "scalar pair"
+    assert abs(out[0, 0, 0, 0] - (-m1)) <= 1e-6 and abs(out[0, 1, 0, 0] - m2) <= 1e-6, "scalar pair out"
+
+
 def pin_batch_invariance(o):
     """Sequences are independent: sequence b's result does not depend on the
     batch it is computed in (bitwise)."""

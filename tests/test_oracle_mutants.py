@@ -28,6 +28,8 @@ MUTANTS = [
     ("head_map_interleaved", "static int32_t key_head_of(int32_t h, int32_t Hk) { return h % Hk; }",
      "static int32_t key_head_of(int32_t h, int32_t Hk) { return (h / 2) % Hk; }"),
     ("seq_wrong_token_stride", "q + (bt * Hk + kh) * dk,", "q + ((size_t)b * Hk + kh) * dk,"),
+    ("pair_tentative_from_old_state", "if (p == 1)", "if (p == 0)"),
+    ("pair_positions_swapped", "const size_t bp = (size_t)b * 2 + p;", "const size_t bp = (size_t)b * 2 + (1 - p);"),
     ("conv_taps_reversed", "acc = acc + conv_w[(size_t)c * K + t] * win[t];",
      "acc = acc + conv_w[(size_t)c * K + (K - 1 - t)] * win[t];"),
     ("conv_cache_not_shifted", "cs[(size_t)t * C + c] = win[t + 1];", "cs[(size_t)t * C + c] = win[t];"),
