@@ -205,6 +205,20 @@ def extra_measurements(torch, g, stream):
                                     "GBps": upd * STATE_UPDATE_BYTES / (ms / 1e3) / 1e9,
                                     "note": "128 MiB state fits the 256 MB Infinity Cache"}
 
+    # gdn_pair: B=256, one layer, two positions (state read once, written twice)
+    c2 = gi.CONFIGS[2]
+    si = {n: torch.from_numpy(x).cuda() for n, x in gi.step_inputs(c2["seed"], 0, 256, T=2).items()}
+    M = torch.from_numpy(gi.state(c2["seed"], 0, 256)).cuda()
+    Mn = torch.empty_like(M)
+    o = torch.empty((256, 2, HV, D), device="cuda")
+    ms = timeit(lambda: g.pair(si["q"], si["k"], si["v"], si["beta"], si["gate"], M, Mn, o,
+                               stream=stream), 10)
+    pair_bytes = 256 * HV * (3 * D * D * 4 + 2 * (STATE_UPDATE_BYTES - 2 * D * D * 4))
+    res["pair_b256"] = {"us_per_call": ms * 1e3, "state_updates_per_s": 2 * 256 * HV / (ms / 1e3),
+                        "GBps": pair_bytes / (ms / 1e3) / 1e9,
+                        "bytes_per_call": pair_bytes}
+    del M, Mn
+
     # config 3: gdn_seq B=8 x T=4096 from a zero state
     c3 = gi.CONFIGS[3]
     si = {n: torch.from_numpy(x).cuda() for n, x in gi.step_inputs(c3["seed"], 0, 8, T=4096).items()}

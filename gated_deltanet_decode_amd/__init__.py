@@ -6,6 +6,7 @@ C entry points:
 
     step(q, k, v, beta, gate, state, out)        -> gdn_step
     seq(q, k, v, beta, gate, state, out)         -> gdn_seq
+    pair(q, k, v, beta, gate, state, state_next, out) -> gdn_pair
     layer_tail(x, conv_w, conv_state, beta, gate, state, z, norm_w, y, ...)
                                                  -> gdn_layer_tail
     layer_tail_workspace_bytes(B)                -> gdn_layer_tail_workspace_bytes
@@ -21,7 +22,7 @@ import os
 
 from ._build import LIBRARY
 
-__all__ = ["GdnError", "Dims", "TailParams", "lib", "step", "seq", "layer_tail",
+__all__ = ["GdnError", "Dims", "TailParams", "lib", "step", "seq", "pair", "layer_tail",
            "layer_tail_workspace_bytes", "last_error", "version", "PAGE_DIMS",
            "PAGE_TAIL", "ERRORS"]
 
@@ -62,6 +63,8 @@ lib.gdn_step.restype = ctypes.c_int
 lib.gdn_step.argtypes = [_DP, _i32] + [_vp] * 7 + [_vp]
 lib.gdn_seq.restype = ctypes.c_int
 lib.gdn_seq.argtypes = [_DP, _i32, _i32] + [_vp] * 7 + [_vp]
+lib.gdn_pair.restype = ctypes.c_int
+lib.gdn_pair.argtypes = [_DP, _i32] + [_vp] * 8 + [_vp]
 lib.gdn_layer_tail.restype = ctypes.c_int
 lib.gdn_layer_tail.argtypes = [_DP, _TP, _i32] + [_vp] * 11 + [_vp, ctypes.c_size_t, _vp]
 lib.gdn_layer_tail_workspace_bytes.restype = ctypes.c_size_t
@@ -145,6 +148,23 @@ def seq(q, k, v, beta, gate, state, out, stream=None) -> None:
         _ptr(beta, "beta", (B, T, d.n_v_heads)), _ptr(gate, "gate", (B, T, d.n_v_heads)),
         _ptr(state, "state", (B, d.n_v_heads, d.d_v, d.d_k)),
         _ptr(out, "out", (B, T, d.n_v_heads, d.d_v)), _stream(stream)))
+
+
+def pair(q, k, v, beta, gate, state, state_next, out, stream=None) -> None:
+    """gdn_pair: q,k [B][2][Hk][dk], v [B][2][Hv][dv], beta/gate [B][2][Hv];
+    state [B][Hv][dv][dk] is committed with position 1 in place;
+    state_next (same shape) receives the tentative state after position 2;
+    out [B][2][Hv][dv]."""
+    B = q.shape[0]
+    d = _dims_of(q, v)
+    _check(lib.gdn_pair(
+        ctypes.byref(d), B,
+        _ptr(q, "q", (B, 2, d.n_k_heads, d.d_k)), _ptr(k, "k", (B, 2, d.n_k_heads, d.d_k)),
+        _ptr(v, "v", (B, 2, d.n_v_heads, d.d_v)),
+        _ptr(beta, "beta", (B, 2, d.n_v_heads)), _ptr(gate, "gate", (B, 2, d.n_v_heads)),
+        _ptr(state, "state", (B, d.n_v_heads, d.d_v, d.d_k)),
+        _ptr(state_next, "state_next", (B, d.n_v_heads, d.d_v, d.d_k)),
+        _ptr(out, "out", (B, 2, d.n_v_heads, d.d_v)), _stream(stream)))
 
 
 def layer_tail_workspace_bytes(B: int, dims: Dims = PAGE_DIMS) -> int:

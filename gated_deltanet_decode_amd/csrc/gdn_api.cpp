@@ -67,12 +67,14 @@ int check_dims(const gdn_dims *d) {
     return GDN_OK;
 }
 
-// Heads of one call map to workgroups along grid x.
+// Heads of one call map to workgroups along grid x, and the persistent
+// kernels count 16 row tiles per head in a 32-bit index.
 int check_batch(const gdn_dims *d, int64_t B, const char *what) {
     if (B < 1) return fail(GDN_ERR_SHAPE, "%s must be >= 1 (got %lld)", what, (long long)B);
-    if (B * d->n_v_heads > INT32_MAX)
-        return fail(GDN_ERR_SHAPE, "B * n_v_heads = %lld exceeds %d", (long long)(B * d->n_v_heads),
-                    INT32_MAX);
+    const int64_t limit = INT32_MAX / 16;
+    if (B * d->n_v_heads > limit)
+        return fail(GDN_ERR_SHAPE, "B * n_v_heads = %lld exceeds %lld",
+                    (long long)(B * d->n_v_heads), (long long)limit);
     return GDN_OK;
 }
 
@@ -178,6 +180,44 @@ int gdn_seq(const gdn_dims *dims, int32_t B, int32_t T, const float *q, const fl
     a.Hk = dims->n_k_heads;
     (void)hipGetLastError();
     return hip_status(gdn::launch_seq(a, static_cast<hipStream_t>(stream)), "gdn_seq launch");
+}
+
+int gdn_pair(const gdn_dims *dims, int32_t B, const float *q, const float *k, const float *v,
+             const float *beta, const float *gate, float *state, float *state_next, float *out,
+             void *stream) {
+    clear_error();
+    GDN_TRY(check_dims(dims));
+    GDN_TRY(check_batch(dims, B, "B"));
+    const size_t f = sizeof(float);
+    const size_t B2 = static_cast<size_t>(B) * 2;
+    const size_t nqk = B2 * dims->n_k_heads * dims->d_k * f;
+    const size_t nv = B2 * dims->n_v_heads * dims->d_v * f;
+    const size_t nh = B2 * dims->n_v_heads * f;
+    const size_t ns = static_cast<size_t>(B) * dims->n_v_heads * dims->d_v * dims->d_k * f;
+    const Buf vec[] = {{"q", q, nqk},     {"k", k, nqk},
+                       {"v", v, nv},      {"state", state, ns},
+                       {"out", out, nv},  {"state_next", state_next, ns}};
+    const Buf sc[] = {{"beta", beta, nh}, {"gate", gate, nh}};
+    GDN_TRY(check_ptrs(vec, 6, 16));
+    GDN_TRY(check_ptrs(sc, 2, 4));
+    const Buf all[] = {vec[0], vec[1], vec[2], vec[3], vec[4], vec[5], sc[0], sc[1]};
+    const Buf outs[] = {vec[3], vec[4], vec[5]};
+    GDN_TRY(check_alias(outs, 3, all, 8));
+
+    gdn::PairArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.gate = gate;
+    a.state = state;
+    a.state_next = state_next;
+    a.out = out;
+    a.B = B;
+    a.Hv = dims->n_v_heads;
+    a.Hk = dims->n_k_heads;
+    (void)hipGetLastError();
+    return hip_status(gdn::launch_pair(a, static_cast<hipStream_t>(stream)), "gdn_pair launch");
 }
 
 size_t gdn_layer_tail_workspace_bytes(const gdn_dims *dims, int32_t B) {

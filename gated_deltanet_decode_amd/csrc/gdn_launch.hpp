@@ -42,6 +42,23 @@ struct SeqArgs {
     int32_t Hk;
 };
 
+// Two positions: position 1 commits into `state`, position 2 (computed from
+// the committed state) goes to `state_next`.  q/k [B][2][Hk][D], v/out
+// [B][2][Hv][D], beta/gate [B][2][Hv].
+struct PairArgs {
+    const float *q;
+    const float *k;
+    const float *v;
+    const float *beta;
+    const float *gate;
+    float *state;
+    float *state_next;
+    float *out;
+    int32_t B;
+    int32_t Hv;
+    int32_t Hk;
+};
+
 // conv-state shift + causal conv1d + SiLU + per-head L2 of the Q and K parts.
 struct PrestateArgs {
     const float *x;
@@ -67,6 +84,7 @@ struct GatedNormArgs {
 
 hipError_t launch_step(const StepArgs &a, hipStream_t s);
 hipError_t launch_seq(const SeqArgs &a, hipStream_t s);
+hipError_t launch_pair(const PairArgs &a, hipStream_t s);
 hipError_t launch_prestate(const PrestateArgs &a, hipStream_t s);
 hipError_t launch_gated_norm(const GatedNormArgs &a, hipStream_t s);
 

@@ -23,7 +23,8 @@
  *   - Inputs are read-only; `state` and `conv_state` are updated in place.
  *     Outputs must not overlap any input or state buffer.
  *   - Supported on the GPU path: d_k = d_v = 128, n_k_heads >= 1,
- *     n_v_heads a multiple of n_k_heads, B >= 1, T >= 1.
+ *     n_v_heads a multiple of n_k_heads, B >= 1, T >= 1,
+ *     B * n_v_heads <= 134217727.
  *   - Results are bitwise deterministic for identical inputs, independent of
  *     B and of the other sequences in the batch.  gdn_seq over T tokens is
  *     bitwise equal to T calls of gdn_step.
@@ -106,6 +107,27 @@ int gdn_seq(const gdn_dims *dims, int32_t B, int32_t T,
             const float *q, const float *k, const float *v,
             const float *beta, const float *gate,
             float *state, float *out, void *stream);
+
+/*
+ * gdn_pair - two consecutive positions for B sequences, fused for speculative
+ * verification (docs.rs "Module linear_core", gdn_pair: lane 1 commits into
+ * the state, lane 2 is tentative in scratch).  Position 1 advances `state`
+ * in place (committed); position 2 advances the committed state into
+ * `state_next` (tentative: the caller adopts it on acceptance, e.g. by
+ * swapping the buffers, or drops it on rejection).
+ *   q, k        [B][2][n_k_heads][d_k]     position 1 then position 2
+ *   v           [B][2][n_v_heads][d_v]
+ *   beta, gate  [B][2][n_v_heads]
+ *   state       [B][n_v_heads][d_v][d_k]   in: before position 1, out: after it
+ *   state_next  [B][n_v_heads][d_v][d_k]   out: after position 2 (caller-owned)
+ *   out         [B][2][n_v_heads][d_v]
+ * The state is read once and written twice.  Results are bitwise equal to
+ * gdn_step on position 1 and to gdn_seq over both positions.
+ */
+int gdn_pair(const gdn_dims *dims, int32_t B,
+             const float *q, const float *k, const float *v,
+             const float *beta, const float *gate,
+             float *state, float *state_next, float *out, void *stream);
 
 /*
  * gdn_layer_tail - the recurrent branch around the step for one token

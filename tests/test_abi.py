@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(g):
     names = declared_functions()
-    assert {"gdn_step", "gdn_seq", "gdn_layer_tail", "gdn_layer_tail_workspace_bytes",
+    assert {"gdn_step", "gdn_seq", "gdn_pair", "gdn_layer_tail", "gdn_layer_tail_workspace_bytes",
             "gdn_last_error", "gdn_version"} <= set(names)
     for n in names:
         assert hasattr(g.lib, n), f"{n} not exported"
@@ -104,6 +104,23 @@ def test_seq_validation(g):
     expect(g, f(1, dict(a, out=a["state"] - 16)), -4, "out")
     # the fake layout is sized for T = 1: with T = 4, k runs into the state
     expect(g, f(4, a), -4, "state")
+
+
+def test_pair_validation(g):
+    a, sz = addrs()
+    d = g.Dims(HV, HK, D, D)
+    nxt = BASE + (1 << 36)
+
+    def f(aa, n=nxt, Bv=1):
+        return g.lib.gdn_pair(ctypes.byref(d), Bv, aa["q"], aa["k"], aa["v"], aa["beta"],
+                              aa["gate"], aa["state"], n, aa["out"], None)
+    expect(g, f(a, n=None), -1, "state_next")
+    expect(g, f(a, n=nxt + 8), -3, "state_next")
+    expect(g, f(a, n=a["state"]), -4, "state")
+    expect(g, f(a, n=a["state"] + sz["state"] // 2 - 4096), -4, "state")
+    expect(g, f(a, Bv=0), -2, "B")
+    # with B = 1 the two positions fill exactly the B = 2 single-step slots
+    expect(g, f(dict(a, out=a["k"])), -4, "out")
 
 
 def test_tail_validation(g):
