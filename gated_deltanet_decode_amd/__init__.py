@@ -40,11 +40,11 @@ class Dims(ctypes.Structure):
 class TailParams(ctypes.Structure):
     """gdn_tail_params"""
     _fields_ = [("conv_kernel", ctypes.c_int32), ("norm_group", ctypes.c_int32),
-                ("norm_eps", ctypes.c_float)]
+                ("norm_eps", ctypes.c_float), ("force_unfused", ctypes.c_int32)]
 
 
 PAGE_DIMS = Dims(32, 16, 128, 128)
-PAGE_TAIL = TailParams(4, 128, 1e-6)
+PAGE_TAIL = TailParams(4, 128, 1e-6, 0)
 
 ERRORS = {0: "GDN_OK", -1: "GDN_ERR_NULL", -2: "GDN_ERR_SHAPE", -3: "GDN_ERR_ALIGN",
           -4: "GDN_ERR_ALIAS", -5: "GDN_ERR_WORKSPACE", -6: "GDN_ERR_HIP"}

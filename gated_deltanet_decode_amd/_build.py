@@ -20,6 +20,9 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Wall", "-Wno-unused-command-line-argument",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # arithmetic exactly as written (explicit fmaf where a fused multiply-add
+    # is wanted), so kernels that share a formula give the same bits
+    "-ffp-contract=off",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

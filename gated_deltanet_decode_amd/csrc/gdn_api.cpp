@@ -291,6 +291,29 @@ int gdn_layer_tail(const gdn_dims *dims, const gdn_tail_params *params, int32_t 
     const hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
 
+    if (!params->force_unfused &&
+        gdn::tail_fused_supported(dims->n_v_heads, dims->n_k_heads, K, params->norm_group)) {
+        gdn::TailFusedArgs fa{};
+        fa.x = x;
+        fa.conv_w = conv_w;
+        fa.conv_state = conv_state;
+        fa.beta = beta;
+        fa.gate = gate;
+        fa.state = state;
+        fa.z = z;
+        fa.norm_w = norm_w;
+        fa.y = y;
+        fa.dbg_qkv = dbg_qkv;
+        fa.dbg_core = dbg_core;
+        fa.B = B;
+        fa.Hv = dims->n_v_heads;
+        fa.Hk = dims->n_k_heads;
+        fa.C = static_cast<int32_t>(C);
+        fa.K = K;
+        fa.eps = params->norm_eps;
+        return hip_status(gdn::launch_tail_fused(fa, s), "gdn_layer_tail fused launch");
+    }
+
     gdn::PrestateArgs pa{};
     pa.x = x;
     pa.conv_w = conv_w;

@@ -82,7 +82,33 @@ struct GatedNormArgs {
     float eps;
 };
 
+// The whole tail in one launch (one workgroup per sequence and key head).
+struct TailFusedArgs {
+    const float *x;
+    const float *conv_w;
+    float *conv_state;
+    const float *beta;
+    const float *gate;
+    float *state;
+    const float *z;
+    const float *norm_w;
+    float *y;
+    float *dbg_qkv;    // optional
+    float *dbg_core;   // optional
+    int32_t B;
+    int32_t Hv;
+    int32_t Hk;
+    int32_t C;
+    int32_t K;
+    float eps;
+};
+
+// True when launch_tail_fused supports these sizes (value heads per key head
+// 1 or 2, conv kernel 4, gated-norm group equal to the head dimension).
+bool tail_fused_supported(int32_t Hv, int32_t Hk, int32_t K, int32_t group);
+
 hipError_t launch_step(const StepArgs &a, hipStream_t s);
+hipError_t launch_tail_fused(const TailFusedArgs &a, hipStream_t s);
 hipError_t launch_seq(const SeqArgs &a, hipStream_t s);
 hipError_t launch_pair(const PairArgs &a, hipStream_t s);
 hipError_t launch_prestate(const PrestateArgs &a, hipStream_t s);

@@ -69,11 +69,15 @@ typedef struct gdn_dims {
     int32_t d_v;       /* value dimension (state rows per head)     */
 } gdn_dims;
 
-/* Tail parameters.  The page's model: {4, 128, 1e-6f}. */
+/* Tail parameters.  The page's model: {4, 128, 1e-6f, 0}. */
 typedef struct gdn_tail_params {
-    int32_t conv_kernel; /* causal conv1d taps, 2..8; cache holds conv_kernel-1 inputs */
-    int32_t norm_group;  /* gated RMSNorm group size; must divide n_v_heads*d_v        */
-    float norm_eps;      /* added to mean(o^2) inside the square root, >= 0            */
+    int32_t conv_kernel;   /* causal conv1d taps, 2..8; cache holds conv_kernel-1 inputs */
+    int32_t norm_group;    /* gated RMSNorm group size; must divide n_v_heads*d_v        */
+    float norm_eps;        /* added to mean(o^2) inside the square root, >= 0            */
+    int32_t force_unfused; /* 0: one launch when supported (conv_kernel 4, norm_group
+                              = d_v, n_v_heads = n_k_heads or 2*n_k_heads), otherwise
+                              three; non-zero: always three launches.  Both give the
+                              same bits.                                                */
 } gdn_tail_params;
 
 /*
@@ -151,7 +155,8 @@ int gdn_pair(const gdn_dims *dims, int32_t B,
  *   dbg_qkv    [B][C] optional (NULL = skip): normalised Q | K | V fed to the step
  *   dbg_core   [B][n_v_heads][d_v] optional: step output before the gated norm
  *   workspace  device scratch of gdn_layer_tail_workspace_bytes() bytes
- *              (16-byte aligned; may be NULL when both dbg buffers are given)
+ *              (16-byte aligned; may be NULL when both dbg buffers are given;
+ *              the single-launch path leaves it untouched)
  */
 int gdn_layer_tail(const gdn_dims *dims, const gdn_tail_params *params, int32_t B,
                    const float *x, const float *conv_w, float *conv_state,

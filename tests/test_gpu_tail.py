@@ -94,6 +94,23 @@ def test_tail_other_kernel_and_group_sizes(g, orc, K, group):
     check(got, want)
 
 
+@pytest.mark.parametrize("Hv,Hk", [(32, 16), (16, 16)])
+def test_fused_and_three_launch_paths_agree_bitwise(g, orc, Hv, Hk):
+    """The single-launch tail and the three-launch tail give the same bits on
+    every output (they share the per-element arithmetic and the reduction
+    order), and both match the oracle."""
+    print(f"\n  gdn_layer_tail fused vs three launches Hv={Hv} Hk={Hk}", flush=True)
+    dims = g.Dims(Hv, Hk, 128, 128)
+    ti = gi.tail_inputs(4400 + Hv, 4, Hv, Hk)
+    M = gi.state(4400 + Hv, 0, 4, Hv)
+    fused = run_tail(g, ti, M, dims=dims, params=g.TailParams(4, 128, 1e-6, 0))
+    three = run_tail(g, ti, M, dims=dims, params=g.TailParams(4, 128, 1e-6, 1))
+    for n in ("y", "state", "conv_state", "qkv", "core"):
+        assert np.array_equal(fused[n], three[n]), f"{n} differs between the two paths"
+    want = oracle_tail(orc, ti, M, Hk=Hk)
+    check(fused, want)
+
+
 def test_tail_three_tokens_fill_the_cache(g, orc):
     """After kernel-1 = 3 tokens the conv cache holds exactly the last three
     raw inputs; the chained GPU and oracle states stay within tolerance."""
