@@ -135,6 +135,67 @@ __device__ __forceinline__ float row_token(RowSlice &r, const VecSlice &k, const
     return group_sum(dot_part(r, q)) * kInvSqrtD;     // 5. output, updated state
 }
 
+// The same arithmetic split at the token boundary, for the multi-token
+// kernel: head_part() is steps 1-2 of a token, body_part() steps 4-5, and
+// pass() runs steps 4-5 of token t and steps 1-2 of token t+1 in one sweep
+// over the row.  Every element sees exactly the operations of row_token(),
+// in the same order, and the partial sums accumulate in the same element
+// order, so the results are bitwise those of row_token().
+__device__ __forceinline__ float head_part(RowSlice &r, const VecSlice &k, float e) {
+    float p = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kF4PerLane; ++i) {
+        r.m[i].x *= e;
+        r.m[i].y *= e;
+        r.m[i].z *= e;
+        r.m[i].w *= e;
+        p = fmaf(r.m[i].x, k.x[i].x, p);
+        p = fmaf(r.m[i].y, k.x[i].y, p);
+        p = fmaf(r.m[i].z, k.x[i].z, p);
+        p = fmaf(r.m[i].w, k.x[i].w, p);
+    }
+    return p;
+}
+
+__device__ __forceinline__ float body_part(RowSlice &r, float d, const VecSlice &k,
+                                           const VecSlice &q) {
+    float o = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kF4PerLane; ++i) {
+        r.m[i].x = fmaf(d, k.x[i].x, r.m[i].x);
+        r.m[i].y = fmaf(d, k.x[i].y, r.m[i].y);
+        r.m[i].z = fmaf(d, k.x[i].z, r.m[i].z);
+        r.m[i].w = fmaf(d, k.x[i].w, r.m[i].w);
+        o = fmaf(r.m[i].x, q.x[i].x, o);
+        o = fmaf(r.m[i].y, q.x[i].y, o);
+        o = fmaf(r.m[i].z, q.x[i].z, o);
+        o = fmaf(r.m[i].w, q.x[i].w, o);
+    }
+    return o;
+}
+
+// Steps 4-5 of token t (delta d, k, q) and steps 1-2 of token t+1 (decay en,
+// key kn): this lane's output partial of t goes to o, its key partial of t+1
+// to p.
+__device__ __forceinline__ void pass(RowSlice &r, float d, const VecSlice &k, const VecSlice &q,
+                                     float en, const VecSlice &kn, float &o, float &p) {
+    o = 0.0f;
+    p = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kF4PerLane; ++i) {
+#define GDN_PASS_LANE(X)                          \
+        r.m[i].X = fmaf(d, k.x[i].X, r.m[i].X);   \
+        o = fmaf(r.m[i].X, q.x[i].X, o);          \
+        r.m[i].X *= en;                           \
+        p = fmaf(r.m[i].X, kn.x[i].X, p);
+        GDN_PASS_LANE(x)
+        GDN_PASS_LANE(y)
+        GDN_PASS_LANE(z)
+        GDN_PASS_LANE(w)
+#undef GDN_PASS_LANE
+    }
+}
+
 // ------------------------------------------------------------- gdn_step
 // HBM-bound: the state is streamed once in and once out.  A persistent grid
 // of kStepWaves-wave workgroups walks the tiles (8 rows = 4 KiB each) of all
@@ -225,42 +286,59 @@ __global__ __launch_bounds__(kStepWaves * 64) void k_pair(PairArgs a, int n_tile
 }
 
 // -------------------------------------------------------------- gdn_seq
-// One workgroup per (sequence, value head): kSeqWaves waves x TPW tiles, so
-// the whole 64 KiB head state lives in VGPRs for all T tokens and is read and
-// written once per call.  The per-token inputs (k, q, v, gate, beta: 1.5 KiB
-// per token) are staged through LDS in chunks of kChunk tokens,
-// double-buffered: the global loads of chunk c+1 are issued before chunk c
-// is computed and written to LDS after it, so their latency hides behind
-// kChunk tokens of arithmetic and there is one barrier per chunk.
-constexpr int kChunk = 16;
+// One workgroup per (sequence, value head): 8 waves x 2 tiles, so the whole
+// 64 KiB head state lives in VGPRs (32 floats per lane) for all T tokens and
+// is read and written once per call.  The per-token inputs (k, q, v,
+// exp(gate), beta: 1.5 KiB per token) are staged through LDS in chunks of
+// kChunk tokens, double-buffered: the global loads of chunk c+1 are issued
+// before chunk c is computed and written to LDS after it, so their latency
+// hides behind kChunk tokens of arithmetic.  Outputs overwrite the consumed v
+// entries in LDS (row j's v is read only by row j's lanes, before its output
+// exists) and are flushed to HBM with coalesced 16-byte stores once per
+// chunk.  Two barriers per chunk; none per token.
+//
+// Within a chunk the row update is software-pipelined (pass()): the update
+// and output of token t share one sweep over the registers with the decay and
+// key dot product of token t+1, so only the key reduction sits on the
+// critical path between tokens.
+#ifndef GDN_SEQ_CHUNK
+#define GDN_SEQ_CHUNK 16
+#endif
+#ifndef GDN_SEQ_TILES_PER_WAVE
+#define GDN_SEQ_TILES_PER_WAVE 2
+#endif
+constexpr int kChunk = GDN_SEQ_CHUNK;
+constexpr int kSeqTilesPerWave = GDN_SEQ_TILES_PER_WAVE;
+constexpr int kSeqWaves = kTilesPerHead / kSeqTilesPerWave;   // 8
+constexpr int kSeqThreads = kSeqWaves * 64;                   // 512
 
 struct alignas(16) TokenLds {
     float k[D];
     float q[D];
-    float v[D];
-    float gate;
+    float v[D];       // v on entry; the token's output once computed
+    float e;          // exp(gate)
     float beta;
     float pad[2];
 };
 static_assert(sizeof(TokenLds) % 16 == 0, "float4 aligned token slots");
 
-// float4 loads needed per token: k (32) + q (32) + v (32)
+// float4 loads per token: k (32) + q (32) + v (32)
 constexpr int kTokF4 = 3 * D / 4;
-constexpr int kChunkF4 = kChunk * kTokF4;                    // 1536
+constexpr int kChunkF4 = kChunk * kTokF4;                     // 1536
+constexpr int kFetchPer = (kChunkF4 + kSeqThreads - 1) / kSeqThreads;   // 3
+constexpr int kFlushPer = (kChunk * D / 4 + kSeqThreads - 1) / kSeqThreads; // 1
+static_assert(2 * kChunk <= kSeqThreads, "one thread per gate and per beta");
 
-template <int THREADS>
 struct ChunkRegs {
-    static constexpr int kPer = (kChunkF4 + THREADS - 1) / THREADS;
-    f4 f[kPer];
+    f4 f[kFetchPer];
     float s;   // gate or beta of one token (threads 0 .. 2*kChunk-1)
 };
 
-template <int THREADS>
-__device__ __forceinline__ void seq_fetch(ChunkRegs<THREADS> &cr, const SeqArgs &a, int64_t b,
-                                          int h, int kh, int t0, int tid) {
+__device__ __forceinline__ void seq_fetch(ChunkRegs &cr, const SeqArgs &a, int64_t b, int h,
+                                          int kh, int t0, int tid) {
 #pragma unroll
-    for (int j = 0; j < ChunkRegs<THREADS>::kPer; ++j) {
-        const int e = tid + j * THREADS;
+    for (int j = 0; j < kFetchPer; ++j) {
+        const int e = tid + j * kSeqThreads;
         const int tt = e / kTokF4;
         const int w = e - tt * kTokF4;
         const int t = t0 + tt;
@@ -289,30 +367,26 @@ __device__ __forceinline__ void seq_fetch(ChunkRegs<THREADS> &cr, const SeqArgs 
     }
 }
 
-template <int THREADS>
-__device__ __forceinline__ void seq_stage(TokenLds *buf, const ChunkRegs<THREADS> &cr, int tid) {
+__device__ __forceinline__ void seq_stage(TokenLds *buf, const ChunkRegs &cr, int tid) {
 #pragma unroll
-    for (int j = 0; j < ChunkRegs<THREADS>::kPer; ++j) {
-        const int e = tid + j * THREADS;
-        if (e < kChunkF4) {
-            const int tt = e / kTokF4;
-            const int w = e - tt * kTokF4;
-            float *dst = w < 32 ? buf[tt].k + 4 * w
-                       : w < 64 ? buf[tt].q + 4 * (w - 32)
-                                : buf[tt].v + 4 * (w - 64);
-            *reinterpret_cast<f4 *>(dst) = cr.f[j];
-        }
+    for (int j = 0; j < kFetchPer; ++j) {
+        const int e = tid + j * kSeqThreads;
+        if (e >= kChunkF4) break;
+        const int tt = e / kTokF4;
+        const int w = e - tt * kTokF4;
+        float *dst = w < 32 ? buf[tt].k + 4 * w
+                   : w < 64 ? buf[tt].q + 4 * (w - 32)
+                            : buf[tt].v + 4 * (w - 64);
+        *reinterpret_cast<f4 *>(dst) = cr.f[j];
     }
     if (tid < kChunk)
-        buf[tid].gate = cr.s;
+        buf[tid].e = expf(cr.s);          // the token's decay factor, computed once
     else if (tid < 2 * kChunk)
         buf[tid - kChunk].beta = cr.s;
 }
 
-template <int TPW>   // tiles (8 rows each) per wave
-__global__ __launch_bounds__((kTilesPerHead / TPW) * 64) void k_seq(SeqArgs a) {
-    constexpr int kWaves = kTilesPerHead / TPW;
-    constexpr int kThreads = kWaves * 64;
+__global__ __launch_bounds__(kSeqThreads) void k_seq(SeqArgs a) {
+    constexpr int TPW = kSeqTilesPerWave;
     __shared__ TokenLds lds[2][kChunk];
 
     const int tid = threadIdx.x;
@@ -335,37 +409,68 @@ __global__ __launch_bounds__((kTilesPerHead / TPW) * 64) void k_seq(SeqArgs a) {
         load_row<false>(r[t], M + rows[t] * D, c);
     }
 
-    ChunkRegs<kThreads> cr;
-    seq_fetch<kThreads>(cr, a, b, h, kh, 0, tid);
-    seq_stage<kThreads>(lds[0], cr, tid);
+    ChunkRegs cr;
+    seq_fetch(cr, a, b, h, kh, 0, tid);
+    seq_stage(lds[0], cr, tid);
     __syncthreads();
 
     const int n_chunks = (a.T + kChunk - 1) / kChunk;
     for (int ch = 0; ch < n_chunks; ++ch) {
         const bool more = ch + 1 < n_chunks;
-        if (more) seq_fetch<kThreads>(cr, a, b, h, kh, (ch + 1) * kChunk, tid);
+        if (more) seq_fetch(cr, a, b, h, kh, (ch + 1) * kChunk, tid);
 
-        const TokenLds *buf = lds[ch & 1];
+        TokenLds *buf = lds[ch & 1];
         const int t0 = ch * kChunk;
         const int nt = min(kChunk, a.T - t0);
-        for (int tt = 0; tt < nt; ++tt) {
-            const TokenLds &tok = buf[tt];
-            VecSlice kv, qv;
-            load_vec(kv, tok.k, c);
-            load_vec(qv, tok.q, c);
-            const float e = expf(tok.gate);
-            const int64_t ob = ((static_cast<int64_t>(b) * a.T + t0 + tt) * a.Hv + h) * D;
+
+        // steps 1-2 of the chunk's first token
+        VecSlice kv;
+        load_vec(kv, buf[0].k, c);
+        float p[TPW];
+        {
+            const float e0 = buf[0].e;
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                const float o = row_token(r[t], kv, qv, e, tok.beta, tok.v[rows[t]]);
-                if (c == 0) a.out[ob + rows[t]] = o;
-            }
+            for (int t = 0; t < TPW; ++t) p[t] = head_part(r[t], kv, e0);
         }
 
-        if (more) {
-            seq_stage<kThreads>(lds[(ch + 1) & 1], cr, tid);
-            __syncthreads();
+        for (int tt = 0; tt < nt; ++tt) {
+            TokenLds &tok = buf[tt];
+            float d[TPW];
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)                      // step 3
+                d[t] = (tok.v[rows[t]] - group_sum(p[t])) * tok.beta;
+            VecSlice qv;
+            load_vec(qv, tok.q, c);
+            float o[TPW];
+            if (tt + 1 < nt) {
+                VecSlice kn;
+                load_vec(kn, buf[tt + 1].k, c);
+                const float en = buf[tt + 1].e;
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) pass(r[t], d[t], kv, qv, en, kn, o[t], p[t]);
+                kv = kn;
+            } else {
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) o[t] = body_part(r[t], d[t], kv, qv);
+            }
+            // every lane of the row group holds the same output bits
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) tok.v[rows[t]] = group_sum(o[t]) * kInvSqrtD;
         }
+        __syncthreads();                 // outputs of chunk ch complete in LDS
+
+#pragma unroll
+        for (int j = 0; j < kFlushPer; ++j) {   // flush: float4s of the outputs
+            const int e = tid + j * kSeqThreads;
+            const int tt = e / (D / 4);
+            const int col = (e % (D / 4)) * 4;
+            if (tt < nt) {
+                const int64_t o = ((static_cast<int64_t>(b) * a.T + t0 + tt) * a.Hv + h) * D + col;
+                *reinterpret_cast<f4 *>(a.out + o) = *reinterpret_cast<const f4 *>(buf[tt].v + col);
+            }
+        }
+        if (more) seq_stage(lds[(ch + 1) & 1], cr, tid);
+        __syncthreads();                 // chunk ch+1 staged; chunk ch flushed
     }
 #pragma unroll
     for (int t = 0; t < TPW; ++t) store_row<false>(M + rows[t] * D, r[t], c);
@@ -570,9 +675,6 @@ __global__ __launch_bounds__(kTailThreads) void k_tail_fused(TailFusedArgs a) {
 #ifndef GDN_STEP_WGS_PER_CU
 #define GDN_STEP_WGS_PER_CU 2
 #endif
-#ifndef GDN_SEQ_TILES_PER_WAVE
-#define GDN_SEQ_TILES_PER_WAVE 2
-#endif
 
 // Compute units of the current device (read once per device; a value that
 // never changes, so concurrent first calls race harmlessly).
@@ -609,9 +711,8 @@ hipError_t launch_pair(const PairArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
-    constexpr int tpw = GDN_SEQ_TILES_PER_WAVE;
     const int64_t heads = static_cast<int64_t>(a.B) * a.Hv;
-    k_seq<tpw><<<dim3(static_cast<unsigned>(heads)), dim3((kTilesPerHead / tpw) * 64), 0, s>>>(a);
+    k_seq<<<dim3(static_cast<unsigned>(heads)), dim3(kSeqThreads), 0, s>>>(a);
     return hipGetLastError();
 }
 
