@@ -126,6 +126,49 @@ def run_step36(g, w, stream, evs=None):
             evs[l][1].record(stream)
 
 
+def config2_variants(torch, g, w, stream, steps):
+    """The same 36-layer step (a) captured once as a HIP graph and replayed,
+    and (b) as one gdn_step launch over all layers: the [36][256] layer and
+    sequence axes of the contiguous buffers flattened into B = 9216."""
+    L, B = w["L"], w["B"]
+    res = {}
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=side):
+        run_step36(g, w, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    gr.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(steps):
+        gr.replay()
+    e.record(stream)
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    res["graph_replay"] = {"ms_per_step": ms, "state_updates_per_s": L * B * HV / (ms / 1e3)}
+
+    cat = {n: torch.cat([w["ins"][l][n] for l in range(L)]) for n in w["ins"][0]}
+    flat = w["states"].view(L * B, HV, D, D)
+    out = w["outs"].view(L * B, HV, D)
+
+    def one():
+        g.step(cat["q"], cat["k"], cat["v"], cat["beta"], cat["gate"], flat, out, stream=stream)
+    one()
+    torch.cuda.synchronize()
+    s.record(stream)
+    for _ in range(steps):
+        one()
+    e.record(stream)
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    res["flattened_b9216_one_launch"] = {
+        "ms_per_step": ms, "state_updates_per_s": L * B * HV / (ms / 1e3),
+        "GBps": L * B * HV * STATE_UPDATE_BYTES / (ms / 1e3) / 1e9}
+    return res
+
+
 def cpu_baseline(seconds):
     """The oracle as it is, on the host cores, over config-2 layers (B=256)
     stepped round-robin until `seconds` have passed."""
@@ -269,8 +312,12 @@ def main():
     torch.cuda.synchronize()
 
     log(f"[bench] timing {args.steps} steps x {L} gdn_step launches")
+    # Every launch of every 5th timed step is bracketed by HIP events on the
+    # launch stream (event records between kernels cost a few us each, so the
+    # other steps run bare).
+    timed = [s for s in range(args.steps) if s % 5 == 0]
     evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-            for _ in range(L)] for _ in range(args.steps)]
+            for _ in range(L)] if s in timed else None for s in range(args.steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -281,7 +328,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_end)
-    launch_ms = [evs[s][l][0].elapsed_time(evs[s][l][1]) for s in range(args.steps) for l in range(L)]
+    launch_ms = [evs[s][l][0].elapsed_time(evs[s][l][1]) for s in timed for l in range(L)]
     avg_launch_ms = float(np.mean(launch_ms))
 
     updates_per_step = L * B * HV
@@ -317,9 +364,12 @@ def main():
                      "traffic": measured_traffic(),
                      "bytes_per_launch": bytes_per_launch,
                      "copy_probe_GBps": copy_gbps,
-                     "avg_launch_us": avg_launch_ms * 1e3},
+                     "avg_launch_us": avg_launch_ms * 1e3,
+                     "launches_timed": len(launch_ms)},
     }
     if not args.no_extra:
+        log("[bench] graph replay and flattened single launch of the 36 layers")
+        line["extra_config2"] = config2_variants(torch, g, w, stream, args.steps)
         log("[bench] secondary entry points")
         del w
         torch.cuda.empty_cache()

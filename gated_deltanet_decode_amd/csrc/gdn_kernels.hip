@@ -198,15 +198,15 @@ __device__ __forceinline__ void pass(RowSlice &r, float d, const VecSlice &k, co
 
 // ------------------------------------------------------------- gdn_step
 // HBM-bound: the state is streamed once in and once out.  A persistent grid
-// of kStepWaves-wave workgroups walks the tiles (8 rows = 4 KiB each) of all
+// of one 8-wave workgroup per CU walks the tiles (8 rows = 4 KiB each) of all
 // heads in a grid-stride loop, one tile per wave per iteration, so the
-// addresses in flight at any moment form one contiguous window of a few MiB
-// that advances through the state (this keeps DRAM pages open; measured on
-// MI355X it beats one workgroup per head and deeper per-wave queues).
-// Workgroup g runs on XCD g % 8; the tile order is remapped so that the 16
-// tiles of a head go to workgroups of one XCD and its k and q are fetched
-// into one L2 only.
-constexpr int kStepWaves = 4;
+// addresses in flight at any moment form one contiguous window of ~8 MiB
+// that advances through the state.  Measured on MI355X this beats one
+// workgroup per head, more or fewer waves per CU, deeper per-wave queues and
+// prefetching the next tile.  Workgroup g runs on XCD g % 8; the tile order
+// is remapped so that the 16 tiles of a head go to workgroups of one XCD and
+// its k and q are fetched into one L2 only.
+constexpr int kStepWaves = 8;
 constexpr int kXcds = 8;
 
 __global__ __launch_bounds__(kStepWaves * 64) void k_step(StepArgs a, int n_tiles) {
@@ -673,7 +673,7 @@ __global__ __launch_bounds__(kTailThreads) void k_tail_fused(TailFusedArgs a) {
 
 // ---------------------------------------------------------------- launch
 #ifndef GDN_STEP_WGS_PER_CU
-#define GDN_STEP_WGS_PER_CU 2
+#define GDN_STEP_WGS_PER_CU 1
 #endif
 
 // Compute units of the current device (read once per device; a value that
