@@ -231,6 +231,17 @@ def extra_measurements(torch, g, stream):
     ms = timeit(lambda: g.step(si["q"], si["k"], si["v"], si["beta"], si["gate"], M, o,
                                stream=stream), 1000)
     res["config0_step_b1"] = {"us_per_call": ms * 1e3, "state_updates_per_s": 32 / (ms / 1e3)}
+    # the same call replayed from a captured graph of 100 calls (no host
+    # launch path in the loop: device-side time per call)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=side):
+        for _ in range(100):
+            g.step(si["q"], si["k"], si["v"], si["beta"], si["gate"], M, o)
+    torch.cuda.synchronize()
+    ms = timeit(gr.replay, 10) / 100
+    res["config0_step_b1"]["graph_us_per_call"] = ms * 1e3
 
     # config 1: B=64 decode, 100 calls with fresh inputs
     c1 = gi.CONFIGS[1]

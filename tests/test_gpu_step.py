@@ -139,3 +139,29 @@ def test_rejected_call_leaves_buffers_untouched(g):
     torch.cuda.synchronize()
     assert rc == -3 and "q" in g.last_error()
     assert np.array_equal(Md.cpu().numpy(), M) and bool((out == 7.0).all())
+
+
+def test_unaligned_to_cache_lines(g, orc):
+    """Buffers that are 16-byte aligned but not 128-byte aligned (views at a
+    16-byte offset into larger allocations) give the same results."""
+    import torch
+    print("\n  gdn_step at 16-byte offsets", flush=True)
+    B = 3
+    si = gi.step_inputs(2500, 0, B)
+    M = gi.state(2500, 0, B)
+    want_M = M.copy()
+    want = ref.step_mt(orc, si, want_M)
+
+    def shifted(a):
+        buf = torch.zeros(a.size + 4, dtype=torch.float32, device="cuda")
+        view = buf[4:].view(a.shape)
+        view.copy_(torch.from_numpy(np.ascontiguousarray(a)))
+        return view
+    t = {n: shifted(x) for n, x in si.items()}
+    Md = shifted(M)
+    out = torch.zeros(B * 32 * 128 + 4, device="cuda")[4:].view(B, 32, 128)
+    assert Md.data_ptr() % 128 == 16
+    g.step(t["q"], t["k"], t["v"], t["beta"], t["gate"], Md, out)
+    torch.cuda.synchronize()
+    ref.assert_close("state", Md.cpu().numpy(), want_M, STATE_TOL)
+    ref.assert_close("out", out.cpu().numpy(), want, OUT_TOL)
