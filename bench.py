@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the secondary entry points")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--config", type=int, default=2, choices=[0, 1, 2, 3, 4],
+                   help="2 (default): the headline run; others: only that configuration's "
+                        "secondary measurement (for profiling)")
     return p.parse_args()
 
 
@@ -169,6 +172,24 @@ def config2_variants(torch, g, w, stream, steps):
     return res
 
 
+def host_info():
+    info = {"nproc": os.cpu_count()}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal"):
+                    info["mem_GiB"] = round(int(line.split()[1]) / 2**20, 1)
+                    break
+    except OSError:
+        pass
+    return info
+
+
 def cpu_baseline(seconds):
     """The oracle as it is, on the host cores, over config-2 layers (B=256)
     stepped round-robin until `seconds` have passed."""
@@ -201,16 +222,32 @@ def cpu_baseline(seconds):
         if el >= seconds or done >= 4000:
             break
     updates = done * B * HV
+
+    # one host thread, a smaller slice (32 sequences of layer 0), ~3 s
+    si = {n: np.ascontiguousarray(x[:32]) for n, x in ins[0].items()}
+    M = np.ascontiguousarray(states[0][:32])
+    done1 = 0
+    t1 = time.perf_counter()
+    while time.perf_counter() - t1 < max(1.0, seconds / 4):
+        o.step_M(si["q"], si["k"], si["v"], si["beta"], si["gate"], M)
+        done1 += 1
+    el1 = time.perf_counter() - t1
     return {"value": updates / el, "unit": "state-updates/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} layer-steps of configuration 2 (B=256, 32 heads; layers 0-"
                       f"{n_layers - 1} stepped round-robin), oracle_gdn_step_M split over "
                       f"{threads} host threads by sequence, {el:.1f} s",
-            "GBps": updates * STATE_UPDATE_BYTES / el / 1e9}
+            "GBps": updates * STATE_UPDATE_BYTES / el / 1e9,
+            "single_thread_value": done1 * 32 * HV / el1,
+            "single_thread_sample": f"{done1} steps of 32 sequences x 32 heads, one thread, "
+                                    f"{el1:.1f} s",
+            "host": host_info()}
 
 
-def extra_measurements(torch, g, stream):
-    """Secondary entry points, timed with events on the launch stream."""
+def extra_measurements(torch, g, stream, only=None):
+    """Secondary entry points, timed with events on the launch stream
+    (`only`: run just that configuration)."""
     res = {}
+    want = lambda c: only is None or only == c
 
     def timeit(fn, reps):
         for _ in range(2):
@@ -225,78 +262,89 @@ def extra_measurements(torch, g, stream):
         return s.elapsed_time(e) / reps
 
     # config 0: B=1 single step (latency-bound)
-    si = {n: torch.from_numpy(x).cuda() for n, x in gi.step_inputs(1000, 0, 1).items()}
-    M = torch.from_numpy(gi.state(1000, 0, 1)).cuda()
-    o = torch.empty((1, HV, D), device="cuda")
-    ms = timeit(lambda: g.step(si["q"], si["k"], si["v"], si["beta"], si["gate"], M, o,
-                               stream=stream), 1000)
-    res["config0_step_b1"] = {"us_per_call": ms * 1e3, "state_updates_per_s": 32 / (ms / 1e3)}
-    # the same call replayed from a captured graph of 100 calls (no host
-    # launch path in the loop: device-side time per call)
-    side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    gr = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gr, stream=side):
-        for _ in range(100):
-            g.step(si["q"], si["k"], si["v"], si["beta"], si["gate"], M, o)
-    torch.cuda.synchronize()
-    ms = timeit(gr.replay, 10) / 100
-    res["config0_step_b1"]["graph_us_per_call"] = ms * 1e3
+    if want(0):
+        si = {n: torch.from_numpy(x).cuda() for n, x in gi.step_inputs(1000, 0, 1).items()}
+        M = torch.from_numpy(gi.state(1000, 0, 1)).cuda()
+        o = torch.empty((1, HV, D), device="cuda")
+        ms = timeit(lambda: g.step(si["q"], si["k"], si["v"], si["beta"], si["gate"], M, o,
+                                   stream=stream), 1000)
+        res["config0_step_b1"] = {"us_per_call": ms * 1e3, "state_updates_per_s": 32 / (ms / 1e3)}
+        # the same call replayed from a captured graph of 100 calls (no host
+        # launch path in the loop: device-side time per call)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=side):
+            for _ in range(100):
+                g.step(si["q"], si["k"], si["v"], si["beta"], si["gate"], M, o)
+        torch.cuda.synchronize()
+        ms = timeit(gr.replay, 10) / 100
+        res["config0_step_b1"]["graph_us_per_call"] = ms * 1e3
 
     # config 1: B=64 decode, 100 calls with fresh inputs
-    c1 = gi.CONFIGS[1]
-    M = torch.from_numpy(gi.state(c1["seed"], 0, 64)).cuda()
-    ins = [{n: torch.from_numpy(x).cuda() for n, x in gi.step_inputs(c1["seed"], i, 64).items()}
-           for i in range(100)]
-    o = torch.empty((64, HV, D), device="cuda")
+    if want(1):
+        c1 = gi.CONFIGS[1]
+        M = torch.from_numpy(gi.state(c1["seed"], 0, 64)).cuda()
+        ins = [{n: torch.from_numpy(x).cuda() for n, x in gi.step_inputs(c1["seed"], i, 64).items()}
+               for i in range(100)]
+        o = torch.empty((64, HV, D), device="cuda")
 
-    def c1run():
-        for t in ins:
-            g.step(t["q"], t["k"], t["v"], t["beta"], t["gate"], M, o, stream=stream)
-    ms = timeit(c1run, 3)
-    upd = 100 * 64 * HV
-    res["config1_step_b64_x100"] = {"ms": ms, "state_updates_per_s": upd / (ms / 1e3),
-                                    "GBps": upd * STATE_UPDATE_BYTES / (ms / 1e3) / 1e9,
-                                    "note": "128 MiB state fits the 256 MB Infinity Cache"}
+        def c1run():
+            for t in ins:
+                g.step(t["q"], t["k"], t["v"], t["beta"], t["gate"], M, o, stream=stream)
+        ms = timeit(c1run, 3)
+        upd = 100 * 64 * HV
+        res["config1_step_b64_x100"] = {"ms": ms, "state_updates_per_s": upd / (ms / 1e3),
+                                        "GBps": upd * STATE_UPDATE_BYTES / (ms / 1e3) / 1e9,
+                                        "note": "128 MiB state fits the 256 MB Infinity Cache"}
 
     # gdn_pair: B=256, one layer, two positions (state read once, written twice)
-    c2 = gi.CONFIGS[2]
-    si = {n: torch.from_numpy(x).cuda() for n, x in gi.step_inputs(c2["seed"], 0, 256, T=2).items()}
-    M = torch.from_numpy(gi.state(c2["seed"], 0, 256)).cuda()
-    Mn = torch.empty_like(M)
-    o = torch.empty((256, 2, HV, D), device="cuda")
-    ms = timeit(lambda: g.pair(si["q"], si["k"], si["v"], si["beta"], si["gate"], M, Mn, o,
-                               stream=stream), 10)
-    pair_bytes = 256 * HV * (3 * D * D * 4 + 2 * (STATE_UPDATE_BYTES - 2 * D * D * 4))
-    res["pair_b256"] = {"us_per_call": ms * 1e3, "state_updates_per_s": 2 * 256 * HV / (ms / 1e3),
-                        "GBps": pair_bytes / (ms / 1e3) / 1e9,
-                        "bytes_per_call": pair_bytes}
-    del M, Mn
+    if only is None:
+        c2 = gi.CONFIGS[2]
+        si = {n: torch.from_numpy(x).cuda() for n, x in gi.step_inputs(c2["seed"], 0, 256, T=2).items()}
+        M = torch.from_numpy(gi.state(c2["seed"], 0, 256)).cuda()
+        Mn = torch.empty_like(M)
+        o = torch.empty((256, 2, HV, D), device="cuda")
+        ms = timeit(lambda: g.pair(si["q"], si["k"], si["v"], si["beta"], si["gate"], M, Mn, o,
+                                   stream=stream), 10)
+        pair_bytes = 256 * HV * (3 * D * D * 4 + 2 * (STATE_UPDATE_BYTES - 2 * D * D * 4))
+        res["pair_b256"] = {"us_per_call": ms * 1e3, "state_updates_per_s": 2 * 256 * HV / (ms / 1e3),
+                            "GBps": pair_bytes / (ms / 1e3) / 1e9,
+                            "bytes_per_call": pair_bytes}
+        del M, Mn
 
     # config 3: gdn_seq B=8 x T=4096 from a zero state
-    c3 = gi.CONFIGS[3]
-    si = {n: torch.from_numpy(x).cuda() for n, x in gi.step_inputs(c3["seed"], 0, 8, T=4096).items()}
-    M = torch.zeros((8, HV, D, D), device="cuda")
-    o = torch.empty((8, 4096, HV, D), device="cuda")
-    ms = timeit(lambda: g.seq(si["q"], si["k"], si["v"], si["beta"], si["gate"], M, o,
-                              stream=stream), 5)
-    upd = 8 * 4096 * HV
-    flops = upd * D * D * 7  # decay mul + 3 FMA per element
-    res["config3_seq_b8_t4096"] = {"ms": ms, "state_updates_per_s": upd / (ms / 1e3),
-                                   "TFLOPs": flops / (ms / 1e3) / 1e12,
-                                   "frac_fp32_vector_nonpacked_78.6": flops / (ms / 1e3) / 78.6e12}
+    if want(3):
+        c3 = gi.CONFIGS[3]
+        si = {n: torch.from_numpy(x).cuda() for n, x in gi.step_inputs(c3["seed"], 0, 8, T=4096).items()}
+        M = torch.zeros((8, HV, D, D), device="cuda")
+        o = torch.empty((8, 4096, HV, D), device="cuda")
+        ms = timeit(lambda: g.seq(si["q"], si["k"], si["v"], si["beta"], si["gate"], M, o,
+                                  stream=stream), 5)
+        upd = 8 * 4096 * HV
+        flops = upd * D * D * 7  # decay mul + 3 FMA per element
+        res["config3_seq_b8_t4096"] = {"ms": ms, "state_updates_per_s": upd / (ms / 1e3),
+                                       "TFLOPs": flops / (ms / 1e3) / 1e12,
+                                       "frac_fp32_vector_nonpacked_78.6": flops / (ms / 1e3) / 78.6e12,
+                                       "frac_fp32_vector_157.3": flops / (ms / 1e3) / 157.3e12}
 
     # config 4: layer tail B=32
-    c4 = gi.CONFIGS[4]
-    ti = {n: torch.from_numpy(x).cuda() for n, x in gi.tail_inputs(c4["seed"], 32).items()}
-    M = torch.from_numpy(gi.state(c4["seed"], 0, 32)).cuda()
-    y = torch.empty((32, HV * D), device="cuda")
-    ws = torch.empty(g.layer_tail_workspace_bytes(32), dtype=torch.uint8, device="cuda")
-    ms = timeit(lambda: g.layer_tail(ti["x"], ti["conv_w"], ti["conv_state"], ti["beta"],
-                                     ti["gate"], M, ti["z"], ti["norm_w"], y, workspace=ws,
-                                     stream=stream), 200)
-    res["config4_layer_tail_b32"] = {"us_per_call": ms * 1e3,
-                                     "state_updates_per_s": 32 * HV / (ms / 1e3)}
+    if want(4):
+        c4 = gi.CONFIGS[4]
+        ti = {n: torch.from_numpy(x).cuda() for n, x in gi.tail_inputs(c4["seed"], 32).items()}
+        M = torch.from_numpy(gi.state(c4["seed"], 0, 32)).cuda()
+        y = torch.empty((32, HV * D), device="cuda")
+        ws = torch.empty(g.layer_tail_workspace_bytes(32), dtype=torch.uint8, device="cuda")
+        ms = timeit(lambda: g.layer_tail(ti["x"], ti["conv_w"], ti["conv_state"], ti["beta"],
+                                         ti["gate"], M, ti["z"], ti["norm_w"], y, workspace=ws,
+                                         stream=stream), 200)
+        res["config4_layer_tail_b32"] = {"us_per_call": ms * 1e3,
+                                         "state_updates_per_s": 32 * HV / (ms / 1e3)}
+        three = g.TailParams(4, 128, 1e-6, 1)
+        ms = timeit(lambda: g.layer_tail(ti["x"], ti["conv_w"], ti["conv_state"], ti["beta"],
+                                         ti["gate"], M, ti["z"], ti["norm_w"], y, workspace=ws,
+                                         params=three, stream=stream), 200)
+        res["config4_layer_tail_b32"]["three_launch_us_per_call"] = ms * 1e3
     return res
 
 
@@ -313,6 +361,10 @@ def main():
         sys.exit(1)
 
     stream = torch.cuda.current_stream()
+    if args.config != 2:
+        res = extra_measurements(torch, g, stream, only=args.config)
+        print(json.dumps({"config": args.config, "extra": res}), flush=True)
+        return
     copy_gbps = copy_probe(torch, stream)
     log(f"[bench] copy probe: {copy_gbps:.0f} GB/s")
     w = setup_config2(torch, g)
@@ -375,6 +427,7 @@ def main():
                      "traffic": measured_traffic(),
                      "bytes_per_launch": bytes_per_launch,
                      "copy_probe_GBps": copy_gbps,
+                     "frac_of_copy_probe": achieved / copy_gbps,
                      "avg_launch_us": avg_launch_ms * 1e3,
                      "launches_timed": len(launch_ms)},
     }

@@ -165,3 +165,19 @@ def test_unaligned_to_cache_lines(g, orc):
     torch.cuda.synchronize()
     ref.assert_close("state", Md.cpu().numpy(), want_M, STATE_TOL)
     ref.assert_close("out", out.cpu().numpy(), want, OUT_TOL)
+
+
+def test_nan_stays_in_its_row(g):
+    """A NaN in one v entry (sequence 1, head 5, row 7) reaches exactly that
+    state row and that output; every other row, head and sequence is
+    bitwise what it is without the NaN (rows never exchange data)."""
+    print("\n  gdn_step NaN isolation", flush=True)
+    si = gi.step_inputs(2600, 0, 3)
+    M = gi.state(2600, 0, 3)
+    clean_M, clean_o = run_step(g, si, M)
+    si["v"][1, 5, 7] = np.nan
+    Mg, og = run_step(g, si, M)
+    assert np.all(np.isnan(Mg[1, 5, 7])) and np.isnan(og[1, 5, 7])
+    mask = np.ones(Mg.shape[:3], bool)
+    mask[1, 5, 7] = False
+    assert np.array_equal(Mg[mask], clean_M[mask]) and np.array_equal(og[mask], clean_o[mask])
