@@ -39,7 +39,8 @@ HBM_PEAK_GBPS = 8000.0
 # WRITE_SIZE, calibrated against a copy of known size); only reported while
 # the kernel source is the one the counters were taken on.
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "k_step_b256_traffic.json")
-KERNEL_SOURCE = os.path.join(HERE, "gated_deltanet_decode_amd", "csrc", "gdn_kernels.hip")
+KERNEL_SOURCES = [os.path.join(HERE, "gated_deltanet_decode_amd", "csrc", f)
+                  for f in ("gdn_device.hpp", "gdn_step.hip")]
 METRIC = "GDN state-updates/s (seq·head·token) and achieved HBM GB/s, B=256 decode"
 
 
@@ -84,8 +85,11 @@ def measured_traffic():
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-        with open(KERNEL_SOURCE, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        h = hashlib.sha256()
+        for path in KERNEL_SOURCES:
+            with open(path, "rb") as f:
+                h.update(f.read())
+        sha = h.hexdigest()
     except (OSError, ValueError):
         return None
     if t.get("kernel_source_sha256") != sha:

@@ -8,7 +8,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBRARY = os.path.join(CSRC, "libgdn.so")
-SOURCES = [os.path.join(CSRC, "gdn_api.cpp"), os.path.join(CSRC, "gdn_kernels.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in
+           ("gdn_api.cpp", "gdn_step.hip", "gdn_seq.hip", "gdn_tail.hip")]
 # Measurement aid (a copy kernel of known size), built as its own library.
 PROBE_LIBRARY = os.path.join(CSRC, "libgdn_probe.so")
 PROBE_SOURCES = [os.path.join(CSRC, "hbm_probe.hip")]

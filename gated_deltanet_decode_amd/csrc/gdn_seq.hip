@@ -1,0 +1,224 @@
+// gdn_seq.hip - gdn_seq: the multi-token kernel with the state resident in
+// registers.
+
+#include "gdn_device.hpp"
+
+namespace gdn {
+namespace {
+
+// -------------------------------------------------------------- gdn_seq
+// One workgroup per (sequence, value head): 8 waves x 2 tiles, so the whole
+// 64 KiB head state lives in VGPRs (32 floats per lane) for all T tokens and
+// is read and written once per call.  The per-token inputs (k, q, v,
+// exp(gate), beta: 1.5 KiB per token) are staged through LDS in chunks of
+// kChunk = 32 tokens, double-buffered (97 KiB of LDS; gfx950 allows 160 KiB
+// per workgroup): the global loads of chunk c+1 are issued before chunk c is
+// computed and written to LDS after it, so their latency hides behind 32
+// tokens of arithmetic.  Outputs overwrite the consumed v entries in LDS
+// (row j's v is read only by row j's lanes, before its output exists) and are
+// flushed to HBM with coalesced 16-byte stores once per chunk.  Two barriers
+// per chunk; none per token.
+//
+// Within a chunk the row update is software-pipelined (pass()): the update
+// and output of token t share one sweep over the registers with the decay and
+// key dot product of token t+1, so only the key reduction sits on the
+// critical path between tokens.  Full chunks are unrolled, so every LDS
+// address is an immediate offset and no loop bookkeeping runs per token.
+// The kernel is VALU-issue bound (measured: VALU busy ~97 %), so every
+// instruction per token counts.
+#ifndef GDN_SEQ_CHUNK
+#define GDN_SEQ_CHUNK 32
+#endif
+#ifndef GDN_SEQ_TILES_PER_WAVE
+#define GDN_SEQ_TILES_PER_WAVE 2
+#endif
+constexpr int kChunk = GDN_SEQ_CHUNK;
+constexpr int kSeqTilesPerWave = GDN_SEQ_TILES_PER_WAVE;
+constexpr int kSeqWaves = kTilesPerHead / kSeqTilesPerWave;   // 8
+constexpr int kSeqThreads = kSeqWaves * 64;                   // 512
+
+struct alignas(16) TokenLds {
+    float k[D];
+    float q[D];
+    float v[D];       // v on entry; the token's output once computed
+    float e;          // exp(gate)
+    float beta;
+    float pad[2];
+};
+static_assert(sizeof(TokenLds) % 16 == 0, "float4 aligned token slots");
+
+// float4 loads per token: k (32) + q (32) + v (32)
+constexpr int kTokF4 = 3 * D / 4;
+constexpr int kChunkF4 = kChunk * kTokF4;                     // 3072
+constexpr int kFetchPer = (kChunkF4 + kSeqThreads - 1) / kSeqThreads;   // 6
+constexpr int kFlushPer = (kChunk * D / 4 + kSeqThreads - 1) / kSeqThreads; // 2
+static_assert(2 * kChunk <= kSeqThreads, "one thread per gate and per beta");
+
+struct ChunkRegs {
+    f4 f[kFetchPer];
+    float s;   // gate or beta of one token (threads 0 .. 2*kChunk-1)
+};
+
+__device__ __forceinline__ void seq_fetch(ChunkRegs &cr, const SeqArgs &a, int64_t b, int h,
+                                          int kh, int t0, int tid) {
+#pragma unroll
+    for (int j = 0; j < kFetchPer; ++j) {
+        const int e = tid + j * kSeqThreads;
+        const int tt = e / kTokF4;
+        const int w = e - tt * kTokF4;
+        const int t = t0 + tt;
+        f4 val = {0.f, 0.f, 0.f, 0.f};
+        if (e < kChunkF4 && t < a.T) {
+            const int64_t bt = b * a.T + t;
+            const float *src;
+            if (w < 32)
+                src = a.k + (bt * a.Hk + kh) * D + 4 * w;
+            else if (w < 64)
+                src = a.q + (bt * a.Hk + kh) * D + 4 * (w - 32);
+            else
+                src = a.v + (bt * a.Hv + h) * D + 4 * (w - 64);
+            val = *reinterpret_cast<const f4 *>(src);
+        }
+        cr.f[j] = val;
+    }
+    cr.s = 0.0f;
+    if (tid < 2 * kChunk) {
+        const int tt = tid < kChunk ? tid : tid - kChunk;
+        const int t = t0 + tt;
+        if (t < a.T) {
+            const int64_t idx = (b * a.T + t) * a.Hv + h;
+            cr.s = tid < kChunk ? a.gate[idx] : a.beta[idx];
+        }
+    }
+}
+
+__device__ __forceinline__ void seq_stage(TokenLds *buf, const ChunkRegs &cr, int tid) {
+#pragma unroll
+    for (int j = 0; j < kFetchPer; ++j) {
+        const int e = tid + j * kSeqThreads;
+        if (e >= kChunkF4) break;
+        const int tt = e / kTokF4;
+        const int w = e - tt * kTokF4;
+        float *dst = w < 32 ? buf[tt].k + 4 * w
+                   : w < 64 ? buf[tt].q + 4 * (w - 32)
+                            : buf[tt].v + 4 * (w - 64);
+        *reinterpret_cast<f4 *>(dst) = cr.f[j];
+    }
+    if (tid < kChunk)
+        buf[tid].e = expf(cr.s);          // the token's decay factor, computed once
+    else if (tid < 2 * kChunk)
+        buf[tid - kChunk].beta = cr.s;
+}
+
+// Token tt of a chunk: steps 3-5 of tt and, when `next`, steps 1-2 of tt+1
+// (kv holds k of token tt on entry and of tt+1 on exit; p the key partials).
+template <int TPW>
+__device__ __forceinline__ void seq_token(TokenLds *buf, int tt, bool next, const int (&rows)[TPW],
+                                          RowSlice (&r)[TPW], VecSlice &kv, float (&p)[TPW],
+                                          int c) {
+    TokenLds &tok = buf[tt];
+    float d[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)                              // step 3
+        d[t] = (tok.v[rows[t]] - group_sum(p[t])) * tok.beta;
+    VecSlice qv;
+    load_vec(qv, tok.q, c);
+    float o[TPW];
+    if (next) {
+        VecSlice kn;
+        load_vec(kn, buf[tt + 1].k, c);
+        const float en = buf[tt + 1].e;
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) pass(r[t], d[t], kv, qv, en, kn, o[t], p[t]);
+        kv = kn;
+    } else {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) o[t] = body_part(r[t], d[t], kv, qv);
+    }
+    // every lane of the row group holds the same output bits
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) tok.v[rows[t]] = group_sum(o[t]) * kInvSqrtD;
+}
+
+__global__ __launch_bounds__(kSeqThreads) void k_seq(SeqArgs a) {
+    constexpr int TPW = kSeqTilesPerWave;
+    __shared__ TokenLds lds[2][kChunk];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int grp = lane >> 3;
+    const int c = lane & 7;
+
+    const int head = blockIdx.x;                  // b * Hv + h
+    const int b = head / a.Hv;
+    const int h = head - b * a.Hv;
+    const int kh = h % a.Hk;
+
+    float *M = a.state + static_cast<int64_t>(head) * (D * D);
+    int rows[TPW];
+    RowSlice r[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        rows[t] = (wave * TPW + t) * kRowsPerTile + grp;
+        load_row<false>(r[t], M + rows[t] * D, c);
+    }
+
+    ChunkRegs cr;
+    seq_fetch(cr, a, b, h, kh, 0, tid);
+    seq_stage(lds[0], cr, tid);
+    __syncthreads();
+
+    const int n_chunks = (a.T + kChunk - 1) / kChunk;
+    for (int ch = 0; ch < n_chunks; ++ch) {
+        const bool more = ch + 1 < n_chunks;
+        if (more) seq_fetch(cr, a, b, h, kh, (ch + 1) * kChunk, tid);
+
+        TokenLds *buf = lds[ch & 1];
+        const int t0 = ch * kChunk;
+        const int nt = min(kChunk, a.T - t0);
+
+        // steps 1-2 of the chunk's first token
+        VecSlice kv;
+        load_vec(kv, buf[0].k, c);
+        float p[TPW];
+        {
+            const float e0 = buf[0].e;
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) p[t] = head_part(r[t], kv, e0);
+        }
+        if (nt == kChunk) {
+            // full chunk: unrolled, so every LDS address is an immediate offset
+#pragma unroll
+            for (int tt = 0; tt < kChunk; ++tt) seq_token(buf, tt, tt + 1 < kChunk, rows, r, kv, p, c);
+        } else {
+            for (int tt = 0; tt < nt; ++tt) seq_token(buf, tt, tt + 1 < nt, rows, r, kv, p, c);
+        }
+        __syncthreads();                 // outputs of chunk ch complete in LDS
+
+#pragma unroll
+        for (int j = 0; j < kFlushPer; ++j) {   // flush: float4s of the outputs
+            const int e = tid + j * kSeqThreads;
+            const int tt = e / (D / 4);
+            const int col = (e % (D / 4)) * 4;
+            if (tt < nt) {
+                const int64_t o = ((static_cast<int64_t>(b) * a.T + t0 + tt) * a.Hv + h) * D + col;
+                *reinterpret_cast<f4 *>(a.out + o) = *reinterpret_cast<const f4 *>(buf[tt].v + col);
+            }
+        }
+        if (more) seq_stage(lds[(ch + 1) & 1], cr, tid);
+        __syncthreads();                 // chunk ch+1 staged; chunk ch flushed
+    }
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) store_row<false>(M + rows[t] * D, r[t], c);
+}
+
+}  // namespace
+
+hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
+    const int64_t heads = static_cast<int64_t>(a.B) * a.Hv;
+    k_seq<<<dim3(static_cast<unsigned>(heads)), dim3(kSeqThreads), 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,138 @@
+// gdn_step.hip - gdn_step and gdn_pair: the HBM-streaming one- and
+// two-position kernels (persistent tile walk over the state).
+
+#include "gdn_device.hpp"
+
+namespace gdn {
+namespace {
+
+// ------------------------------------------------------------- gdn_step
+// HBM-bound: the state is streamed once in and once out.  A persistent grid
+// of one 8-wave workgroup per CU walks the tiles (8 rows = 4 KiB each) of all
+// heads in a grid-stride loop, one tile per wave per iteration, so the
+// addresses in flight at any moment form one contiguous window of ~8 MiB
+// that advances through the state.  Measured on MI355X this beats one
+// workgroup per head, more or fewer waves per CU, deeper per-wave queues and
+// prefetching the next tile.  Workgroup g runs on XCD g % 8; the tile order
+// is remapped so that the 16 tiles of a head go to workgroups of one XCD and
+// its k and q are fetched into one L2 only.
+constexpr int kStepWaves = 8;
+constexpr int kXcds = 8;
+
+__global__ __launch_bounds__(kStepWaves * 64) void k_step(StepArgs a, int n_tiles) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = lane >> 3;
+    const int c = lane & 7;
+
+    const int G = gridDim.x;
+    const int g = blockIdx.x;
+    const int lg = (G % kXcds == 0) ? (g % kXcds) * (G / kXcds) + g / kXcds : g;
+    const int stride = G * kStepWaves;
+
+    for (int u = lg * kStepWaves + wave; u < n_tiles; u += stride) {
+        const int head = u / kTilesPerHead;                   // b * Hv + h
+        const int row = (u % kTilesPerHead) * kRowsPerTile + grp;
+        const int b = head / a.Hv;
+        const int h = head - b * a.Hv;
+        const int kh = h % a.Hk;                              // key-head broadcast
+
+        float *Mrow = a.state + static_cast<int64_t>(head) * (D * D) + row * D;
+        RowSlice r;
+        load_row<true>(r, Mrow, c);
+        VecSlice kv, qv;
+        load_vec(kv, a.k + b * a.qk_bstride + kh * D, c);
+        load_vec(qv, a.q + b * a.qk_bstride + kh * D, c);
+        const float e = expf(a.gate[head]);
+        const float bt = a.beta[head];
+        const float vj = a.v[b * a.v_bstride + h * D + row];
+
+        const float o = row_token(r, kv, qv, e, bt, vj);
+        store_row<true>(Mrow, r, c);
+        if (c == 0) a.out[static_cast<int64_t>(head) * D + row] = o;
+    }
+}
+
+// ------------------------------------------------------------- gdn_pair
+// Speculative two-position step (docs.rs "Module linear_core", gdn_pair):
+// the same persistent tile walk as k_step; each row is read once, advanced
+// by position 1 and written back to `state` (committed), then advanced by
+// position 2 in registers and written to `state_next` (tentative).  Three
+// state transfers instead of the four of two separate steps.
+__global__ __launch_bounds__(kStepWaves * 64) void k_pair(PairArgs a, int n_tiles) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = lane >> 3;
+    const int c = lane & 7;
+
+    const int G = gridDim.x;
+    const int g = blockIdx.x;
+    const int lg = (G % kXcds == 0) ? (g % kXcds) * (G / kXcds) + g / kXcds : g;
+    const int stride = G * kStepWaves;
+
+    for (int u = lg * kStepWaves + wave; u < n_tiles; u += stride) {
+        const int head = u / kTilesPerHead;
+        const int row = (u % kTilesPerHead) * kRowsPerTile + grp;
+        const int b = head / a.Hv;
+        const int h = head - b * a.Hv;
+        const int kh = h % a.Hk;
+        const int64_t roff = static_cast<int64_t>(head) * (D * D) + row * D;
+
+        RowSlice r;
+        load_row<true>(r, a.state + roff, c);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int64_t bp = static_cast<int64_t>(b) * 2 + p;
+            VecSlice kv, qv;
+            load_vec(kv, a.k + (bp * a.Hk + kh) * D, c);
+            load_vec(qv, a.q + (bp * a.Hk + kh) * D, c);
+            const int64_t hp = bp * a.Hv + h;
+            const float e = expf(a.gate[hp]);
+            const float o = row_token(r, kv, qv, e, a.beta[hp], a.v[hp * D + row]);
+            store_row<true>((p == 0 ? a.state : a.state_next) + roff, r, c);
+            if (c == 0) a.out[hp * D + row] = o;
+        }
+    }
+}
+
+}  // namespace
+
+#ifndef GDN_STEP_WGS_PER_CU
+#define GDN_STEP_WGS_PER_CU 1
+#endif
+
+// Compute units of the current device (read once per device; a value that
+// never changes, so concurrent first calls race harmlessly).
+static int device_cus() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+hipError_t launch_step(const StepArgs &a, hipStream_t s) {
+    const int64_t tiles = static_cast<int64_t>(a.B) * a.Hv * kTilesPerHead;
+    const int64_t full = device_cus() * static_cast<int64_t>(GDN_STEP_WGS_PER_CU);
+    const int64_t need = (tiles + kStepWaves - 1) / kStepWaves;
+    const int grid = static_cast<int>(need < full ? need : full);
+    k_step<<<dim3(grid), dim3(kStepWaves * 64), 0, s>>>(a, static_cast<int>(tiles));
+    return hipGetLastError();
+}
+
+hipError_t launch_pair(const PairArgs &a, hipStream_t s) {
+    const int64_t tiles = static_cast<int64_t>(a.B) * a.Hv * kTilesPerHead;
+    const int64_t full = device_cus() * static_cast<int64_t>(GDN_STEP_WGS_PER_CU);
+    const int64_t need = (tiles + kStepWaves - 1) / kStepWaves;
+    const int grid = static_cast<int>(need < full ? need : full);
+    k_pair<<<dim3(grid), dim3(kStepWaves * 64), 0, s>>>(a, static_cast<int>(tiles));
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,225 @@
+// gdn_tail.hip - gdn_layer_tail: conv1d prestate, gated RMSNorm and the
+// single-launch fused tail.
+
+#include "gdn_device.hpp"
+
+namespace gdn {
+namespace {
+
+// conv-state shift + causal conv1d + SiLU for one 128-channel chunk of one
+// sequence; chunks inside the Q and K parts are also L2-normalised (the head
+// dim is 128, so a chunk is exactly one head).
+template <int K>
+__global__ __launch_bounds__(D) void k_prestate(PrestateArgs a) {
+    __shared__ float scratch[D / 64];
+    const int n_chunks = a.C / D;
+    const int64_t b = blockIdx.x / n_chunks;
+    const int chunk = static_cast<int>(blockIdx.x - b * n_chunks);
+    const int c = chunk * D + threadIdx.x;
+    float *cs = a.conv_state + b * (K - 1) * static_cast<int64_t>(a.C);
+
+    float win[K];
+#pragma unroll
+    for (int t = 0; t < K - 1; ++t) win[t] = cs[static_cast<int64_t>(t) * a.C + c];
+    win[K - 1] = a.x[b * a.C + c];
+
+    const float *w = a.conv_w + static_cast<int64_t>(c) * K;
+    float acc = 0.0f;
+#pragma unroll
+    for (int t = 0; t < K; ++t) acc = fmaf(w[t], win[t], acc);
+#pragma unroll
+    for (int t = 0; t < K - 1; ++t) cs[static_cast<int64_t>(t) * a.C + c] = win[t + 1];
+
+    float s = silu(acc);
+    if (chunk * D < a.n_qk) {        // block-uniform: a Q or K head
+        const float ss = block_sum<D / 64>(s * s, scratch);
+        const float nrm = fmaxf(sqrtf(ss), 1e-6f);
+        s = s / nrm;
+    }
+    a.qkv[b * a.C + c] = s;
+}
+
+// Gated RMSNorm x SiLU(z) over one group of one row.
+constexpr int kNormThreads = 128;
+__global__ __launch_bounds__(kNormThreads) void k_gated_norm(GatedNormArgs a) {
+    __shared__ float scratch[kNormThreads / 64];
+    const int groups = a.n / a.group;
+    const int64_t row = blockIdx.x / groups;
+    const int64_t base = row * a.n + static_cast<int64_t>(blockIdx.x - row * groups) * a.group;
+    float ss = 0.0f;
+    for (int i = threadIdx.x; i < a.group; i += kNormThreads) {
+        const float o = a.o[base + i];
+        ss = fmaf(o, o, ss);
+    }
+    ss = block_sum<kNormThreads / 64>(ss, scratch);
+    const float rms = sqrtf(ss / static_cast<float>(a.group) + a.eps);
+    for (int i = threadIdx.x; i < a.group; i += kNormThreads)
+        a.y[base + i] = (a.o[base + i] / rms) * a.w[i] * silu(a.z[base + i]);
+}
+
+
+// ------------------------------------------------------ fused layer tail
+// The whole recurrent-branch tail for one token in one launch.  One
+// workgroup per (sequence b, key head kh) owns every channel that key head's
+// value heads need: Q head kh, K head kh and the V channels of the RV value
+// heads h = kh + i*Hk.  Owning them outright makes the conv-cache shift
+// race-free, and lets the step read Q, K and V from LDS.  The workgroup issues
+// the nontemporal loads of its RV x 64 KiB of state first and computes the
+// prestate while they are in flight.  Every reduction keeps the order of the
+// three-launch path (k_prestate, k_step, k_gated_norm), so both paths give
+// the same bits.
+constexpr int kTailThreads = 256;
+
+template <int RV, int K>
+__global__ __launch_bounds__(kTailThreads) void k_tail_fused(TailFusedArgs a) {
+    constexpr int kCh = (2 + RV) * D;               // owned channels
+    constexpr int kTiles = RV * kTilesPerHead;      // state tiles of the workgroup
+    constexpr int kTilesPerWave = kTiles / (kTailThreads / 64);
+    __shared__ alignas(16) float act[kCh];          // Q | K | V_0 .. V_{RV-1}
+    __shared__ float core[RV * D];
+    __shared__ float scratch[kTailThreads / 64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int grp = lane >> 3;
+    const int c = lane & 7;
+    const int b = blockIdx.x / a.Hk;
+    const int kh = blockIdx.x - b * a.Hk;
+    const int nq = a.Hk * D;
+
+    // 1. state loads in flight
+    RowSlice r[kTilesPerWave];
+    int64_t roff[kTilesPerWave];
+#pragma unroll
+    for (int j = 0; j < kTilesPerWave; ++j) {
+        const int t = wave * kTilesPerWave + j;
+        const int h = kh + (t / kTilesPerHead) * a.Hk;
+        const int row = (t % kTilesPerHead) * kRowsPerTile + grp;
+        roff[j] = (static_cast<int64_t>(b) * a.Hv + h) * (D * D) + row * D;
+        load_row<true>(r[j], a.state + roff[j], c);
+    }
+
+    // 2. conv-state shift + conv1d + SiLU on the owned channels; the first
+    //    pass holds Q (threads 0..127) and K (threads 128..255), which are
+    //    L2-normalised per head with the reduction order of k_prestate.
+    float *cs = a.conv_state + static_cast<int64_t>(b) * (K - 1) * a.C;
+#pragma unroll
+    for (int pass = 0; pass < (kCh + kTailThreads - 1) / kTailThreads; ++pass) {
+        const int slot = tid + pass * kTailThreads;
+        if (pass > 0 && slot >= kCh) continue;     // only in a partial last pass
+        int ch;
+        if (slot < D)
+            ch = kh * D + slot;
+        else if (slot < 2 * D)
+            ch = nq + kh * D + (slot - D);
+        else
+            ch = 2 * nq + (kh + ((slot - 2 * D) / D) * a.Hk) * D + (slot % D);
+        float win[K];
+#pragma unroll
+        for (int t = 0; t < K - 1; ++t) win[t] = cs[static_cast<int64_t>(t) * a.C + ch];
+        win[K - 1] = a.x[static_cast<int64_t>(b) * a.C + ch];
+        const float *w = a.conv_w + static_cast<int64_t>(ch) * K;
+        float acc = 0.0f;
+#pragma unroll
+        for (int t = 0; t < K; ++t) acc = fmaf(w[t], win[t], acc);
+#pragma unroll
+        for (int t = 0; t < K - 1; ++t) cs[static_cast<int64_t>(t) * a.C + ch] = win[t + 1];
+        float s = silu(acc);
+        if (pass == 0) {
+            float x2 = s * s;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) x2 += __shfl_xor(x2, off, 64);
+            if (lane == 0) scratch[wave] = x2;
+            __syncthreads();
+            const int h2 = wave >> 1;              // 0: Q, 1: K
+            const float ss = (0.0f + scratch[2 * h2]) + scratch[2 * h2 + 1];
+            s = s / fmaxf(sqrtf(ss), 1e-6f);
+        }
+        act[slot] = s;
+        if (a.dbg_qkv) a.dbg_qkv[static_cast<int64_t>(b) * a.C + ch] = s;
+    }
+    __syncthreads();
+
+    // 3. the state step on the preloaded rows; k and q come from LDS
+    VecSlice kv, qv;
+    load_vec(kv, act + D, c);
+    load_vec(qv, act, c);
+#pragma unroll
+    for (int j = 0; j < kTilesPerWave; ++j) {
+        const int t = wave * kTilesPerWave + j;
+        const int i = t / kTilesPerHead;
+        const int h = kh + i * a.Hk;
+        const int row = (t % kTilesPerHead) * kRowsPerTile + grp;
+        const int bh = b * a.Hv + h;
+        const float e = expf(a.gate[bh]);
+        const float o = row_token(r[j], kv, qv, e, a.beta[bh], act[(2 + i) * D + row]);
+        store_row<true>(a.state + roff[j], r[j], c);
+        if (c == 0) core[i * D + row] = o;
+    }
+    __syncthreads();
+
+    // 4. gated RMSNorm x SiLU(z), one 128-element group per value head, with
+    //    the reduction order of k_gated_norm (128 threads per group); with
+    //    RV = 1 the upper 128 threads carry zeros through the barriers.
+    {
+        const int i = tid / D;                     // value head slot
+        const int j = tid - i * D;
+        const bool live = tid < RV * D;
+        const float o = live ? core[tid] : 0.0f;
+        float x2 = fmaf(o, o, 0.0f);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) x2 += __shfl_xor(x2, off, 64);
+        if (lane == 0) scratch[wave] = x2;
+        __syncthreads();
+        if (live) {
+            const float ss = (0.0f + scratch[2 * i]) + scratch[2 * i + 1];
+            const float rms = sqrtf(ss / static_cast<float>(D) + a.eps);
+            const int h = kh + i * a.Hk;
+            const int64_t yo = static_cast<int64_t>(b) * a.Hv * D + static_cast<int64_t>(h) * D + j;
+            a.y[yo] = (o / rms) * a.norm_w[j] * silu(a.z[yo]);
+            if (a.dbg_core) a.dbg_core[yo] = o;
+        }
+    }
+}
+
+}  // namespace
+
+bool tail_fused_supported(int32_t Hv, int32_t Hk, int32_t K, int32_t group) {
+    const int32_t rv = Hv / Hk;
+    return (rv == 1 || rv == 2) && K == 4 && group == D;
+}
+
+hipError_t launch_tail_fused(const TailFusedArgs &a, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hk));
+    if (a.Hv == a.Hk && a.K == 4)
+        k_tail_fused<1, 4><<<grid, dim3(kTailThreads), 0, s>>>(a);
+    else if (a.Hv == 2 * a.Hk && a.K == 4)
+        k_tail_fused<2, 4><<<grid, dim3(kTailThreads), 0, s>>>(a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_prestate(const PrestateArgs &a, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.C / D) * a.B));
+    switch (a.K) {
+    case 2: k_prestate<2><<<grid, dim3(D), 0, s>>>(a); break;
+    case 3: k_prestate<3><<<grid, dim3(D), 0, s>>>(a); break;
+    case 4: k_prestate<4><<<grid, dim3(D), 0, s>>>(a); break;
+    case 5: k_prestate<5><<<grid, dim3(D), 0, s>>>(a); break;
+    case 6: k_prestate<6><<<grid, dim3(D), 0, s>>>(a); break;
+    case 7: k_prestate<7><<<grid, dim3(D), 0, s>>>(a); break;
+    case 8: k_prestate<8><<<grid, dim3(D), 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gated_norm(const GatedNormArgs &a, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.n / a.group) * a.rows));
+    k_gated_norm<<<grid, dim3(kNormThreads), 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace gdn
