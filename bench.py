@@ -349,6 +349,21 @@ def extra_measurements(torch, g, stream, only=None):
                                          ti["gate"], M, ti["z"], ti["norm_w"], y, workspace=ws,
                                          params=three, stream=stream), 200)
         res["config4_layer_tail_b32"]["three_launch_us_per_call"] = ms * 1e3
+        # the same call over 6 state sets in rotation (768 MiB of state, more
+        # than the 256 MB Infinity Cache holds): an HBM-streaming figure
+        sets = [torch.from_numpy(gi.state(c4["seed"], s_, 32)).cuda() for s_ in range(6)]
+        css = [ti["conv_state"].clone() for _ in range(6)]
+        k = [0]
+
+        def rot():
+            i = k[0] % 6
+            k[0] += 1
+            g.layer_tail(ti["x"], ti["conv_w"], css[i], ti["beta"], ti["gate"], sets[i], ti["z"],
+                         ti["norm_w"], y, workspace=ws, stream=stream)
+        ms = timeit(rot, 120)
+        res["config4_layer_tail_b32"]["rotating_6_states_us_per_call"] = ms * 1e3
+        res["config4_layer_tail_b32"]["rotating_GBps"] = 142.75e6 / (ms / 1e3) / 1e9
+        del sets, css
     return res
 
 
