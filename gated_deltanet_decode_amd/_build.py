@@ -28,6 +28,28 @@ HIPCC_FLAGS = [
 ]
 
 
+# A plain-C program that calls the library through its C ABI only (a test).
+C_CHECK_SOURCE = os.path.join(ROOT, "tests", "c", "gdn_c_check.c")
+C_CHECK_BINARY = os.path.join(ROOT, "tests", "c", "gdn_c_check")
+
+
+def build_c_check(verbose: bool = False) -> str:
+    """Compile tests/c/gdn_c_check.c as plain C (gcc, HIP's C runtime API)
+    against libgdn.so."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"),
+           C_CHECK_SOURCE, "-o", C_CHECK_BINARY, "-L", CSRC, "-lgdn", f"-Wl,-rpath,{CSRC}",
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64", f"-Wl,-rpath,{os.path.join(rocm, 'lib')}",
+           "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
+    return C_CHECK_BINARY
+
+
 def hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     return os.path.join(rocm, "bin", "hipcc")
