@@ -56,14 +56,16 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the secondary entry points")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
-    p.add_argument("--config", type=int, default=2, choices=[0, 1, 2, 3, 4],
-                   help="2 (default): the headline run; others: only that configuration's "
-                        "secondary measurement (for profiling)")
+    p.add_argument("--workload", default="step_b256_x36",
+                   choices=["step_b1", "step_b64_x100", "step_b256_x36", "seq_b8_t4096",
+                            "tail_b32"],
+                   help="step_b256_x36 (default): the headline run; the others run only that "
+                        "workload's secondary measurement (for profiling)")
     return p.parse_args()
 
 
-def setup_config2(torch, g):
-    c = gi.CONFIGS[2]
+def setup_step_b256_x36(torch, g):
+    c = gi.WORKLOADS["step_b256_x36"]
     B, L, seed = c["B"], c["layers"], c["seed"]
     log(f"[bench] generating {L} x {B} x {HV} x {D}x{D} f32 states (seeded) ...")
     states = torch.empty((L, B, HV, D, D), device="cuda")
@@ -133,7 +135,7 @@ def run_step36(g, w, stream, evs=None):
             evs[l][1].record(stream)
 
 
-def config2_variants(torch, g, w, stream, steps):
+def step_b256_x36_variants(torch, g, w, stream, steps):
     """The same 36-layer step (a) captured once as a HIP graph and replayed,
     and (b) as one gdn_step launch over all layers: the [36][256] layer and
     sequence axes of the contiguous buffers flattened into B = 9216."""
@@ -200,7 +202,7 @@ def cpu_baseline(seconds):
     import oracle
     from concurrent.futures import ThreadPoolExecutor
     o = oracle.get()
-    c = gi.CONFIGS[2]
+    c = gi.WORKLOADS["step_b256_x36"]
     B, seed, n_layers = c["B"], c["seed"], 4
     threads = max(1, min(16, os.cpu_count() or 1))
     states = [gi.state(seed, l, B) for l in range(n_layers)]
@@ -237,7 +239,7 @@ def cpu_baseline(seconds):
         done1 += 1
     el1 = time.perf_counter() - t1
     return {"value": updates / el, "unit": "state-updates/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} layer-steps of configuration 2 (B=256, 32 heads; layers 0-"
+            "sample": f"{done} layer-steps of the B=256 x 36-layer decode (32 heads; layers 0-"
                       f"{n_layers - 1} stepped round-robin), oracle_gdn_step_M split over "
                       f"{threads} host threads by sequence, {el:.1f} s",
             "GBps": updates * STATE_UPDATE_BYTES / el / 1e9,
@@ -265,14 +267,14 @@ def extra_measurements(torch, g, stream, only=None):
         torch.cuda.synchronize()
         return s.elapsed_time(e) / reps
 
-    # config 0: B=1 single step (latency-bound)
-    if want(0):
+    # step_b1: B=1 single step (latency-bound)
+    if want("step_b1"):
         si = {n: torch.from_numpy(x).cuda() for n, x in gi.step_inputs(1000, 0, 1).items()}
         M = torch.from_numpy(gi.state(1000, 0, 1)).cuda()
         o = torch.empty((1, HV, D), device="cuda")
         ms = timeit(lambda: g.step(si["q"], si["k"], si["v"], si["beta"], si["gate"], M, o,
                                    stream=stream), 1000)
-        res["config0_step_b1"] = {"us_per_call": ms * 1e3, "state_updates_per_s": 32 / (ms / 1e3)}
+        res["step_b1"] = {"us_per_call": ms * 1e3, "state_updates_per_s": 32 / (ms / 1e3)}
         # the same call replayed from a captured graph of 100 calls (no host
         # launch path in the loop: device-side time per call)
         side = torch.cuda.Stream()
@@ -283,11 +285,11 @@ def extra_measurements(torch, g, stream, only=None):
                 g.step(si["q"], si["k"], si["v"], si["beta"], si["gate"], M, o)
         torch.cuda.synchronize()
         ms = timeit(gr.replay, 10) / 100
-        res["config0_step_b1"]["graph_us_per_call"] = ms * 1e3
+        res["step_b1"]["graph_us_per_call"] = ms * 1e3
 
-    # config 1: B=64 decode, 100 calls with fresh inputs
-    if want(1):
-        c1 = gi.CONFIGS[1]
+    # step_b64_x100: B=64 decode, 100 calls with fresh inputs
+    if want("step_b64_x100"):
+        c1 = gi.WORKLOADS["step_b64_x100"]
         M = torch.from_numpy(gi.state(c1["seed"], 0, 64)).cuda()
         ins = [{n: torch.from_numpy(x).cuda() for n, x in gi.step_inputs(c1["seed"], i, 64).items()}
                for i in range(100)]
@@ -298,13 +300,13 @@ def extra_measurements(torch, g, stream, only=None):
                 g.step(t["q"], t["k"], t["v"], t["beta"], t["gate"], M, o, stream=stream)
         ms = timeit(c1run, 3)
         upd = 100 * 64 * HV
-        res["config1_step_b64_x100"] = {"ms": ms, "state_updates_per_s": upd / (ms / 1e3),
+        res["step_b64_x100"] = {"ms": ms, "state_updates_per_s": upd / (ms / 1e3),
                                         "GBps": upd * STATE_UPDATE_BYTES / (ms / 1e3) / 1e9,
                                         "note": "128 MiB state fits the 256 MB Infinity Cache"}
 
     # gdn_pair: B=256, one layer, two positions (state read once, written twice)
     if only is None:
-        c2 = gi.CONFIGS[2]
+        c2 = gi.WORKLOADS["step_b256_x36"]
         si = {n: torch.from_numpy(x).cuda() for n, x in gi.step_inputs(c2["seed"], 0, 256, T=2).items()}
         M = torch.from_numpy(gi.state(c2["seed"], 0, 256)).cuda()
         Mn = torch.empty_like(M)
@@ -317,9 +319,9 @@ def extra_measurements(torch, g, stream, only=None):
                             "bytes_per_call": pair_bytes}
         del M, Mn
 
-    # config 3: gdn_seq B=8 x T=4096 from a zero state
-    if want(3):
-        c3 = gi.CONFIGS[3]
+    # seq_b8_t4096: gdn_seq B=8 x T=4096 from a zero state
+    if want("seq_b8_t4096"):
+        c3 = gi.WORKLOADS["seq_b8_t4096"]
         si = {n: torch.from_numpy(x).cuda() for n, x in gi.step_inputs(c3["seed"], 0, 8, T=4096).items()}
         M = torch.zeros((8, HV, D, D), device="cuda")
         o = torch.empty((8, 4096, HV, D), device="cuda")
@@ -327,14 +329,14 @@ def extra_measurements(torch, g, stream, only=None):
                                   stream=stream), 5)
         upd = 8 * 4096 * HV
         flops = upd * D * D * 7  # decay mul + 3 FMA per element
-        res["config3_seq_b8_t4096"] = {"ms": ms, "state_updates_per_s": upd / (ms / 1e3),
+        res["seq_b8_t4096"] = {"ms": ms, "state_updates_per_s": upd / (ms / 1e3),
                                        "TFLOPs": flops / (ms / 1e3) / 1e12,
                                        "frac_fp32_vector_nonpacked_78.6": flops / (ms / 1e3) / 78.6e12,
                                        "frac_fp32_vector_157.3": flops / (ms / 1e3) / 157.3e12}
 
-    # config 4: layer tail B=32
-    if want(4):
-        c4 = gi.CONFIGS[4]
+    # tail_b32: layer tail B=32
+    if want("tail_b32"):
+        c4 = gi.WORKLOADS["tail_b32"]
         ti = {n: torch.from_numpy(x).cuda() for n, x in gi.tail_inputs(c4["seed"], 32).items()}
         M = torch.from_numpy(gi.state(c4["seed"], 0, 32)).cuda()
         y = torch.empty((32, HV * D), device="cuda")
@@ -342,13 +344,13 @@ def extra_measurements(torch, g, stream, only=None):
         ms = timeit(lambda: g.layer_tail(ti["x"], ti["conv_w"], ti["conv_state"], ti["beta"],
                                          ti["gate"], M, ti["z"], ti["norm_w"], y, workspace=ws,
                                          stream=stream), 200)
-        res["config4_layer_tail_b32"] = {"us_per_call": ms * 1e3,
+        res["tail_b32"] = {"us_per_call": ms * 1e3,
                                          "state_updates_per_s": 32 * HV / (ms / 1e3)}
         three = g.TailParams(4, 128, 1e-6, 1)
         ms = timeit(lambda: g.layer_tail(ti["x"], ti["conv_w"], ti["conv_state"], ti["beta"],
                                          ti["gate"], M, ti["z"], ti["norm_w"], y, workspace=ws,
                                          params=three, stream=stream), 200)
-        res["config4_layer_tail_b32"]["three_launch_us_per_call"] = ms * 1e3
+        res["tail_b32"]["three_launch_us_per_call"] = ms * 1e3
         # the same call over 6 state sets in rotation (768 MiB of state, more
         # than the 256 MB Infinity Cache holds): an HBM-streaming figure
         sets = [torch.from_numpy(gi.state(c4["seed"], s_, 32)).cuda() for s_ in range(6)]
@@ -361,8 +363,8 @@ def extra_measurements(torch, g, stream, only=None):
             g.layer_tail(ti["x"], ti["conv_w"], css[i], ti["beta"], ti["gate"], sets[i], ti["z"],
                          ti["norm_w"], y, workspace=ws, stream=stream)
         ms = timeit(rot, 120)
-        res["config4_layer_tail_b32"]["rotating_6_states_us_per_call"] = ms * 1e3
-        res["config4_layer_tail_b32"]["rotating_GBps"] = 142.75e6 / (ms / 1e3) / 1e9
+        res["tail_b32"]["rotating_6_states_us_per_call"] = ms * 1e3
+        res["tail_b32"]["rotating_GBps"] = 142.75e6 / (ms / 1e3) / 1e9
         del sets, css
     return res
 
@@ -380,13 +382,13 @@ def main():
         sys.exit(1)
 
     stream = torch.cuda.current_stream()
-    if args.config != 2:
-        res = extra_measurements(torch, g, stream, only=args.config)
-        print(json.dumps({"config": args.config, "extra": res}), flush=True)
+    if args.workload != "step_b256_x36":
+        res = extra_measurements(torch, g, stream, only=args.workload)
+        print(json.dumps({"workload": args.workload, "extra": res}), flush=True)
         return
     copy_gbps = copy_probe(torch, stream)
     log(f"[bench] copy probe: {copy_gbps:.0f} GB/s")
-    w = setup_config2(torch, g)
+    w = setup_step_b256_x36(torch, g)
     L, B = w["L"], w["B"]
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -439,7 +441,7 @@ def main():
                                "state per layer, 18 GiB), 32 value / 16 key heads, d=128, "
                                "one token per layer",
                    "global_batch": B, "layers": L, "launches_per_step": L,
-                   "seed": gi.CONFIGS[2]["seed"]},
+                   "seed": gi.WORKLOADS["step_b256_x36"]["seed"]},
         "achieved_GBps_step": updates_per_step * STATE_UPDATE_BYTES / (ms_per_step / 1e3) / 1e9,
         "roofline": {"bound": "hbm", "kernel": "k_step (gdn_step)", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
@@ -452,7 +454,7 @@ def main():
     }
     if not args.no_extra:
         log("[bench] graph replay and flattened single launch of the 36 layers")
-        line["extra_config2"] = config2_variants(torch, g, w, stream, args.steps)
+        line["extra_step_b256_x36"] = step_b256_x36_variants(torch, g, w, stream, args.steps)
         log("[bench] secondary entry points")
         del w
         torch.cuda.empty_cache()

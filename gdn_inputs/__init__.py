@@ -50,13 +50,18 @@ CONV_K = 4
 NORM_GROUP = 128
 NORM_EPS = 1e-6
 
-# Seed of configuration i is 1000 + i.
-CONFIGS = {
-    0: dict(name="step_b1", B=1, seed=1000),
-    1: dict(name="step_b64_x100", B=64, calls=100, seed=1001),
-    2: dict(name="step_b256_x36layers", B=256, layers=36, seed=1002),
-    3: dict(name="seq_b8_t4096", B=8, T=4096, seed=1003),
-    4: dict(name="layer_tail_b32", B=32, seed=1004),
+# The workloads, by what they are; each has its own seed.
+WORKLOADS = {
+    # gdn_step, one sequence, one token
+    "step_b1": dict(B=1, seed=1000),
+    # gdn_step, 64 sequences, 100 calls with fresh inputs (slot = call)
+    "step_b64_x100": dict(B=64, calls=100, seed=1001),
+    # gdn_step, 256 sequences x 36 recurrent layers (slot = layer), 18 GiB of state
+    "step_b256_x36": dict(B=256, layers=36, seed=1002),
+    # gdn_seq, 8 sequences x 4096 tokens from a zero state
+    "seq_b8_t4096": dict(B=8, T=4096, seed=1003),
+    # gdn_layer_tail, 32 sequences, 8192 channels
+    "tail_b32": dict(B=32, seed=1004),
 }
 
 

@@ -432,7 +432,7 @@ def pin_printed_constants(o):
     assert gi.D * gi.D * gi.HV * 4 == G("state_bytes_per_layer")
     assert "%.8e" % np.float32(gi.NORM_EPS) == G("rms_epsilon_f32_printed")
     assert gi.D == G("output_scale_divisor_squared")
-    assert gi.CONFIGS[2]["layers"] == G("recurrent_layers")
+    assert gi.WORKLOADS["step_b256_x36"]["layers"] == G("recurrent_layers")
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -88,7 +88,7 @@ def test_seq_chunked_resume_is_bitwise(g):
 
 
 def test_seq_contraction_from_zero_state(g, orc):
-    """Zero initial state (configuration 3's start) over a ragged T."""
+    """Zero initial state (as in the B=8 x T=4096 workload) over a ragged T."""
     print("\n  gdn_seq zero state T=70", flush=True)
     B, T = 2, 70
     si = gi.step_inputs(3300, 0, B, T=T)

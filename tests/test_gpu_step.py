@@ -48,10 +48,10 @@ def test_step_matches_oracle(g, orc, B, Hv, Hk):
     ref.assert_close("out", og, want, OUT_TOL)
 
 
-def test_config0_single_sequence(g, orc):
-    """Configuration 0: B=1, the page geometry, seed 1000."""
-    c = gi.CONFIGS[0]
-    print("\n  config 0: gdn_step B=1", flush=True)
+def test_step_b1_single_sequence(g, orc):
+    """One sequence, one token, the page geometry."""
+    c = gi.WORKLOADS["step_b1"]
+    print("\n  gdn_step B=1 (step_b1)", flush=True)
     si = gi.step_inputs(c["seed"], 0, 1)
     M = gi.state(c["seed"], 0, 1)
     M64 = M.astype(np.float64)

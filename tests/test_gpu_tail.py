@@ -61,10 +61,10 @@ def check(got, want, state_tol=1e-6):
     assert np.array_equal(got["conv_state"], want["conv_state"]), "conv cache not bitwise"
 
 
-def test_config4_layer_tail(g, orc):
-    """Configuration 4: B=32, 8192 channels, kernel 4, group 128, eps 1e-6."""
-    c = gi.CONFIGS[4]
-    print("\n  config 4: gdn_layer_tail B=32", flush=True)
+def test_tail_b32_layer_tail(g, orc):
+    """B=32, 8192 channels, kernel 4, group 128, eps 1e-6."""
+    c = gi.WORKLOADS["tail_b32"]
+    print("\n  gdn_layer_tail B=32 (tail_b32)", flush=True)
     ti = gi.tail_inputs(c["seed"], c["B"])
     M = gi.state(c["seed"], 0, c["B"])
     got = run_tail(g, ti, M)

@@ -1,11 +1,11 @@
-"""GPU: the full-size configurations, in the launch configuration the
-benchmark times, checked against the oracle on sampled sequences (config 2)
-or in full (configs 1 and 3).
+"""GPU: the full-size workloads, in the launch configuration the benchmark
+times, checked against the oracle on sampled sequences (step_b256_x36) or in
+full (the other two).
 
-  config 1: B=64 decode, 100 gdn_step calls with fresh inputs
-  config 2: B=256 x 36 layers (18 GiB of state), one gdn_step per layer,
-            plus the same 36 layers flattened into one B=9216 call
-  config 3: gdn_seq B=8 x T=4096 from a zero state
+  step_b64_x100: B=64 decode, 100 gdn_step calls with fresh inputs
+  step_b256_x36: B=256 x 36 layers (18 GiB of state), one gdn_step per
+                 layer, plus the same 36 layers flattened into one B=9216 call
+  seq_b8_t4096:  gdn_seq B=8 x T=4096 from a zero state
 """
 import numpy as np
 import pytest
@@ -30,11 +30,11 @@ def dev(a):
 
 
 @pytest.mark.timeout(600)
-def test_config1_b64_x100(g, orc):
+def test_step_b64_x100(g, orc):
     import torch
-    c = gi.CONFIGS[1]
+    c = gi.WORKLOADS["step_b64_x100"]
     B, calls = c["B"], c["calls"]
-    print(f"\n  config 1: gdn_step B={B} x {calls} calls", flush=True)
+    print(f"\n  step_b64_x100: gdn_step B={B} x {calls} calls", flush=True)
     M = gi.state(c["seed"], 0, B)
     Md = dev(M)
     inputs = [gi.step_inputs(c["seed"], i, B) for i in range(calls)]
@@ -60,11 +60,11 @@ def test_config1_b64_x100(g, orc):
 
 
 @pytest.mark.timeout(900)
-def test_config2_b256_x36_layers(g, orc):
+def test_step_b256_x36_layers(g, orc):
     import torch
-    c = gi.CONFIGS[2]
+    c = gi.WORKLOADS["step_b256_x36"]
     B, L, seed = c["B"], c["layers"], c["seed"]
-    print(f"\n  config 2: gdn_step B={B} x {L} layers (18 GiB state)", flush=True)
+    print(f"\n  step_b256_x36: gdn_step B={B} x {L} layers (18 GiB state)", flush=True)
     states = torch.empty((L, B, 32, 128, 128), device="cuda")
     stage = torch.empty((B, 32, 128, 128), pin_memory=True)
     sn = stage.numpy()
@@ -121,11 +121,11 @@ def test_config2_b256_x36_layers(g, orc):
 
 
 @pytest.mark.timeout(600)
-def test_config3_seq_b8_t4096(g, orc):
+def test_seq_b8_t4096(g, orc):
     import torch
-    c = gi.CONFIGS[3]
+    c = gi.WORKLOADS["seq_b8_t4096"]
     B, T = c["B"], c["T"]
-    print(f"\n  config 3: gdn_seq B={B} T={T} from zero state", flush=True)
+    print(f"\n  seq_b8_t4096: gdn_seq B={B} T={T} from zero state", flush=True)
     si = gi.step_inputs(c["seed"], 0, B, T=T)
     M = np.zeros((B, 32, 128, 128), np.float32)
     t = {n: dev(x) for n, x in si.items()}
