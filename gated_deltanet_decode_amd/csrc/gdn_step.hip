@@ -1,6 +1,8 @@
 // gdn_step.hip - gdn_step and gdn_pair: the HBM-streaming one- and
 // two-position kernels (persistent tile walk over the state).
 
+#include <atomic>
+
 #include "gdn_device.hpp"
 
 namespace gdn {
@@ -101,20 +103,21 @@ __global__ __launch_bounds__(kStepWaves * 64) void k_pair(PairArgs a, int n_tile
 #define GDN_STEP_WGS_PER_CU 1
 #endif
 
-// Compute units of the current device (read once per device; a value that
-// never changes, so concurrent first calls race harmlessly).
+// Compute units of the current device, read once per device and cached (a
+// value that never changes; relaxed atomics make concurrent first calls
+// from several host threads well defined).
 static int device_cus() {
-    static int cache[64];
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             n <= 0)
             n = 256;
-        cache[dev] = n;
+        cache[dev].store(n, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return n;
 }
 
 hipError_t launch_step(const StepArgs &a, hipStream_t s) {

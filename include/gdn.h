@@ -38,8 +38,8 @@
  * call may have run.
  *
  * Thread safety: every call may be made concurrently from several host
- * threads.  The library holds no mutable global state apart from the
- * thread-local error text.
+ * threads.  The library's only mutable global state is the thread-local
+ * error text and a per-device cache of the compute-unit count.
  */
 #ifndef GDN_H
 #define GDN_H

@@ -221,6 +221,35 @@ def pin_scalar_recurrence(o):
     assert abs(M[0, 0, 0, 0] - m) <= 1e-5, "final scalar state"
 
 
+def pin_orthonormal_keys_are_all_remembered(o):
+    """With beta=1, gate=0 and T mutually orthonormal keys, each delta-rule
+    update writes v_t along k_t without disturbing the other directions, so
+    after the whole sequence M k_s = v_s for every s <= T (and the output of
+    token t is M_t q_t / sqrt(d)).  Checked on gdn_seq at the page geometry
+    with T = 24 tokens, each key head getting its own orthonormal set."""
+    rng = np.random.default_rng(21)
+    B, T, Hv, Hk, d = 2, 24, 32, 16, 128
+    q = np.empty((B, T, Hk, d), np.float32)
+    k = np.empty((B, T, Hk, d), np.float32)
+    for b in range(B):
+        for h in range(Hk):
+            Q, _ = np.linalg.qr(rng.standard_normal((d, T)))       # orthonormal columns
+            k[b, :, h] = Q.T.astype(np.float32)
+            qq = rng.standard_normal((T, d))
+            q[b, :, h] = (qq / np.linalg.norm(qq, axis=1, keepdims=True)).astype(np.float32)
+    v = rng.standard_normal((B, T, Hv, d)).astype(np.float32)
+    beta = np.ones((B, T, Hv), np.float32)
+    gate = np.zeros((B, T, Hv), np.float32)
+    M = (0.1 * rng.standard_normal((B, Hv, d, d))).astype(np.float32)
+    o.seq(q, k, v, beta, gate, M)
+    for b in range(B):
+        for h in range(Hv):
+            kh = h % Hk
+            R = M[b, h].astype(np.float64) @ k[b, :, kh].astype(np.float64).T    # [d][T]
+            assert np.max(np.abs(R - v[b, :, h].astype(np.float64).T)) <= 2e-5, \
+                f"association lost at b={b} h={h}"
+
+
 def pin_seq_is_repeated_step(o):
     """linear_core: the batch path is the single-token step applied to the
     positions in order, elementwise identical (bitwise here)."""

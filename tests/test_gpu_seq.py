@@ -97,3 +97,43 @@ def test_seq_contraction_from_zero_state(g, orc):
     want = ref.seq_mt(orc, si, M)
     ref.assert_close("state", Mg, M, 1e-6)
     ref.assert_close("out", og, want, 1e-5)
+
+
+def test_seq_keeps_all_associations_with_orthonormal_keys(g):
+    """beta=1, gate=0 and T = 128 mutually orthonormal keys per key head:
+    every token writes v_t along k_t without disturbing the other
+    directions, so after the whole sequence the GPU state satisfies
+    M k_s = v_s for all 128 tokens (a full-rank delta-rule check)."""
+    print("\n  gdn_seq orthonormal keys T=128", flush=True)
+    rng = np.random.default_rng(31)
+    B, T, Hv, Hk, d = 2, 128, 32, 16, 128
+    q = np.empty((B, T, Hk, d), np.float32)
+    k = np.empty((B, T, Hk, d), np.float32)
+    for b in range(B):
+        for h in range(Hk):
+            Q, _ = np.linalg.qr(rng.standard_normal((d, d)))
+            k[b, :, h] = Q.T.astype(np.float32)
+            qq = rng.standard_normal((T, d))
+            q[b, :, h] = (qq / np.linalg.norm(qq, axis=1, keepdims=True)).astype(np.float32)
+    si = dict(q=q, k=k, v=rng.standard_normal((B, T, Hv, d)).astype(np.float32),
+              beta=np.ones((B, T, Hv), np.float32), gate=np.zeros((B, T, Hv), np.float32))
+    M = (0.1 * rng.standard_normal((B, Hv, d, d))).astype(np.float32)
+    Mg, _ = run_seq(g, si, M)
+    worst = 0.0
+    for b in range(B):
+        for h in range(Hv):
+            R = Mg[b, h].astype(np.float64) @ k[b, :, h % Hk].astype(np.float64).T
+            worst = max(worst, float(np.max(np.abs(R - si["v"][b, :, h].astype(np.float64).T))))
+    print(f"    max |M k_s - v_s| over 128 tokens: {worst:.3e}", flush=True)
+    assert worst <= 5e-5
+
+
+def test_seq_more_heads_than_compute_units(g, orc):
+    """B=16 x 32 heads = 512 workgroups (two per CU in turn), ragged T."""
+    print("\n  gdn_seq B=16 T=40 (512 heads)", flush=True)
+    si = gi.step_inputs(3400, 0, 16, T=40)
+    M = gi.state(3400, 0, 16)
+    Mg, og = run_seq(g, si, M)
+    want = ref.seq_mt(orc, si, M)
+    ref.assert_close("state", Mg, M, 1e-6)
+    ref.assert_close("out", og, want, 1e-5)

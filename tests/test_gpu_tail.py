@@ -136,3 +136,13 @@ def test_tail_three_tokens_fill_the_cache(g, orc):
     assert np.array_equal(t["conv_state"].cpu().numpy(), np.stack(xs, 1))
     ref.assert_close("y", y.cpu().numpy(), yo, 1e-5)
     ref.assert_close("state", Md.cpu().numpy(), M, 1e-6)
+
+
+def test_tail_b128(g, orc):
+    """A larger batch (B=128: 2048 workgroups of the single-launch tail)."""
+    print("\n  gdn_layer_tail B=128", flush=True)
+    ti = gi.tail_inputs(4500, 128)
+    M = gi.state(4500, 0, 128)
+    got = run_tail(g, ti, M)
+    want = oracle_tail(orc, ti, M)
+    check(got, want)
