@@ -19,9 +19,10 @@
 // (row_half_mirror, then two quad_perm swaps); all eight lanes end with
 // bitwise-identical sums, so delta is the same in every lane that applies it.
 //
-// All kernels share row_token(), so a row's arithmetic is the same in the
-// single-step kernel, the multi-token kernel and the tail: a T-token gdn_seq
-// is bitwise equal to T gdn_step calls.
+// All kernels share this arithmetic (row_token() or the parts it is split
+// into below), so a row's arithmetic is the same in the single-step kernel,
+// the multi-token kernel and the tail: a T-token gdn_seq is bitwise equal to
+// T gdn_step calls.
 //
 // No MFMA: the update is a sequence of rank-1 updates and matrix-vector
 // products (one multiply-add per state element per operation), which is
@@ -115,6 +116,17 @@ __device__ __forceinline__ float dot_part(const RowSlice &r, const VecSlice &w) 
     return p;
 }
 
+// Step 4 alone: the rank-1 update M[j] += d k^T of this lane's columns.
+__device__ __forceinline__ void update_part(RowSlice &r, float d, const VecSlice &k) {
+#pragma unroll
+    for (int i = 0; i < kF4PerLane; ++i) {
+        r.m[i].x = fmaf(d, k.x[i].x, r.m[i].x);
+        r.m[i].y = fmaf(d, k.x[i].y, r.m[i].y);
+        r.m[i].z = fmaf(d, k.x[i].z, r.m[i].z);
+        r.m[i].w = fmaf(d, k.x[i].w, r.m[i].w);
+    }
+}
+
 // One token on one state row j (steps 1-5), in the page's order.
 // Returns out[j].
 __device__ __forceinline__ float row_token(RowSlice &r, const VecSlice &k, const VecSlice &q,
@@ -128,19 +140,14 @@ __device__ __forceinline__ float row_token(RowSlice &r, const VecSlice &k, const
     }
     const float sk = group_sum(dot_part(r, k));       // 2. sk = M[j] . k
     const float d = (vj - sk) * beta;                 // 3. delta
-#pragma unroll
-    for (int i = 0; i < kF4PerLane; ++i) {           // 4. rank-1 update
-        r.m[i].x = fmaf(d, k.x[i].x, r.m[i].x);
-        r.m[i].y = fmaf(d, k.x[i].y, r.m[i].y);
-        r.m[i].z = fmaf(d, k.x[i].z, r.m[i].z);
-        r.m[i].w = fmaf(d, k.x[i].w, r.m[i].w);
-    }
+    update_part(r, d, k);                             // 4. rank-1 update
     return group_sum(dot_part(r, q)) * kInvSqrtD;     // 5. output, updated state
 }
 
-// The same arithmetic split at the token boundary, for the multi-token
-// kernel: head_part() is steps 1-2 of a token, body_part() steps 4-5, and
-// pass() runs steps 4-5 of token t and steps 1-2 of token t+1 in one sweep
+// The same arithmetic split into parts, for kernels that interleave it with
+// memory traffic or with the next token: head_part() is steps 1-2 of a token
+// (decay, then the key partial), update_part() step 4, body_part() steps 4-5,
+// and pass() steps 4-5 of token t with steps 1-2 of token t+1 in one sweep
 // over the row.  Every element sees exactly the operations of row_token(),
 // in the same order, and the partial sums accumulate in the same element
 // order, so the results are bitwise those of row_token().
