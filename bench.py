@@ -366,6 +366,13 @@ def extra_measurements(torch, g, stream, only=None):
         res["tail_b32"]["rotating_6_states_us_per_call"] = ms * 1e3
         res["tail_b32"]["rotating_GBps"] = 142.75e6 / (ms / 1e3) / 1e9
         del sets, css
+        # the same tail starting from the raw beta/alpha logits (gdn_layer_tail_ba)
+        gin = {n: torch.from_numpy(x).cuda() for n, x in gi.gate_inputs(c4["seed"], 32).items()}
+        wsb = torch.empty(g.layer_tail_ba_workspace_bytes(32), dtype=torch.uint8, device="cuda")
+        ms = timeit(lambda: g.layer_tail_ba(ti["x"], ti["conv_w"], ti["conv_state"], gin["ba"],
+                                            gin["a_log"], gin["dt_bias"], M, ti["z"], ti["norm_w"],
+                                            y, workspace=wsb, stream=stream), 200)
+        res["tail_b32"]["raw_gates_us_per_call"] = ms * 1e3
     return res
 
 

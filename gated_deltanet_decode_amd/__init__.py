@@ -10,6 +10,10 @@ C entry points:
     layer_tail(x, conv_w, conv_state, beta, gate, state, z, norm_w, y, ...)
                                                  -> gdn_layer_tail
     layer_tail_workspace_bytes(B)                -> gdn_layer_tail_workspace_bytes
+    gate_transform(ba, a_log, dt_bias, beta, gate) -> gdn_gate_transform
+    layer_tail_ba(x, conv_w, conv_state, ba, a_log, dt_bias, state, z, norm_w, y, ...)
+                                                 -> gdn_layer_tail_ba
+    layer_tail_ba_workspace_bytes(B)             -> gdn_layer_tail_ba_workspace_bytes
     last_error(), version()
 
 If the library has not been built, importing this package raises: there is
@@ -22,8 +26,9 @@ import os
 
 from ._build import LIBRARY
 
-__all__ = ["GdnError", "Dims", "TailParams", "lib", "step", "seq", "pair", "layer_tail",
-           "layer_tail_workspace_bytes", "last_error", "version", "PAGE_DIMS",
+__all__ = ["GdnError", "Dims", "TailParams", "GateInputs", "lib", "step", "seq", "pair",
+           "layer_tail", "layer_tail_workspace_bytes", "gate_transform", "layer_tail_ba",
+           "layer_tail_ba_workspace_bytes", "last_error", "version", "PAGE_DIMS",
            "PAGE_TAIL", "ERRORS"]
 
 if not os.path.exists(LIBRARY):
@@ -43,6 +48,12 @@ class TailParams(ctypes.Structure):
                 ("norm_eps", ctypes.c_float), ("force_unfused", ctypes.c_int32)]
 
 
+class GateInputs(ctypes.Structure):
+    """gdn_gate_inputs (device pointers)"""
+    _fields_ = [("ba", ctypes.c_void_p), ("a_log", ctypes.c_void_p),
+                ("dt_bias", ctypes.c_void_p)]
+
+
 PAGE_DIMS = Dims(32, 16, 128, 128)
 PAGE_TAIL = TailParams(4, 128, 1e-6, 0)
 
@@ -53,6 +64,7 @@ _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
 _DP = ctypes.POINTER(Dims)
 _TP = ctypes.POINTER(TailParams)
+_GP = ctypes.POINTER(GateInputs)
 
 lib = ctypes.CDLL(LIBRARY)
 lib.gdn_version.restype = ctypes.c_int
@@ -69,6 +81,13 @@ lib.gdn_layer_tail.restype = ctypes.c_int
 lib.gdn_layer_tail.argtypes = [_DP, _TP, _i32] + [_vp] * 11 + [_vp, ctypes.c_size_t, _vp]
 lib.gdn_layer_tail_workspace_bytes.restype = ctypes.c_size_t
 lib.gdn_layer_tail_workspace_bytes.argtypes = [_DP, _i32]
+lib.gdn_gate_transform.restype = ctypes.c_int
+lib.gdn_gate_transform.argtypes = [_DP, _i32, _GP, _vp, _vp, _vp]
+lib.gdn_layer_tail_ba.restype = ctypes.c_int
+lib.gdn_layer_tail_ba.argtypes = [_DP, _TP, _i32] + [_vp] * 3 + [_GP] + [_vp] * 6 + \
+    [_vp, ctypes.c_size_t, _vp]
+lib.gdn_layer_tail_ba_workspace_bytes.restype = ctypes.c_size_t
+lib.gdn_layer_tail_ba_workspace_bytes.argtypes = [_DP, _i32]
 
 
 class GdnError(RuntimeError):
@@ -171,26 +190,72 @@ def layer_tail_workspace_bytes(B: int, dims: Dims = PAGE_DIMS) -> int:
     return int(lib.gdn_layer_tail_workspace_bytes(ctypes.byref(dims), B))
 
 
+def _workspace(workspace):
+    import torch
+    if workspace is None:
+        return None, 0
+    if not (isinstance(workspace, torch.Tensor) and workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 def layer_tail(x, conv_w, conv_state, beta, gate, state, z, norm_w, y,
                dbg_qkv=None, dbg_core=None, workspace=None,
                dims: Dims = PAGE_DIMS, params: TailParams = PAGE_TAIL, stream=None) -> None:
     """gdn_layer_tail.  workspace: a GPU tensor of at least
     layer_tail_workspace_bytes(B) bytes (any dtype), or None when both dbg
     buffers are given."""
-    import torch
     B, C = x.shape
     K = params.conv_kernel
     nv = dims.n_v_heads * dims.d_v
-    ws_ptr, ws_bytes = None, 0
-    if workspace is not None:
-        if not (isinstance(workspace, torch.Tensor) and workspace.is_cuda and workspace.is_contiguous()):
-            raise ValueError("workspace must be a contiguous GPU tensor")
-        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    ws_ptr, ws_bytes = _workspace(workspace)
     _check(lib.gdn_layer_tail(
         ctypes.byref(dims), ctypes.byref(params), B,
         _ptr(x, "x", (B, C)), _ptr(conv_w, "conv_w", (C, K)),
         _ptr(conv_state, "conv_state", (B, K - 1, C)),
         _ptr(beta, "beta", (B, dims.n_v_heads)), _ptr(gate, "gate", (B, dims.n_v_heads)),
+        _ptr(state, "state", (B, dims.n_v_heads, dims.d_v, dims.d_k)),
+        _ptr(z, "z", (B, nv)), _ptr(norm_w, "norm_w", (params.norm_group,)),
+        _ptr(y, "y", (B, nv)),
+        _ptr(dbg_qkv, "dbg_qkv", (B, C), optional=True),
+        _ptr(dbg_core, "dbg_core", (B, dims.n_v_heads, dims.d_v), optional=True),
+        ws_ptr, ws_bytes, _stream(stream)))
+
+
+def _gate_inputs(ba, a_log, dt_bias, B, Hv):
+    return GateInputs(_ptr(ba, "ba", (B, 2 * Hv)), _ptr(a_log, "a_log", (Hv,)),
+                      _ptr(dt_bias, "dt_bias", (Hv,)))
+
+
+def gate_transform(ba, a_log, dt_bias, beta, gate, dims: Dims = PAGE_DIMS, stream=None) -> None:
+    """gdn_gate_transform: ba [B][2*Hv] (beta logits | alpha logits), a_log and
+    dt_bias [Hv] -> beta, gate [B][Hv]."""
+    B = ba.shape[0]
+    Hv = dims.n_v_heads
+    gi = _gate_inputs(ba, a_log, dt_bias, B, Hv)
+    _check(lib.gdn_gate_transform(ctypes.byref(dims), B, ctypes.byref(gi),
+                                  _ptr(beta, "beta", (B, Hv)), _ptr(gate, "gate", (B, Hv)),
+                                  _stream(stream)))
+
+
+def layer_tail_ba_workspace_bytes(B: int, dims: Dims = PAGE_DIMS) -> int:
+    return int(lib.gdn_layer_tail_ba_workspace_bytes(ctypes.byref(dims), B))
+
+
+def layer_tail_ba(x, conv_w, conv_state, ba, a_log, dt_bias, state, z, norm_w, y,
+                  dbg_qkv=None, dbg_core=None, workspace=None,
+                  dims: Dims = PAGE_DIMS, params: TailParams = PAGE_TAIL, stream=None) -> None:
+    """gdn_layer_tail_ba: layer_tail with beta and gate made from the raw gate
+    inputs.  workspace: at least layer_tail_ba_workspace_bytes(B) bytes."""
+    B, C = x.shape
+    K = params.conv_kernel
+    nv = dims.n_v_heads * dims.d_v
+    gi = _gate_inputs(ba, a_log, dt_bias, B, dims.n_v_heads)
+    ws_ptr, ws_bytes = _workspace(workspace)
+    _check(lib.gdn_layer_tail_ba(
+        ctypes.byref(dims), ctypes.byref(params), B,
+        _ptr(x, "x", (B, C)), _ptr(conv_w, "conv_w", (C, K)),
+        _ptr(conv_state, "conv_state", (B, K - 1, C)), ctypes.byref(gi),
         _ptr(state, "state", (B, dims.n_v_heads, dims.d_v, dims.d_k)),
         _ptr(z, "z", (B, nv)), _ptr(norm_w, "norm_w", (params.norm_group,)),
         _ptr(y, "y", (B, nv)),

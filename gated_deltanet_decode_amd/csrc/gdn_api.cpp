@@ -231,12 +231,28 @@ size_t gdn_layer_tail_workspace_bytes(const gdn_dims *dims, int32_t B) {
     return qkv + core;  // both parts are multiples of 16 bytes (d_k = d_v = 128)
 }
 
-int gdn_layer_tail(const gdn_dims *dims, const gdn_tail_params *params, int32_t B,
-                   const float *x, const float *conv_w, float *conv_state, const float *beta,
-                   const float *gate, float *state, const float *z, const float *norm_w, float *y,
-                   float *dbg_qkv, float *dbg_core, void *workspace, size_t workspace_bytes,
-                   void *stream) {
-    clear_error();
+}  // extern "C"
+
+namespace {
+
+// Checks the raw gate inputs of B sequences.
+int check_gate_inputs(const gdn_dims *dims, int32_t B, const gdn_gate_inputs *in, Buf *bufs) {
+    if (!in) return fail(GDN_ERR_NULL, "gate inputs are NULL");
+    const size_t f = sizeof(float);
+    bufs[0] = {"ba", in->ba, static_cast<size_t>(B) * 2 * dims->n_v_heads * f};
+    bufs[1] = {"a_log", in->a_log, static_cast<size_t>(dims->n_v_heads) * f};
+    bufs[2] = {"dt_bias", in->dt_bias, static_cast<size_t>(dims->n_v_heads) * f};
+    return check_ptrs(bufs, 3, 4);
+}
+
+// The layer tail with beta/gate given (raw == NULL) or computed from the raw
+// gate inputs.  With raw inputs the unfused path writes beta and gate to the
+// end of the workspace first.
+int layer_tail(const char *name, const gdn_dims *dims, const gdn_tail_params *params, int32_t B,
+               const float *x, const float *conv_w, float *conv_state, const float *beta,
+               const float *gate, const gdn_gate_inputs *raw, float *state, const float *z,
+               const float *norm_w, float *y, float *dbg_qkv, float *dbg_core, void *workspace,
+               size_t workspace_bytes, void *stream) {
     GDN_TRY(check_dims(dims));
     if (!params) return fail(GDN_ERR_NULL, "params is NULL");
     GDN_TRY(check_batch(dims, B, "B"));
@@ -263,15 +279,20 @@ int gdn_layer_tail(const gdn_dims *dims, const gdn_tail_params *params, int32_t 
 
     const Buf vec[] = {{"x", x, nx}, {"conv_state", conv_state, ncs}, {"state", state, ns},
                        {"z", z, nz}, {"y", y, nz}};
-    const Buf sc[] = {{"conv_w", conv_w, nw}, {"beta", beta, nh}, {"gate", gate, nh},
-                      {"norm_w", norm_w, nnw}};
+    Buf sc[6] = {{"conv_w", conv_w, nw}, {"norm_w", norm_w, nnw}, {"beta", beta, nh},
+                 {"gate", gate, nh}};
+    int n_sc = 4;
+    if (raw) {
+        GDN_TRY(check_gate_inputs(dims, B, raw, sc + 2));
+        n_sc = 5;
+    }
     GDN_TRY(check_ptrs(vec, 5, 16));
-    GDN_TRY(check_ptrs(sc, 4, 4));
+    GDN_TRY(check_ptrs(sc, n_sc, 4));
     if (dbg_qkv && !aligned(dbg_qkv, 16)) return fail(GDN_ERR_ALIGN, "dbg_qkv is not 16-byte aligned");
     if (dbg_core && !aligned(dbg_core, 16))
         return fail(GDN_ERR_ALIGN, "dbg_core is not 16-byte aligned");
 
-    const size_t need = (dbg_qkv ? 0 : nx) + (dbg_core ? 0 : nz);
+    const size_t need = (dbg_qkv ? 0 : nx) + (dbg_core ? 0 : nz) + (raw ? 2 * nh : 0);
     if (need > 0) {
         if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
         if (!aligned(workspace, 16)) return fail(GDN_ERR_ALIGN, "workspace is not 16-byte aligned");
@@ -279,17 +300,37 @@ int gdn_layer_tail(const gdn_dims *dims, const gdn_tail_params *params, int32_t 
             return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
                         need);
     }
-    float *qkv = dbg_qkv ? dbg_qkv : static_cast<float *>(workspace);
-    float *core = dbg_core ? dbg_core
-                           : static_cast<float *>(workspace) + (dbg_qkv ? 0 : nx / f);
+    float *ws = static_cast<float *>(workspace);
+    float *qkv = dbg_qkv ? dbg_qkv : ws;
+    float *core = dbg_core ? dbg_core : ws + (dbg_qkv ? 0 : nx / f);
+    float *wbeta = raw ? ws + ((dbg_qkv ? 0 : nx) + (dbg_core ? 0 : nz)) / f : nullptr;
+    float *wgate = raw ? wbeta + nh / f : nullptr;
+    if (raw) {
+        beta = wbeta;
+        gate = wgate;
+    }
 
-    const Buf all[] = {vec[0], vec[1], vec[2], vec[3], vec[4], sc[0],
-                       sc[1],  sc[2],  sc[3],  {"qkv buffer", qkv, nx}, {"core buffer", core, nz}};
-    const Buf outs[] = {vec[1], vec[2], vec[4], all[9], all[10]};
-    GDN_TRY(check_alias(outs, 5, all, 11));
+    // Every written buffer (conv_state, state, y and the intermediates) must be
+    // disjoint from every other buffer; outputs are copies of entries of all[].
+    Buf all[16];
+    int n_all = 0;
+    for (const Buf &b : vec) all[n_all++] = b;
+    for (int i = 0; i < n_sc; ++i) all[n_all++] = sc[i];
+    const int i_mid = n_all;
+    all[n_all++] = {"qkv buffer", qkv, nx};
+    all[n_all++] = {"core buffer", core, nz};
+    if (raw) {
+        all[n_all++] = {"beta buffer", wbeta, nh};
+        all[n_all++] = {"gate buffer", wgate, nh};
+    }
+    Buf outs[7] = {vec[1], vec[2], vec[4]};
+    int n_out = 3;
+    for (int i = i_mid; i < n_all; ++i) outs[n_out++] = all[i];
+    GDN_TRY(check_alias(outs, n_out, all, n_all));
 
     const hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
+    char what[96];
 
     if (!params->force_unfused &&
         gdn::tail_fused_supported(dims->n_v_heads, dims->n_k_heads, K, params->norm_group)) {
@@ -297,8 +338,11 @@ int gdn_layer_tail(const gdn_dims *dims, const gdn_tail_params *params, int32_t 
         fa.x = x;
         fa.conv_w = conv_w;
         fa.conv_state = conv_state;
-        fa.beta = beta;
-        fa.gate = gate;
+        fa.beta = raw ? nullptr : beta;
+        fa.gate = raw ? nullptr : gate;
+        fa.ba = raw ? raw->ba : nullptr;
+        fa.a_log = raw ? raw->a_log : nullptr;
+        fa.dt_bias = raw ? raw->dt_bias : nullptr;
         fa.state = state;
         fa.z = z;
         fa.norm_w = norm_w;
@@ -311,7 +355,21 @@ int gdn_layer_tail(const gdn_dims *dims, const gdn_tail_params *params, int32_t 
         fa.C = static_cast<int32_t>(C);
         fa.K = K;
         fa.eps = params->norm_eps;
-        return hip_status(gdn::launch_tail_fused(fa, s), "gdn_layer_tail fused launch");
+        snprintf(what, sizeof what, "%s fused launch", name);
+        return hip_status(gdn::launch_tail_fused(fa, s), what);
+    }
+
+    if (raw) {
+        gdn::GateArgs ga{};
+        ga.ba = raw->ba;
+        ga.a_log = raw->a_log;
+        ga.dt_bias = raw->dt_bias;
+        ga.beta = wbeta;
+        ga.gate = wgate;
+        ga.B = B;
+        ga.Hv = dims->n_v_heads;
+        snprintf(what, sizeof what, "%s gate-transform launch", name);
+        GDN_TRY(hip_status(gdn::launch_gate_transform(ga, s), what));
     }
 
     gdn::PrestateArgs pa{};
@@ -323,7 +381,8 @@ int gdn_layer_tail(const gdn_dims *dims, const gdn_tail_params *params, int32_t 
     pa.C = static_cast<int32_t>(C);
     pa.K = K;
     pa.n_qk = 2 * dims->n_k_heads * dims->d_k;
-    GDN_TRY(hip_status(gdn::launch_prestate(pa, s), "gdn_layer_tail prestate launch"));
+    snprintf(what, sizeof what, "%s prestate launch", name);
+    GDN_TRY(hip_status(gdn::launch_prestate(pa, s), what));
 
     gdn::StepArgs sa{};
     sa.q = qkv;
@@ -338,7 +397,8 @@ int gdn_layer_tail(const gdn_dims *dims, const gdn_tail_params *params, int32_t 
     sa.B = B;
     sa.Hv = dims->n_v_heads;
     sa.Hk = dims->n_k_heads;
-    GDN_TRY(hip_status(gdn::launch_step(sa, s), "gdn_layer_tail step launch"));
+    snprintf(what, sizeof what, "%s step launch", name);
+    GDN_TRY(hip_status(gdn::launch_step(sa, s), what));
 
     gdn::GatedNormArgs na{};
     na.o = core;
@@ -349,7 +409,67 @@ int gdn_layer_tail(const gdn_dims *dims, const gdn_tail_params *params, int32_t 
     na.n = static_cast<int32_t>(nvw);
     na.group = params->norm_group;
     na.eps = params->norm_eps;
-    return hip_status(gdn::launch_gated_norm(na, s), "gdn_layer_tail gated-norm launch");
+    snprintf(what, sizeof what, "%s gated-norm launch", name);
+    return hip_status(gdn::launch_gated_norm(na, s), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_layer_tail(const gdn_dims *dims, const gdn_tail_params *params, int32_t B,
+                   const float *x, const float *conv_w, float *conv_state, const float *beta,
+                   const float *gate, float *state, const float *z, const float *norm_w, float *y,
+                   float *dbg_qkv, float *dbg_core, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+    clear_error();
+    return layer_tail("gdn_layer_tail", dims, params, B, x, conv_w, conv_state, beta, gate,
+                      nullptr, state, z, norm_w, y, dbg_qkv, dbg_core, workspace,
+                      workspace_bytes, stream);
+}
+
+int gdn_layer_tail_ba(const gdn_dims *dims, const gdn_tail_params *params, int32_t B,
+                      const float *x, const float *conv_w, float *conv_state,
+                      const gdn_gate_inputs *gates, float *state, const float *z,
+                      const float *norm_w, float *y, float *dbg_qkv, float *dbg_core,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+    clear_error();
+    if (!gates) return fail(GDN_ERR_NULL, "gates is NULL");
+    return layer_tail("gdn_layer_tail_ba", dims, params, B, x, conv_w, conv_state, nullptr,
+                      nullptr, gates, state, z, norm_w, y, dbg_qkv, dbg_core, workspace,
+                      workspace_bytes, stream);
+}
+
+size_t gdn_layer_tail_ba_workspace_bytes(const gdn_dims *dims, int32_t B) {
+    const size_t base = gdn_layer_tail_workspace_bytes(dims, B);
+    if (base == 0) return 0;
+    return base + 2 * static_cast<size_t>(B) * dims->n_v_heads * sizeof(float);
+}
+
+int gdn_gate_transform(const gdn_dims *dims, int32_t B, const gdn_gate_inputs *in, float *beta,
+                       float *gate, void *stream) {
+    clear_error();
+    GDN_TRY(check_dims(dims));
+    GDN_TRY(check_batch(dims, B, "B"));
+    Buf inb[3];
+    GDN_TRY(check_gate_inputs(dims, B, in, inb));
+    const size_t nh = static_cast<size_t>(B) * dims->n_v_heads * sizeof(float);
+    const Buf ob[] = {{"beta", beta, nh}, {"gate", gate, nh}};
+    GDN_TRY(check_ptrs(ob, 2, 4));
+    const Buf all[] = {inb[0], inb[1], inb[2], ob[0], ob[1]};
+    GDN_TRY(check_alias(ob, 2, all, 5));
+
+    gdn::GateArgs a{};
+    a.ba = in->ba;
+    a.a_log = in->a_log;
+    a.dt_bias = in->dt_bias;
+    a.beta = beta;
+    a.gate = gate;
+    a.B = B;
+    a.Hv = dims->n_v_heads;
+    (void)hipGetLastError();
+    return hip_status(gdn::launch_gate_transform(a, static_cast<hipStream_t>(stream)),
+                      "gdn_gate_transform launch");
 }
 
 }  // extern "C"

@@ -222,5 +222,20 @@ __device__ __forceinline__ float block_sum(float x, float *scratch) {
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
+// beta/alpha parameter transforms (Red Lite dev15a, "Validation boundary":
+// named as the stage before the update; the formula is the reading of the
+// Gated DeltaNet paper's Mamba-2 style gating):
+//   beta = 1 / (1 + exp(-b)),  gate = -exp(a_log) * softplus(a + dt_bias),
+// softplus(x) = log(1 + exp(x)), evaluated as x + log1p(exp(-x)) for x > 0.
+__device__ __forceinline__ float softplus(float x) {
+    return x > 0.0f ? x + log1pf(expf(-x)) : log1pf(expf(x));
+}
+
+__device__ __forceinline__ void beta_gate(float b, float a, float a_log, float dt_bias,
+                                          float &beta, float &gate) {
+    beta = 1.0f / (1.0f + expf(-b));
+    gate = -expf(a_log) * softplus(a + dt_bias);
+}
+
 }  // namespace
 }  // namespace gdn

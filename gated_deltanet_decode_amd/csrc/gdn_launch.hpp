@@ -82,13 +82,30 @@ struct GatedNormArgs {
     float eps;
 };
 
+// beta/alpha parameter transforms: beta, gate [B][Hv] from the raw projection
+// ba [B][2*Hv] ([beta logits | alpha logits]) and a_log, dt_bias [Hv].
+struct GateArgs {
+    const float *ba;
+    const float *a_log;
+    const float *dt_bias;
+    float *beta;
+    float *gate;
+    int32_t B;
+    int32_t Hv;
+};
+
 // The whole tail in one launch (one workgroup per sequence and key head).
+// beta/gate are used as given, or, when ba is set, computed in the kernel
+// from ba, a_log and dt_bias as in GateArgs.
 struct TailFusedArgs {
     const float *x;
     const float *conv_w;
     float *conv_state;
     const float *beta;
     const float *gate;
+    const float *ba;       // optional raw gate inputs (then beta/gate are unused)
+    const float *a_log;
+    const float *dt_bias;
     float *state;
     const float *z;
     const float *norm_w;
@@ -113,5 +130,6 @@ hipError_t launch_seq(const SeqArgs &a, hipStream_t s);
 hipError_t launch_pair(const PairArgs &a, hipStream_t s);
 hipError_t launch_prestate(const PrestateArgs &a, hipStream_t s);
 hipError_t launch_gated_norm(const GatedNormArgs &a, hipStream_t s);
+hipError_t launch_gate_transform(const GateArgs &a, hipStream_t s);
 
 }  // namespace gdn

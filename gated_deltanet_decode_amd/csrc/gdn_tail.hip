@@ -1,5 +1,5 @@
-// gdn_tail.hip - gdn_layer_tail: conv1d prestate, gated RMSNorm and the
-// single-launch fused tail.
+// gdn_tail.hip - gdn_layer_tail: conv1d prestate, gated RMSNorm, the
+// beta/alpha parameter transforms and the single-launch fused tail.
 
 #include "gdn_device.hpp"
 
@@ -57,6 +57,17 @@ __global__ __launch_bounds__(kNormThreads) void k_gated_norm(GatedNormArgs a) {
         a.y[base + i] = (a.o[base + i] / rms) * a.w[i] * silu(a.z[base + i]);
 }
 
+// beta/alpha parameter transforms, one thread per (sequence, value head).
+constexpr int kGateThreads = 256;
+__global__ __launch_bounds__(kGateThreads) void k_gate_transform(GateArgs a) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kGateThreads + threadIdx.x;
+    if (i >= static_cast<int64_t>(a.B) * a.Hv) return;
+    const int64_t b = i / a.Hv;
+    const int h = static_cast<int>(i - b * a.Hv);
+    const float *row = a.ba + b * 2 * a.Hv;
+    beta_gate(row[h], row[a.Hv + h], a.a_log[h], a.dt_bias[h], a.beta[i], a.gate[i]);
+}
+
 
 // ------------------------------------------------------ fused layer tail
 // The whole recurrent-branch tail for one token in one launch.  One
@@ -67,10 +78,11 @@ __global__ __launch_bounds__(kNormThreads) void k_gated_norm(GatedNormArgs a) {
 // the nontemporal loads of its RV x 64 KiB of state first and computes the
 // prestate while they are in flight.  Every reduction keeps the order of the
 // three-launch path (k_prestate, k_step, k_gated_norm), so both paths give
-// the same bits.
+// the same bits.  With kRaw the lanes also make their heads' beta and gate
+// from the raw gate inputs with beta_gate(), as k_gate_transform does.
 constexpr int kTailThreads = 256;
 
-template <int RV, int K>
+template <int RV, int K, bool kRaw>
 __global__ __launch_bounds__(kTailThreads) void k_tail_fused(TailFusedArgs a) {
     constexpr int kCh = (2 + RV) * D;               // owned channels
     constexpr int kTiles = RV * kTilesPerHead;      // state tiles of the workgroup
@@ -88,16 +100,30 @@ __global__ __launch_bounds__(kTailThreads) void k_tail_fused(TailFusedArgs a) {
     const int kh = blockIdx.x - b * a.Hk;
     const int nq = a.Hk * D;
 
-    // 1. state loads in flight
+    // 1. state loads in flight, with the wave's beta and gate (or, with kRaw,
+    //    the raw logits and per-head parameters they are made from).  All
+    //    tiles of a wave lie in one value head.
+    static_assert(kTilesPerHead % kTilesPerWave == 0, "a wave's tiles must share a head");
+    const int hw = kh + (wave * kTilesPerWave / kTilesPerHead) * a.Hk;
     RowSlice r[kTilesPerWave];
     int64_t roff[kTilesPerWave];
 #pragma unroll
     for (int j = 0; j < kTilesPerWave; ++j) {
         const int t = wave * kTilesPerWave + j;
-        const int h = kh + (t / kTilesPerHead) * a.Hk;
         const int row = (t % kTilesPerHead) * kRowsPerTile + grp;
-        roff[j] = (static_cast<int64_t>(b) * a.Hv + h) * (D * D) + row * D;
+        roff[j] = (static_cast<int64_t>(b) * a.Hv + hw) * (D * D) + row * D;
         load_row<true>(r[j], a.state + roff[j], c);
+    }
+    float bt = 0.0f, gt = 0.0f, raw_b = 0.0f, raw_a = 0.0f, raw_l = 0.0f, raw_d = 0.0f;
+    if constexpr (kRaw) {
+        const float *ba = a.ba + static_cast<int64_t>(b) * 2 * a.Hv;
+        raw_b = ba[hw];
+        raw_a = ba[a.Hv + hw];
+        raw_l = a.a_log[hw];
+        raw_d = a.dt_bias[hw];
+    } else {
+        bt = a.beta[static_cast<int64_t>(b) * a.Hv + hw];
+        gt = a.gate[static_cast<int64_t>(b) * a.Hv + hw];
     }
 
     // 2. conv-state shift + conv1d + SiLU on the owned channels; the first
@@ -139,6 +165,8 @@ __global__ __launch_bounds__(kTailThreads) void k_tail_fused(TailFusedArgs a) {
         act[slot] = s;
         if (a.dbg_qkv) a.dbg_qkv[static_cast<int64_t>(b) * a.C + ch] = s;
     }
+    if constexpr (kRaw) beta_gate(raw_b, raw_a, raw_l, raw_d, bt, gt);
+    const float e = expf(gt);
     __syncthreads();
 
     // 3. the state step on the preloaded rows; k and q come from LDS
@@ -149,11 +177,8 @@ __global__ __launch_bounds__(kTailThreads) void k_tail_fused(TailFusedArgs a) {
     for (int j = 0; j < kTilesPerWave; ++j) {
         const int t = wave * kTilesPerWave + j;
         const int i = t / kTilesPerHead;
-        const int h = kh + i * a.Hk;
         const int row = (t % kTilesPerHead) * kRowsPerTile + grp;
-        const int bh = b * a.Hv + h;
-        const float e = expf(a.gate[bh]);
-        const float o = row_token(r[j], kv, qv, e, a.beta[bh], act[(2 + i) * D + row]);
+        const float o = row_token(r[j], kv, qv, e, bt, act[(2 + i) * D + row]);
         store_row<true>(a.state + roff[j], r[j], c);
         if (c == 0) core[i * D + row] = o;
     }
@@ -192,12 +217,20 @@ bool tail_fused_supported(int32_t Hv, int32_t Hk, int32_t K, int32_t group) {
 
 hipError_t launch_tail_fused(const TailFusedArgs &a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hk));
-    if (a.Hv == a.Hk && a.K == 4)
-        k_tail_fused<1, 4><<<grid, dim3(kTailThreads), 0, s>>>(a);
-    else if (a.Hv == 2 * a.Hk && a.K == 4)
-        k_tail_fused<2, 4><<<grid, dim3(kTailThreads), 0, s>>>(a);
-    else
+    const bool raw = a.ba != nullptr;
+    if (a.Hv == a.Hk && a.K == 4) {
+        if (raw)
+            k_tail_fused<1, 4, true><<<grid, dim3(kTailThreads), 0, s>>>(a);
+        else
+            k_tail_fused<1, 4, false><<<grid, dim3(kTailThreads), 0, s>>>(a);
+    } else if (a.Hv == 2 * a.Hk && a.K == 4) {
+        if (raw)
+            k_tail_fused<2, 4, true><<<grid, dim3(kTailThreads), 0, s>>>(a);
+        else
+            k_tail_fused<2, 4, false><<<grid, dim3(kTailThreads), 0, s>>>(a);
+    } else {
         return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
@@ -219,6 +252,13 @@ hipError_t launch_prestate(const PrestateArgs &a, hipStream_t s) {
 hipError_t launch_gated_norm(const GatedNormArgs &a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.n / a.group) * a.rows));
     k_gated_norm<<<grid, dim3(kNormThreads), 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_transform(const GateArgs &a, hipStream_t s) {
+    const int64_t n = static_cast<int64_t>(a.B) * a.Hv;
+    const dim3 grid(static_cast<unsigned>((n + kGateThreads - 1) / kGateThreads));
+    k_gate_transform<<<grid, dim3(kGateThreads), 0, s>>>(a);
     return hipGetLastError();
 }
 

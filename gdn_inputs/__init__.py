@@ -31,6 +31,11 @@ Distributions (one token per call unless stated):
 * conv_state   N(0,1)
 * z            N(0,1)
 * norm_w       1 + N(0, 0.02^2)
+* ba           N(0,1)  raw beta/alpha projection outputs, [B][2*Hv]
+* a_log        log U(1, 16) per value head
+* dt_bias      softplus^-1(dt), dt = exp(U(log 1e-3, log 1e-1)) per value head
+               (the pages give no values for a_log and dt_bias; these ranges
+               follow the published Mamba-2 initialisation; synthetic)
 """
 from __future__ import annotations
 
@@ -42,6 +47,7 @@ import numpy as np
 STREAMS = {
     "state": 1, "q": 2, "k": 3, "v": 4, "beta": 5, "gate": 6,
     "x": 7, "z": 8, "conv_w": 9, "conv_state": 10, "norm_w": 11,
+    "ba": 12, "a_log": 13, "dt_bias": 14,
 }
 
 # The page geometry (value heads, key heads, head dim) and the tail geometry.
@@ -163,6 +169,19 @@ def tail_inputs(seed, B, Hv=HV, Hk=HK, d=D, K=CONV_K, group=NORM_GROUP, b0=0, sl
     si = step_inputs(seed, slot, B, Hv, Hk, d, b0)
     return dict(x=x, conv_w=conv_w, conv_state=cs, z=z, norm_w=norm_w,
                 beta=si["beta"], gate=si["gate"])
+
+
+# ---------------------------------------------------------------- gate inputs
+def gate_inputs(seed, B, Hv=HV, b0=0, slot=0):
+    """Raw inputs of the beta/alpha parameter transforms for sequences
+    b0 .. b0+B-1: ba [B][2*Hv] and the per-head a_log, dt_bias [Hv]."""
+    ba = np.empty((B, 2 * Hv), np.float32)
+    _parallel(lambda i: normal32_into(ba[i], seed, "ba", slot, b0 + i), B)
+    u = _gen(seed, "a_log", slot, 0).uniform(1.0, 16.0, Hv)
+    a_log = np.log(u).astype(np.float32)
+    dt = np.exp(_gen(seed, "dt_bias", slot, 0).uniform(np.log(1e-3), np.log(1e-1), Hv))
+    dt_bias = (dt + np.log(-np.expm1(-dt))).astype(np.float32)
+    return dict(ba=ba, a_log=a_log, dt_bias=dt_bias)
 
 
 def _parallel(fn, n):

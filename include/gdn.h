@@ -17,7 +17,8 @@
  *   - All tensors are float32 (IEEE binary32), row-major and contiguous.
  *   - Every pointer is a device pointer (hipMalloc'd or torch CUDA memory)
  *     that the caller owns; the library keeps no reference after the call.
- *   - Tensor pointers must be 16-byte aligned; beta and gate 4-byte aligned.
+ *   - Tensor pointers must be 16-byte aligned; per-head vectors (beta, gate,
+ *     the raw gate inputs, conv_w, norm_w) 4-byte aligned.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls enqueue their kernels on it and return without synchronising.
  *   - Inputs are read-only; `state` and `conv_state` are updated in place.
@@ -51,7 +52,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 10000 /* 1.0.0 */
+#define GDN_VERSION 10100 /* 1.1.0 */
 
 #define GDN_OK 0
 #define GDN_ERR_NULL (-1)      /* a required pointer is NULL                  */
@@ -168,6 +169,56 @@ int gdn_layer_tail(const gdn_dims *dims, const gdn_tail_params *params, int32_t 
 /* Bytes of workspace gdn_layer_tail needs when no dbg buffer is given
  * (0 on invalid arguments). */
 size_t gdn_layer_tail_workspace_bytes(const gdn_dims *dims, int32_t B);
+
+/*
+ * Raw inputs of the beta/alpha parameter transforms (Red Lite dev15a,
+ * "Validation boundary": the stage before the recurrent update;
+ * "DeltaNet projection parity - real layer 0": the beta/alpha projection has
+ * 64 outputs per token, two per value head).
+ *   ba       [B][2*n_v_heads]  projection outputs: the n_v_heads beta logits,
+ *                              then the n_v_heads alpha logits
+ *   a_log    [n_v_heads]       per-head log decay rate
+ *   dt_bias  [n_v_heads]       per-head bias of the alpha logit
+ */
+typedef struct {
+    const float *ba;
+    const float *a_log;
+    const float *dt_bias;
+} gdn_gate_inputs;
+
+/*
+ * gdn_gate_transform - beta and gate from the raw inputs:
+ *   beta[b][h] = 1 / (1 + exp(-ba[b][h]))
+ *   gate[b][h] = -exp(a_log[h]) * softplus(ba[b][n_v_heads + h] + dt_bias[h]),
+ *   softplus(x) = log(1 + exp(x)).
+ * The pages name these transforms but print no formula; this is the
+ * Mamba-2 style gating of the Gated DeltaNet paper (sigmoid write strength,
+ * log-decay -exp(A_log) * softplus(alpha + dt_bias)).  gate <= 0, so the
+ * per-token decay exp(gate) lies in (0, 1].  Computed in binary32.
+ *   beta, gate [B][n_v_heads] outputs (must not overlap the inputs)
+ */
+int gdn_gate_transform(const gdn_dims *dims, int32_t B, const gdn_gate_inputs *in,
+                       float *beta, float *gate, void *stream);
+
+/*
+ * gdn_layer_tail_ba - gdn_layer_tail with beta and gate computed from the
+ * raw gate inputs as in gdn_gate_transform (the whole recurrent branch of
+ * one token from the projection outputs x, ba and z to y).  Arguments as in
+ * gdn_layer_tail; the workspace must hold gdn_layer_tail_ba_workspace_bytes()
+ * bytes, of which the unfused path uses the last 2*B*n_v_heads floats for
+ * beta and gate.  Results are bitwise equal to gdn_gate_transform followed
+ * by gdn_layer_tail.
+ */
+int gdn_layer_tail_ba(const gdn_dims *dims, const gdn_tail_params *params, int32_t B,
+                      const float *x, const float *conv_w, float *conv_state,
+                      const gdn_gate_inputs *gates, float *state,
+                      const float *z, const float *norm_w, float *y,
+                      float *dbg_qkv, float *dbg_core,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace gdn_layer_tail_ba needs when no dbg buffer is given
+ * (0 on invalid arguments). */
+size_t gdn_layer_tail_ba_workspace_bytes(const gdn_dims *dims, int32_t B);
 
 /* Message for the last non-zero return on this thread ("" if none). */
 const char *gdn_last_error(void);

@@ -69,9 +69,10 @@ class Oracle:
         L.oracle_gated_rmsnorm.argtypes = [_i32, _i32, _i32, ctypes.c_float,
                                            _f32p, _f32p, _f32p, _f32p]
         L.oracle_layer_tail.argtypes = [_i32] * 7 + [ctypes.c_float] + [_f32p] * 11
+        L.oracle_gate_transform.argtypes = [_i32, _i32] + [_f32p] * 5
         for name in ("oracle_gdn_step_M", "oracle_gdn_step_S", "oracle_gdn_step_f64",
                      "oracle_gdn_seq", "oracle_gdn_pair", "oracle_conv_silu", "oracle_l2norm_rows",
-                     "oracle_gated_rmsnorm", "oracle_layer_tail"):
+                     "oracle_gated_rmsnorm", "oracle_layer_tail", "oracle_gate_transform"):
             getattr(L, name).restype = None
         self.lib = L
 
@@ -180,6 +181,22 @@ class Oracle:
                                    _p32(beta), _p32(gate), _p32(M), _p32(z),
                                    _p32(norm_w), _p32(y), _p32(qkv), _p32(core))
         return y, qkv, core
+
+    # -- the beta/alpha parameter transforms ------------------------------
+    def gate_transform(self, ba, a_log, dt_bias):
+        """beta, gate [B][Hv] from the raw projection ba [B][2*Hv] and the
+        per-head a_log, dt_bias [Hv]."""
+        ba = np.ascontiguousarray(ba, dtype=np.float32)
+        a_log = np.ascontiguousarray(a_log, dtype=np.float32)
+        dt_bias = np.ascontiguousarray(dt_bias, dtype=np.float32)
+        B, two_hv = ba.shape
+        Hv = two_hv // 2
+        assert two_hv == 2 * Hv and a_log.shape == (Hv,) and dt_bias.shape == (Hv,)
+        beta = np.empty((B, Hv), np.float32)
+        gate = np.empty((B, Hv), np.float32)
+        self.lib.oracle_gate_transform(B, Hv, _p32(ba), _p32(a_log), _p32(dt_bias),
+                                       _p32(beta), _p32(gate))
+        return beta, gate
 
 
 _default = None

@@ -378,3 +378,34 @@ void oracle_layer_tail(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv
     free(v);
     free(o);
 }
+
+/* ---------------------------------------------------------------------
+ * [dev15a] "Validation boundary" names the beta/alpha parameter transforms
+ * as the stage before the recurrent update, and "DeltaNet projection parity -
+ * real layer 0" gives their projection 64 outputs per token, i.e. one beta
+ * and one alpha logit per value head.  The pages print no formula.  Reading
+ * taken (the Mamba-2 style gating of the Gated DeltaNet paper, Yang, Kautz
+ * and Hatamizadeh, restated): per sequence b and value head h,
+ *   beta = sigmoid(b_h) = 1 / (1 + exp(-b_h))
+ *   gate = -exp(A_log[h]) * softplus(a_h + dt_bias[h]),
+ *          softplus(x) = log(1 + exp(x)),
+ * with the projection row laid out [b_0 .. b_{Hv-1} | a_0 .. a_{Hv-1}].
+ * softplus is evaluated as x + log1p(exp(-x)) for x > 0, the same function
+ * without the overflow of exp(x).
+ */
+static float softplus(float x) { return x > 0.0f ? x + log1pf(expf(-x)) : log1pf(expf(x)); }
+
+void oracle_gate_transform(int32_t B, int32_t Hv, const float *ba, const float *a_log,
+                           const float *dt_bias, float *beta, float *gate)
+{
+    int32_t b, h;
+    for (b = 0; b < B; ++b) {
+        const float *row = ba + (size_t)b * 2 * Hv;
+        for (h = 0; h < Hv; ++h) {
+            const float bl = row[h];
+            const float al = row[Hv + h];
+            beta[(size_t)b * Hv + h] = 1.0f / (1.0f + expf(-bl));
+            gate[(size_t)b * Hv + h] = -expf(a_log[h]) * softplus(al + dt_bias[h]);
+        }
+    }
+}

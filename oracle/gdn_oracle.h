@@ -121,6 +121,14 @@ void oracle_layer_tail(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv
                        const float *z, const float *norm_w, float *y,
                        float *qkv_out, float *core_out);
 
+/* [dev15a] beta/alpha parameter transforms (the pages name them; the
+ * formula is a reading, see the definition):
+ *   beta[b][h] = sigmoid(ba[b][h]),
+ *   gate[b][h] = -exp(a_log[h]) * softplus(ba[b][Hv + h] + dt_bias[h]).
+ * ba [B][2*Hv]; a_log, dt_bias [Hv]; beta, gate [B][Hv]. */
+void oracle_gate_transform(int32_t B, int32_t Hv, const float *ba, const float *a_log,
+                           const float *dt_bias, float *beta, float *gate);
+
 #ifdef __cplusplus
 }
 #endif

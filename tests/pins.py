@@ -464,6 +464,77 @@ def pin_printed_constants(o):
     assert gi.WORKLOADS["step_b256_x36"]["layers"] == G("recurrent_layers")
 
 
+
+# ---------------------------------------------------------- gate transforms
+# dev15a names the beta/alpha parameter transforms and prints a 64-output
+# projection for them; the formula is a reading (sigmoid for beta, the
+# Mamba-2 style gate -exp(A_log) * softplus(alpha + dt_bias)).  These pins tie
+# the oracle to closed forms and identities of sigmoid and softplus, not to a
+# retyped formula.
+def _ulps(x, n):
+    return n * np.spacing(np.abs(np.float32(x))).astype(np.float64)
+
+
+def pin_gate_transform_closed_forms(o):
+    """sigmoid(ln m) = m / (1 + m), softplus(ln m) = ln(1 + m), exp(ln n) = n,
+    with a different m, n per head (head indexing and the [beta | alpha]
+    split of the projection row), plus sigmoid(0) = 1/2 exactly."""
+    Hv = G("value_heads")
+    assert 2 * Hv == G("beta_alpha_outputs"), "beta/alpha projection width"
+    h = np.arange(Hv, dtype=np.float64)
+    a_log = np.log(h + 1).astype(np.float32)                    # exp -> h + 1
+    dt_bias = (0.25 * (h % 4) - 0.5).astype(np.float32)
+    ba = np.empty((2, 2 * Hv), np.float32)
+    ba[0, :Hv] = np.log((h + 1) / 2)                            # beta -> (h+1)/(h+3)
+    ba[0, Hv:] = (np.log(h + 1) - dt_bias.astype(np.float64))  # a + dt_bias -> ln(h+1)
+    ba[1, :Hv] = 0.0                                            # beta -> 1/2 exactly
+    ba[1, Hv:] = -dt_bias                                       # softplus(0) = ln 2
+    beta, gate = o.gate_transform(ba, a_log, dt_bias)
+    want_b = (h + 1) / (h + 3)
+    # softplus(ln(h+1)) = ln(h+2); the argument is rounded to f32 on the way
+    x = ba[0, Hv:].astype(np.float32) + dt_bias                 # f32 sum, as computed
+    want_g = -(h + 1) * np.log(h + 2)
+    slack = (h + 1) * np.abs(x.astype(np.float64) - np.log(h + 1)) * ((h + 1) / (h + 2))
+    assert np.all(np.abs(beta[0] - want_b) <= _ulps(want_b, 4) + 2e-8), "sigmoid(ln m)"
+    assert np.all(np.abs(gate[0] - want_g) <= _ulps(want_g, 8) + slack), "gate closed form"
+    assert np.all(beta[1] == np.float32(0.5)), "sigmoid(0)"
+    want1 = -(h + 1) * np.log(2.0)                              # -dt_bias + dt_bias = 0 exactly
+    assert np.all(np.abs(gate[1] - want1) <= _ulps(want1, 8)), "softplus(0) = ln 2"
+
+
+def pin_gate_transform_identities(o):
+    """With A_log = 0 and dt_bias = 0: exp(gate) = 1 - beta (softplus and
+    sigmoid agree), sigmoid(x) + sigmoid(-x) = 1, softplus(x) - softplus(-x)
+    = x, max(x, 0) <= softplus(x) <= max(x, 0) + ln 2, d softplus / dx =
+    sigmoid (central difference), and finite values at |x| = 100."""
+    Hv = G("value_heads")
+    rng = np.random.default_rng(23)
+    x = (8.0 * rng.standard_normal((6, Hv))).astype(np.float32)
+    x[0, :4] = [100.0, -100.0, 0.0, 30.0]
+    z = np.zeros(Hv, np.float32)
+    rows = np.concatenate([x, -x])
+    ba = np.concatenate([rows, rows], axis=1)                   # b = a = x
+    beta, gate = o.gate_transform(ba, z, z)
+    assert np.all(np.isfinite(beta)) and np.all(np.isfinite(gate)), "finite"
+    n = len(x)
+    bp, bm, gp, gm = (beta[:n].astype(np.float64), beta[n:].astype(np.float64),
+                      gate[:n].astype(np.float64), gate[n:].astype(np.float64))
+    assert np.all(np.abs(np.exp(gp) - (1.0 - bp)) <= 3e-7), "exp(gate) = 1 - beta"
+    assert np.all(np.abs(bp + bm - 1.0) <= 3e-7), "sigmoid symmetry"
+    xd = x.astype(np.float64)
+    assert np.all(np.abs((gm - gp) - xd) <= _ulps(xd, 4) + 4e-7), "softplus(x) - softplus(-x) = x"
+    sp = -gp
+    assert np.all(sp >= np.maximum(xd, 0) - _ulps(xd, 2)) and \
+        np.all(sp <= np.maximum(xd, 0) + np.log(2.0) + 4e-7), "softplus bounds"
+    # derivative: (softplus(x + e) - softplus(x - e)) / 2e = sigmoid(x)
+    eps = 2.0 ** -6
+    xs = np.linspace(-4, 4, Hv).astype(np.float32)
+    bad = np.stack([xs + eps, xs - eps, xs]).astype(np.float32)
+    b2, g2 = o.gate_transform(np.concatenate([bad, bad], axis=1), z, z)
+    slope = (-(g2[0].astype(np.float64)) + g2[1].astype(np.float64)) / (2 * eps)
+    assert np.all(np.abs(slope - b2[2]) <= 5e-5), "d softplus/dx = sigmoid"
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 

@@ -25,6 +25,7 @@ def declared_functions():
 def test_exports_every_declared_symbol(g):
     names = declared_functions()
     assert {"gdn_step", "gdn_seq", "gdn_pair", "gdn_layer_tail", "gdn_layer_tail_workspace_bytes",
+            "gdn_gate_transform", "gdn_layer_tail_ba", "gdn_layer_tail_ba_workspace_bytes",
             "gdn_last_error", "gdn_version"} <= set(names)
     for n in names:
         assert hasattr(g.lib, n), f"{n} not exported"
@@ -162,9 +163,69 @@ def test_tail_validation(g):
     expect(g, f(dq=dq + 4), -3, "dbg_qkv")
 
 
+def test_gate_transform_validation(g):
+    d = g.Dims(HV, HK, D, D)
+    base = {"ba": BASE, "a_log": BASE + (1 << 20), "dt": BASE + (2 << 20),
+            "beta": BASE + (3 << 20), "gate": BASE + (4 << 20)}
+
+    def f(dd=d, Bv=B, null_in=False, **over):
+        a = dict(base, **over)
+        gi = g.GateInputs(a["ba"], a["a_log"], a["dt"])
+        return g.lib.gdn_gate_transform(ctypes.byref(dd), Bv, None if null_in else ctypes.byref(gi),
+                                        a["beta"], a["gate"], None)
+
+    expect(g, f(null_in=True), -1, "gate inputs")
+    expect(g, f(ba=None), -1, "ba")
+    expect(g, f(a_log=None), -1, "a_log")
+    expect(g, f(dt=None), -1, "dt_bias")
+    expect(g, f(beta=None), -1, "beta")
+    expect(g, f(gate=base["ba"] + 2), -3, "gate")
+    expect(g, f(Bv=0), -2, "B")
+    expect(g, f(dd=g.Dims(HV, HK, 64, 64)), -2, "d_k")
+    # beta over the second half of ba, gate over a_log
+    expect(g, f(beta=base["ba"] + B * HV * 4), -4, "beta")
+    expect(g, f(gate=base["a_log"]), -4, "gate")
+    expect(g, f(gate=base["beta"] + 4), -4, "beta")
+
+
+def test_tail_ba_validation(g):
+    d = g.Dims(HV, HK, D, D)
+    C = 2 * HK * D + HV * D
+    p = g.TailParams(4, 128, 1e-6)
+    base = {"x": BASE, "conv_w": BASE + (1 << 24), "cs": BASE + (2 << 24), "ba": BASE + (3 << 24),
+            "a_log": BASE + (4 << 24), "dt": BASE + (4 << 24) + 4096, "state": BASE + (5 << 24),
+            "z": BASE + (8 << 24), "nw": BASE + (9 << 24), "y": BASE + (10 << 24),
+            "ws": BASE + (11 << 24)}
+    need = g.layer_tail_ba_workspace_bytes(B)
+    assert need == B * (C + HV * D) * 4 + 2 * B * HV * 4
+    assert need == g.layer_tail_workspace_bytes(B) + 2 * B * HV * 4
+
+    def f(ws_bytes=need, null_gates=False, dq=None, dc=None, **over):
+        a = dict(base, **over)
+        gi = g.GateInputs(a["ba"], a["a_log"], a["dt"])
+        return g.lib.gdn_layer_tail_ba(
+            ctypes.byref(d), ctypes.byref(p), B, a["x"], a["conv_w"], a["cs"],
+            None if null_gates else ctypes.byref(gi), a["state"], a["z"], a["nw"], a["y"],
+            dq, dc, a["ws"], ws_bytes, None)
+
+    expect(g, f(null_gates=True), -1, "gates")
+    expect(g, f(ba=None), -1, "ba")
+    expect(g, f(dt=None), -1, "dt_bias")
+    expect(g, f(ws_bytes=need - 4), -5, "workspace")
+    # the dbg buffers replace the qkv and core parts; beta/gate still need room
+    dq, dc = BASE + (12 << 24), BASE + (13 << 24)
+    expect(g, f(ws=None, ws_bytes=0, dq=dq, dc=dc), -5, "workspace")
+    expect(g, f(ws_bytes=2 * B * HV * 4 - 4, dq=dq, dc=dc), -5, "workspace")
+    # the beta/gate part of the workspace must not overlap the inputs
+    expect(g, f(ws=base["ba"] - need + 16, ws_bytes=need), -4, "buffer")
+    expect(g, f(y=base["x"] + 64), -4, "y")
+
+
 def test_workspace_bytes_invalid(g):
     assert g.lib.gdn_layer_tail_workspace_bytes(None, 4) == 0
     assert g.lib.gdn_layer_tail_workspace_bytes(ctypes.byref(g.PAGE_DIMS), 0) == 0
+    assert g.lib.gdn_layer_tail_ba_workspace_bytes(None, 4) == 0
+    assert g.lib.gdn_layer_tail_ba_workspace_bytes(ctypes.byref(g.PAGE_DIMS), 0) == 0
 
 
 def test_binding_rejects_cpu_tensors(g):

@@ -41,6 +41,13 @@ MUTANTS = [
     ("tail_split_q_from_k", "memcpy(q + (size_t)b * nq, act + (size_t)b * C, ",
      "memcpy(q + (size_t)b * nq, act + (size_t)b * C + nq, "),
     ("tail_k_not_normalized", "oracle_l2norm_rows(B * Hk, dk, k);", ";"),
+    ("gate_tf_halves_swapped", "const float bl = row[h];", "const float bl = row[Hv + h];"),
+    ("gate_tf_sigmoid_sign", "1.0f / (1.0f + expf(-bl));", "1.0f / (1.0f + expf(bl));"),
+    ("gate_tf_gate_sign", "= -expf(a_log[h]) *", "= expf(a_log[h]) *"),
+    ("gate_tf_dt_bias_dropped", "softplus(al + dt_bias[h])", "softplus(al)"),
+    ("gate_tf_a_log_not_exponentiated", "= -expf(a_log[h]) *", "= -a_log[h] *"),
+    ("gate_tf_softplus_branch", "x + log1pf(expf(-x))", "log1pf(expf(-x))"),
+    ("gate_tf_head_index", "softplus(al + dt_bias[h])", "softplus(al + dt_bias[0])"),
 ]
 
 
