@@ -82,26 +82,27 @@ def test_gate_transform_extremes(g, orc):
     assert np.all(beta[0] == np.float32(0.5))
 
 
-def tail_inputs_ba(seed, B):
-    ti = gi.tail_inputs(seed, B)
-    gin = gi.gate_inputs(seed, B)
+def tail_inputs_ba(seed, B, Hv=HV, Hk=16):
+    ti = gi.tail_inputs(seed, B, Hv=Hv, Hk=Hk)
+    gin = gi.gate_inputs(seed, B, Hv=Hv)
     return ti, gin
 
 
-def run_tail_ba(g, ti, gin, M, force_unfused=0, use_dbg=False):
+def run_tail_ba(g, ti, gin, M, force_unfused=0, use_dbg=False, Hv=HV, Hk=16):
     import torch
     B, C = ti["x"].shape
+    dims = g.Dims(Hv, Hk, 128, 128)
     t = {n: dev(x) for n, x in ti.items()}
     gd = {n: dev(x) for n, x in gin.items()}
     Md = dev(M)
-    y = torch.empty((B, HV * 128), device="cuda")
+    y = torch.empty((B, Hv * 128), device="cuda")
     dq = torch.empty((B, C), device="cuda") if use_dbg else None
-    dc = torch.empty((B, HV, 128), device="cuda") if use_dbg else None
-    ws = torch.empty(g.layer_tail_ba_workspace_bytes(B), dtype=torch.uint8, device="cuda")
+    dc = torch.empty((B, Hv, 128), device="cuda") if use_dbg else None
+    ws = torch.empty(g.layer_tail_ba_workspace_bytes(B, dims), dtype=torch.uint8, device="cuda")
     params = g.TailParams(4, 128, 1e-6, force_unfused)
     g.layer_tail_ba(t["x"], t["conv_w"], t["conv_state"], gd["ba"], gd["a_log"], gd["dt_bias"],
                     Md, t["z"], t["norm_w"], y, dbg_qkv=dq, dbg_core=dc, workspace=ws,
-                    params=params)
+                    dims=dims, params=params)
     torch.cuda.synchronize()
     return dict(y=y.cpu().numpy(), state=Md.cpu().numpy(),
                 conv_state=t["conv_state"].cpu().numpy(),
@@ -125,11 +126,11 @@ def run_two_calls(g, ti, gin, M, force_unfused=0):
                 conv_state=t["conv_state"].cpu().numpy())
 
 
-def oracle_tail_ba(orc, ti, gin, M):
+def oracle_tail_ba(orc, ti, gin, M, Hk=16):
     beta, gate = orc.gate_transform(gin["ba"], gin["a_log"], gin["dt_bias"])
     cs = ti["conv_state"].copy()
     y, qkv, core = orc.layer_tail(ti["x"], ti["conv_w"], cs, beta, gate, M, ti["z"],
-                                  ti["norm_w"], 16, 128)
+                                  ti["norm_w"], Hk, 128)
     return dict(y=y, qkv=qkv, core=core, conv_state=cs, state=M)
 
 
@@ -169,3 +170,17 @@ def test_tail_ba_fused_equals_unfused(g):
     b = run_tail_ba(g, ti, gin, M.copy(), 1)
     for k in ("y", "state", "conv_state"):
         assert np.array_equal(a[k], b[k]), f"{k} differs"
+
+
+@pytest.mark.parametrize("force_unfused", [0, 1])
+def test_tail_ba_one_value_head_per_key_head(g, orc, force_unfused):
+    """Hv = Hk = 16 (the single-launch tail's one-value-head specialisation)."""
+    print(f"\n  gdn_layer_tail_ba Hv=Hk=16 unfused={force_unfused}", flush=True)
+    B, Hv, Hk = 4, 16, 16
+    ti, gin = tail_inputs_ba(5400, B, Hv, Hk)
+    M = gi.state(5400, 0, B, Hv=Hv)
+    got = run_tail_ba(g, ti, gin, M, force_unfused, Hv=Hv, Hk=Hk)
+    want = oracle_tail_ba(orc, ti, gin, M, Hk=Hk)
+    ref.assert_close("y", got["y"], want["y"], 1e-5)
+    ref.assert_close("state", got["state"], want["state"], 1e-6)
+    assert np.array_equal(got["conv_state"], want["conv_state"]), "conv cache not bitwise"
