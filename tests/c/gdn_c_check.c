@@ -7,6 +7,9 @@
  *   3. full forget (gate = -1e4):   M' = beta v k^T
  *   4. gdn_seq over 3 tokens == 3 gdn_step calls, bit for bit
  *   5. argument errors: GDN_ERR_ALIGN / GDN_ERR_ALIAS before any work
+ *   6. gdn_gate_transform: sigmoid(0) = 1/2 exactly, sigmoid(ln 3) = 3/4,
+ *      gate = -ln 2 at a zero softplus argument, exp(gate) = 1 - beta when
+ *      a_log = dt_bias = 0 and the alpha logit equals the beta logit
  * Exits 0 on success; prints the first failure otherwise.
  */
 #include <hip/hip_runtime_api.h>
@@ -183,6 +186,43 @@ int main(void) {
         return fail("misaligned q not rejected", 0);
     if (gdn_step(&dims, B, d.q, d.k, d.v, d.beta, d.gate, d.M, d.M, NULL) != GDN_ERR_ALIAS)
         return fail("out aliasing state not rejected", 0);
+
+    /* 6. beta/alpha parameter transforms */
+    {
+        float ba[B * 2 * HV], al[HV], dt[HV], hb[B * HV], hg[B * HV];
+        for (int h = 0; h < HV; ++h) {
+            al[h] = 0.0f;
+            dt[h] = 0.0f;
+            ba[h] = (h % 2) ? 0.0f : (float)log(3.0);       /* sequence 0: beta logits */
+            ba[HV + h] = 0.0f;                              /* sequence 0: alpha logits */
+            ba[2 * HV + h] = 0.25f * (float)(h - 16);       /* sequence 1: b = a = x */
+            ba[3 * HV + h] = 0.25f * (float)(h - 16);
+        }
+        float *dba, *dal, *ddt, *db, *dg;
+        HIP_OK(hipMalloc((void **)&dba, sizeof ba));
+        HIP_OK(hipMalloc((void **)&dal, sizeof al));
+        HIP_OK(hipMalloc((void **)&ddt, sizeof dt));
+        HIP_OK(hipMalloc((void **)&db, sizeof hb));
+        HIP_OK(hipMalloc((void **)&dg, sizeof hg));
+        HIP_OK(hipMemcpy(dba, ba, sizeof ba, hipMemcpyHostToDevice));
+        HIP_OK(hipMemcpy(dal, al, sizeof al, hipMemcpyHostToDevice));
+        HIP_OK(hipMemcpy(ddt, dt, sizeof dt, hipMemcpyHostToDevice));
+        const gdn_gate_inputs gin = {dba, dal, ddt};
+        if (gdn_gate_transform(&dims, B, &gin, db, dg, NULL) != GDN_OK) return fail(gdn_last_error(), 0);
+        HIP_OK(hipMemcpy(hb, db, sizeof hb, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(hg, dg, sizeof hg, hipMemcpyDeviceToHost));
+        for (int h = 0; h < HV; ++h) {
+            const double want_b = (h % 2) ? 0.5 : 0.75;
+            if ((h % 2) && hb[h] != 0.5f) return fail("sigmoid(0) != 1/2", fabs(hb[h] - 0.5));
+            if (fabs(hb[h] - want_b) > 3e-7) return fail("sigmoid(ln 3) != 3/4", fabs(hb[h] - want_b));
+            if (fabs(hg[h] + log(2.0)) > 3e-7) return fail("softplus(0) != ln 2", fabs(hg[h] + log(2.0)));
+            const double e = exp((double)hg[HV + h]) - (1.0 - (double)hb[HV + h]);
+            if (fabs(e) > 3e-7) return fail("exp(gate) != 1 - beta", fabs(e));
+        }
+        if (gdn_gate_transform(&dims, B, &gin, db, dba, NULL) != GDN_ERR_ALIAS)
+            return fail("gate aliasing ba not rejected", 0);
+        hipFree(dba); hipFree(dal); hipFree(ddt); hipFree(db); hipFree(dg);
+    }
 
     HIP_OK(hipDeviceSynchronize());
     printf("C ABI check ok (version %d)\n", gdn_version());

@@ -1,7 +1,7 @@
 """GPU: the library driven from plain C through its ABI only (no Python in
 the tested path, as the Red Lite pages test their native code): closed-form
-checks of gdn_step, gdn_seq == repeated gdn_step bitwise, and argument
-errors.  The program is tests/c/gdn_c_check.c, built by __graft_entry__.build()."""
+checks of gdn_step and gdn_gate_transform, gdn_seq == repeated gdn_step
+bitwise, and argument errors.  The program is tests/c/gdn_c_check.c, built by __graft_entry__.build()."""
 import os
 import subprocess
 
