@@ -197,7 +197,7 @@ def host_info():
 
 
 def cpu_baseline(seconds):
-    """The oracle as it is, on the host cores, over config-2 layers (B=256)
+    """The oracle as it is, on the host cores, over layers of the B=256 x 36-layer decode
     stepped round-robin until `seconds` have passed."""
     import oracle
     from concurrent.futures import ThreadPoolExecutor

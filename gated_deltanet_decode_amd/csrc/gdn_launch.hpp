@@ -1,5 +1,6 @@
 // gdn_launch.hpp - internal interface between the C-ABI layer (gdn_api.cpp)
-// and the gfx950 kernels (gdn_kernels.hip).  Not installed, not part of the ABI.
+// and the gfx950 kernels (gdn_step.hip, gdn_seq.hip, gdn_tail.hip).  Not
+// installed, not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime_api.h>

@@ -79,12 +79,12 @@ def test_pair_reject_then_accept(g, orc):
     Md = dev(M)
     Mn = torch.empty_like(Md)
     out = torch.empty((B, 2, 32, 128), device="cuda")
-    # round 1: draft rejected -> only position 1 counts
+    # first verification: draft rejected -> only position 1 counts
     s1 = gi.step_inputs(5200, 1, B, T=2)
     t = {n: dev(x) for n, x in s1.items()}
     g.pair(t["q"], t["k"], t["v"], t["beta"], t["gate"], Md, Mn, out)
     orc.step_M(*(np.ascontiguousarray(s1[n][:, 0]) for n in ("q", "k", "v", "beta", "gate")), M)
-    # round 2: draft accepted -> adopt the tentative state
+    # second verification: draft accepted -> adopt the tentative state
     s2 = gi.step_inputs(5200, 2, B, T=2)
     t = {n: dev(x) for n, x in s2.items()}
     g.pair(t["q"], t["k"], t["v"], t["beta"], t["gate"], Md, Mn, out)
