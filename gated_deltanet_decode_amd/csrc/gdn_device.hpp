@@ -206,36 +206,5 @@ __device__ __forceinline__ void pass(RowSlice &r, float d, const VecSlice &k, co
     }
 }
 
-// --------------------------------------------------------- tail helpers
-// Block-wide sum for a block of NW waves; every thread gets the same bits.
-template <int NW>
-__device__ __forceinline__ float block_sum(float x, float *scratch) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = x;
-    __syncthreads();
-    float s = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) s += scratch[w];
-    return s;
-}
-
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
-
-// beta/alpha parameter transforms (Red Lite dev15a, "Validation boundary":
-// named as the stage before the update; the formula is the reading of the
-// Gated DeltaNet paper's Mamba-2 style gating):
-//   beta = 1 / (1 + exp(-b)),  gate = -exp(a_log) * softplus(a + dt_bias),
-// softplus(x) = log(1 + exp(x)), evaluated as x + log1p(exp(-x)) for x > 0.
-__device__ __forceinline__ float softplus(float x) {
-    return x > 0.0f ? x + log1pf(expf(-x)) : log1pf(expf(x));
-}
-
-__device__ __forceinline__ void beta_gate(float b, float a, float a_log, float dt_bias,
-                                          float &beta, float &gate) {
-    beta = 1.0f / (1.0f + expf(-b));
-    gate = -expf(a_log) * softplus(a + dt_bias);
-}
-
 }  // namespace
 }  // namespace gdn

@@ -82,6 +82,28 @@ def test_graph_capture_step_seq_pair_tail(g):
             {"M": M, "cs": ti["conv_state"]}, {"y": torch.empty((B, 4096), device="cuda")})
 
 
+def test_graph_capture_gate_transform_and_tail_ba(g):
+    import torch
+    print("\n  graph capture: gate transform, tail from raw gates", flush=True)
+    B = 4
+    gin = {n: dev(x) for n, x in gi.gate_inputs(6004, B).items()}
+    _replay_matches_eager(
+        lambda st, o: g.gate_transform(gin["ba"], gin["a_log"], gin["dt_bias"], o["beta"],
+                                       o["gate"]),
+        {}, {"beta": torch.empty((B, 32), device="cuda"),
+             "gate": torch.empty((B, 32), device="cuda")})
+    ti = {n: dev(x) for n, x in gi.tail_inputs(6004, B).items()}
+    M = dev(gi.state(6004, 0, B))
+    ws = torch.empty(g.layer_tail_ba_workspace_bytes(B), dtype=torch.uint8, device="cuda")
+    for fu in (0, 1):
+        p = g.TailParams(4, 128, 1e-6, fu)
+        _replay_matches_eager(
+            lambda st, o: g.layer_tail_ba(ti["x"], ti["conv_w"], st["cs"], gin["ba"],
+                                          gin["a_log"], gin["dt_bias"], st["M"], ti["z"],
+                                          ti["norm_w"], o["y"], workspace=ws, params=p),
+            {"M": M, "cs": ti["conv_state"]}, {"y": torch.empty((B, 4096), device="cuda")})
+
+
 def test_concurrent_host_threads(g):
     """Four host threads, each on its own stream and buffers, call gdn_step
     and gdn_seq repeatedly at the same time."""
