@@ -99,6 +99,31 @@ def measured_traffic():
     return t.get("traffic_bytes_per_launch")
 
 
+def inplace_probe(torch, stream, buf, reps=5):
+    """Rate of an in-place read-modify-write of `buf` with the step kernel's
+    memory pattern and no arithmetic (read + write bytes / s); the data is
+    left unchanged."""
+    import ctypes
+    from gated_deltanet_decode_amd._build import PROBE_LIBRARY
+    lib = ctypes.CDLL(PROBE_LIBRARY)
+    lib.gdn_probe_inplace.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint,
+                                      ctypes.c_void_p]
+    nbytes = buf.numel() * buf.element_size()
+
+    def once():
+        assert lib.gdn_probe_inplace(buf.data_ptr(), nbytes, 0, stream.cuda_stream) == 0
+    once()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(reps):
+        once()
+    e.record(stream)
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    return 2 * nbytes / (ms / 1e3) / 1e9
+
+
 def copy_probe(torch, stream, nbytes=1 << 30, reps=5):
     """Bandwidth of a plain device-to-device copy (read + write bytes / s)."""
     import ctypes
@@ -397,6 +422,8 @@ def main():
     log(f"[bench] copy probe: {copy_gbps:.0f} GB/s")
     w = setup_step_b256_x36(torch, g)
     L, B = w["L"], w["B"]
+    inplace_gbps = inplace_probe(torch, stream, w["states"][0])
+    log(f"[bench] in-place probe (the step's access pattern, no arithmetic): {inplace_gbps:.0f} GB/s")
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
         run_step36(g, w, stream)
@@ -456,6 +483,8 @@ def main():
                      "bytes_per_launch": bytes_per_launch,
                      "copy_probe_GBps": copy_gbps,
                      "frac_of_copy_probe": achieved / copy_gbps,
+                     "inplace_probe_GBps": inplace_gbps,
+                     "frac_of_inplace_probe": achieved / inplace_gbps,
                      "avg_launch_us": avg_launch_ms * 1e3,
                      "launches_timed": len(launch_ms)},
     }

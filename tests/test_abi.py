@@ -251,3 +251,16 @@ def test_product_never_imports_the_oracle():
                     and "gdn_oracle" not in txt, f"{fn} references the oracle"
     hdr = open(os.path.join(ROOT, "include", "gdn.h")).read()
     assert "oracle" not in hdr
+
+
+def test_probe_library_rejects_bad_arguments():
+    """The measurement probes validate before launching anything."""
+    from gated_deltanet_decode_amd._build import PROBE_LIBRARY
+    lib = ctypes.CDLL(PROBE_LIBRARY)
+    lib.gdn_probe_inplace.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint, ctypes.c_void_p]
+    lib.gdn_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert lib.gdn_probe_inplace(None, 4096, 0, None) == -1
+    assert lib.gdn_probe_inplace(BASE, 4000, 0, None) == -1
+    assert lib.gdn_probe_inplace(BASE + 8, 4096, 0, None) == -1
+    assert lib.gdn_probe_copy(None, BASE, 16, None) == -1
+    assert lib.gdn_probe_copy(BASE, BASE + (1 << 20), 20, None) == -1
