@@ -263,6 +263,7 @@ def cpu_baseline(seconds):
         o.step_M(si["q"], si["k"], si["v"], si["beta"], si["gate"], M)
         done1 += 1
     el1 = time.perf_counter() - t1
+    other = oracle_other_workloads(o, threads)
     return {"value": updates / el, "unit": "state-updates/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} layer-steps of the B=256 x 36-layer decode (32 heads; layers 0-"
                       f"{n_layers - 1} stepped round-robin), oracle_gdn_step_M split over "
@@ -271,7 +272,87 @@ def cpu_baseline(seconds):
             "single_thread_value": done1 * 32 * HV / el1,
             "single_thread_sample": f"{done1} steps of 32 sequences x 32 heads, one thread, "
                                     f"{el1:.1f} s",
+            "other_workloads": other,
             "host": host_info()}
+
+
+def _timed(fn, seconds):
+    """Calls fn() until `seconds` have passed (at least once); returns (calls, s)."""
+    n, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return n, el
+
+
+def oracle_other_workloads(o, threads, seconds=1.0):
+    """The oracle on the secondary workloads (bounded samples, ~1 s each),
+    split over host threads by sequence where there is more than one."""
+    from concurrent.futures import ThreadPoolExecutor
+    res = {}
+    ex = ThreadPoolExecutor(threads)
+
+    def split(B, fn):
+        bounds = np.linspace(0, B, min(threads, B) + 1).astype(int)
+        list(ex.map(lambda i: fn(bounds[i], bounds[i + 1]), range(len(bounds) - 1)))
+
+    # step_b1: one call, one thread
+    si = gi.step_inputs(1000, 0, 1)
+    M = gi.state(1000, 0, 1)
+    n, el = _timed(lambda: o.step_M(si["q"], si["k"], si["v"], si["beta"], si["gate"], M), seconds)
+    res["step_b1"] = {"us_per_call": el / n * 1e6, "state_updates_per_s": n * HV / el, "threads": 1}
+
+    # step_b64_x100: B = 64 calls
+    si = gi.step_inputs(1001, 0, 64)
+    M = gi.state(1001, 0, 64)
+
+    def b64():
+        def part(a, b):
+            s_ = {k: np.ascontiguousarray(x[a:b]) for k, x in si.items()}
+            m = np.ascontiguousarray(M[a:b])
+            o.step_M(s_["q"], s_["k"], s_["v"], s_["beta"], s_["gate"], m)
+            M[a:b] = m
+        split(64, part)
+    n, el = _timed(b64, seconds)
+    res["step_b64_x100"] = {"ms_per_100_calls": el / n * 100 * 1e3,
+                            "state_updates_per_s": n * 64 * HV / el, "threads": min(threads, 64)}
+
+    # seq_b8_t4096: a 64-token sample of the 8 sequences, one thread per sequence
+    T = 64
+    ss = gi.step_inputs(1003, 0, 8, T=T)
+    Ms = np.zeros((8, HV, D, D), np.float32)
+
+    def seq():
+        def part(a, b):
+            s_ = {k: np.ascontiguousarray(x[a:b]) for k, x in ss.items()}
+            m = np.ascontiguousarray(Ms[a:b])
+            o.seq(s_["q"], s_["k"], s_["v"], s_["beta"], s_["gate"], m)
+        split(8, part)
+    n, el = _timed(seq, seconds)
+    rate = n * 8 * T * HV / el
+    res["seq_b8_t4096"] = {"state_updates_per_s": rate, "threads": min(threads, 8),
+                           "ms_full_run_estimate": 8 * 4096 * HV / rate * 1e3,
+                           "sample": f"T={T} of the 4096 tokens"}
+
+    # tail_b32
+    ti = gi.tail_inputs(1004, 32)
+    Mt = gi.state(1004, 0, 32)
+
+    def tail():
+        def part(a, b):
+            t_ = {k: (np.ascontiguousarray(x[a:b]) if k not in ("conv_w", "norm_w") else x)
+                  for k, x in ti.items()}
+            m = np.ascontiguousarray(Mt[a:b])
+            o.layer_tail(t_["x"], t_["conv_w"], t_["conv_state"], t_["beta"], t_["gate"], m,
+                         t_["z"], t_["norm_w"], HK, D)
+        split(32, part)
+    n, el = _timed(tail, seconds)
+    res["tail_b32"] = {"us_per_call": el / n * 1e6, "state_updates_per_s": n * 32 * HV / el,
+                       "threads": min(threads, 32)}
+    ex.shutdown()
+    return res
 
 
 def extra_measurements(torch, g, stream, only=None):
