@@ -68,10 +68,11 @@ int check_dims(const gdn_dims *d) {
 }
 
 // Heads of one call map to workgroups along grid x, and the persistent
-// kernels count 16 row tiles per head in a 32-bit index.
+// kernels count 16 row tiles per head in a 32-bit index that may run up to
+// one grid stride (at most 65536 tiles) past the last tile.
 int check_batch(const gdn_dims *d, int64_t B, const char *what) {
     if (B < 1) return fail(GDN_ERR_SHAPE, "%s must be >= 1 (got %lld)", what, (long long)B);
-    const int64_t limit = INT32_MAX / 16;
+    const int64_t limit = (static_cast<int64_t>(INT32_MAX) - 65536) / 16;   // 134213631
     if (B * d->n_v_heads > limit)
         return fail(GDN_ERR_SHAPE, "B * n_v_heads = %lld exceeds %lld",
                     (long long)(B * d->n_v_heads), (long long)limit);

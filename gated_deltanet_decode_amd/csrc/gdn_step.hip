@@ -185,9 +185,15 @@ static int device_cus() {
     return n;
 }
 
+// The walks' 32-bit tile index may run one stride (grid x kStepWaves) past
+// the last tile; the C ABI leaves 65536 of headroom below INT32_MAX, so the
+// grid is capped at 8192 workgroups.
+constexpr int64_t kMaxGrid = 65536 / kStepWaves;
+
 hipError_t launch_step(const StepArgs &a, hipStream_t s) {
     const int64_t tiles = static_cast<int64_t>(a.B) * a.Hv * kTilesPerHead;
-    const int64_t full = device_cus() * static_cast<int64_t>(GDN_STEP_WGS_PER_CU);
+    int64_t full = device_cus() * static_cast<int64_t>(GDN_STEP_WGS_PER_CU);
+    if (full > kMaxGrid) full = kMaxGrid;
     const int64_t need = (tiles + kStepWaves - 1) / kStepWaves;
     const int grid = static_cast<int>(need < full ? need : full);
     if (tiles > static_cast<int64_t>(grid) * kStepWaves)   // several passes per wave
@@ -199,7 +205,8 @@ hipError_t launch_step(const StepArgs &a, hipStream_t s) {
 
 hipError_t launch_pair(const PairArgs &a, hipStream_t s) {
     const int64_t tiles = static_cast<int64_t>(a.B) * a.Hv * kTilesPerHead;
-    const int64_t full = device_cus() * static_cast<int64_t>(GDN_STEP_WGS_PER_CU);
+    int64_t full = device_cus() * static_cast<int64_t>(GDN_STEP_WGS_PER_CU);
+    if (full > kMaxGrid) full = kMaxGrid;
     const int64_t need = (tiles + kStepWaves - 1) / kStepWaves;
     const int grid = static_cast<int>(need < full ? need : full);
     k_pair<<<dim3(grid), dim3(kStepWaves * 64), 0, s>>>(a, static_cast<int>(tiles));

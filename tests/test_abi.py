@@ -82,6 +82,9 @@ def test_step_validation(g):
     expect(g, call_step(g, g.Dims(32, 16, 128, 64), B, a), -2, "d_v")
     expect(g, call_step(g, g.Dims(0, 16, 128, 128), B, a), -2, "head")
     expect(g, call_step(g, d, (1 << 31) // 32 + 1, a), -2, "exceeds")
+    # one past the largest accepted B * n_v_heads (134213631, which leaves one
+    # grid stride of headroom below INT32_MAX for the 32-bit tile index)
+    expect(g, call_step(g, d, 134213631 // 32 + 1, a), -2, "exceeds")
     for n in ("q", "k", "v", "state", "out"):
         expect(g, call_step(g, d, B, dict(a, **{n: a[n] + 8})), -3, n)
     for n in ("beta", "gate"):
