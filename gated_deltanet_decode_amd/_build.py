@@ -10,7 +10,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIBRARY = os.path.join(CSRC, "libgdn.so")
 SOURCES = [os.path.join(CSRC, f) for f in
            ("gdn_api.cpp", "gdn_step.hip", "gdn_seq.hip", "gdn_tail.hip")]
-# Measurement aid (a copy kernel of known size), built as its own library.
+# Measurement aids (a copy of known size and an in-place read-modify-write with
+# the step kernel's access pattern), built as their own library.
 PROBE_LIBRARY = os.path.join(CSRC, "libgdn_probe.so")
 PROBE_SOURCES = [os.path.join(CSRC, "hbm_probe.hip")]
 ARCH = "gfx950"

@@ -13,6 +13,25 @@ if TESTS not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+    # A CPU-only session ("-m 'not gpu'") on a fresh checkout builds what the
+    # CPU tests load (hipcc cross-compiles for gfx950 without a GPU).  GPU
+    # sessions never build: they run what was built beforehand and fail
+    # loudly if it is missing.
+    if (config.option.markexpr or "").replace(" ", "") == "notgpu":
+        import importlib.util
+        # load the build script by path: importing the package itself needs
+        # the library it is about to build
+        spec = importlib.util.spec_from_file_location(
+            "_gdn_build", os.path.join(ROOT, "gated_deltanet_decode_amd", "_build.py"))
+        _build = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(_build)
+        if not (os.path.exists(_build.LIBRARY) and os.path.exists(_build.PROBE_LIBRARY)):
+            _build.build()
+        if not os.path.exists(_build.C_CHECK_BINARY):
+            _build.build_c_check()
+        import oracle
+        if not os.path.exists(oracle.LIBRARY):
+            oracle.build()
 
 
 @pytest.fixture(scope="session")
