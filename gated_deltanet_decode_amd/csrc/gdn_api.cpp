@@ -180,7 +180,26 @@ int gdn_seq(const gdn_dims *dims, int32_t B, int32_t T, const float *q, const fl
     a.Hv = dims->n_v_heads;
     a.Hk = dims->n_k_heads;
     (void)hipGetLastError();
-    return hip_status(gdn::launch_seq(a, static_cast<hipStream_t>(stream)), "gdn_seq launch");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T == 1) {
+        // one token is gdn_step (same per-row arithmetic, same bits): the
+        // streaming kernel moves the state faster than the multi-token one
+        gdn::StepArgs sa{};
+        sa.q = q;
+        sa.k = k;
+        sa.v = v;
+        sa.beta = beta;
+        sa.gate = gate;
+        sa.state = state;
+        sa.out = out;
+        sa.qk_bstride = static_cast<int64_t>(dims->n_k_heads) * dims->d_k;
+        sa.v_bstride = static_cast<int64_t>(dims->n_v_heads) * dims->d_v;
+        sa.B = B;
+        sa.Hv = dims->n_v_heads;
+        sa.Hk = dims->n_k_heads;
+        return hip_status(gdn::launch_step(sa, s), "gdn_seq launch");
+    }
+    return hip_status(gdn::launch_seq(a, s), "gdn_seq launch");
 }
 
 int gdn_pair(const gdn_dims *dims, int32_t B, const float *q, const float *k, const float *v,

@@ -11,10 +11,10 @@ namespace {
 // 64 KiB head state lives in VGPRs (32 floats per lane) for all T tokens and
 // is read and written once per call.  The per-token inputs (k, q, v,
 // exp(gate), beta: 1.5 KiB per token) are staged through LDS in chunks of
-// kChunk = 32 tokens, double-buffered (97 KiB of LDS; gfx950 allows 160 KiB
-// per workgroup): the global loads of chunk c+1 are issued before chunk c is
-// computed and written to LDS after it, so their latency hides behind 32
-// tokens of arithmetic.  Outputs overwrite the consumed v entries in LDS
+// CH tokens (8, 16 or 32 by sequence length), double-buffered (97 KiB of LDS
+// for CH = 32; gfx950 allows 160 KiB per workgroup): the global loads of
+// chunk c+1 are issued before chunk c is computed and written to LDS after
+// it, so their latency hides behind CH tokens of arithmetic.  Outputs overwrite the consumed v entries in LDS
 // (row j's v is read only by row j's lanes, before its output exists) and are
 // flushed to HBM with coalesced 16-byte stores once per chunk.  Two barriers
 // per chunk; none per token.
@@ -26,13 +26,9 @@ namespace {
 // address is an immediate offset and no loop bookkeeping runs per token.
 // The kernel is VALU-issue bound (measured: VALU busy ~97 %), so every
 // instruction per token counts.
-#ifndef GDN_SEQ_CHUNK
-#define GDN_SEQ_CHUNK 32
-#endif
 #ifndef GDN_SEQ_TILES_PER_WAVE
 #define GDN_SEQ_TILES_PER_WAVE 2
 #endif
-constexpr int kChunk = GDN_SEQ_CHUNK;
 constexpr int kSeqTilesPerWave = GDN_SEQ_TILES_PER_WAVE;
 constexpr int kSeqWaves = kTilesPerHead / kSeqTilesPerWave;   // 8
 constexpr int kSeqThreads = kSeqWaves * 64;                   // 512
@@ -49,26 +45,33 @@ static_assert(sizeof(TokenLds) % 16 == 0, "float4 aligned token slots");
 
 // float4 loads per token: k (32) + q (32) + v (32)
 constexpr int kTokF4 = 3 * D / 4;
-constexpr int kChunkF4 = kChunk * kTokF4;                     // 3072
-constexpr int kFetchPer = (kChunkF4 + kSeqThreads - 1) / kSeqThreads;   // 6
-constexpr int kFlushPer = (kChunk * D / 4 + kSeqThreads - 1) / kSeqThreads; // 2
-static_assert(2 * kChunk <= kSeqThreads, "one thread per gate and per beta");
 
-struct ChunkRegs {
-    f4 f[kFetchPer];
-    float s;   // gate or beta of one token (threads 0 .. 2*kChunk-1)
+// Sizes of a chunk of CH tokens (CH = 32: 3072 float4, 6 per thread).
+template <int CH>
+struct Chunk {
+    static constexpr int kF4 = CH * kTokF4;
+    static constexpr int kFetchPer = (kF4 + kSeqThreads - 1) / kSeqThreads;
+    static constexpr int kFlushPer = (CH * D / 4 + kSeqThreads - 1) / kSeqThreads;
+    static_assert(2 * CH <= kSeqThreads, "one thread per gate and per beta");
 };
 
-__device__ __forceinline__ void seq_fetch(ChunkRegs &cr, const SeqArgs &a, int64_t b, int h,
+template <int CH>
+struct ChunkRegs {
+    f4 f[Chunk<CH>::kFetchPer];
+    float s;   // gate or beta of one token (threads 0 .. 2*CH-1)
+};
+
+template <int CH>
+__device__ __forceinline__ void seq_fetch(ChunkRegs<CH> &cr, const SeqArgs &a, int64_t b, int h,
                                           int kh, int t0, int tid) {
 #pragma unroll
-    for (int j = 0; j < kFetchPer; ++j) {
+    for (int j = 0; j < Chunk<CH>::kFetchPer; ++j) {
         const int e = tid + j * kSeqThreads;
         const int tt = e / kTokF4;
         const int w = e - tt * kTokF4;
         const int t = t0 + tt;
         f4 val = {0.f, 0.f, 0.f, 0.f};
-        if (e < kChunkF4 && t < a.T) {
+        if (e < Chunk<CH>::kF4 && t < a.T) {
             const int64_t bt = b * a.T + t;
             const float *src;
             if (w < 32)
@@ -82,21 +85,22 @@ __device__ __forceinline__ void seq_fetch(ChunkRegs &cr, const SeqArgs &a, int64
         cr.f[j] = val;
     }
     cr.s = 0.0f;
-    if (tid < 2 * kChunk) {
-        const int tt = tid < kChunk ? tid : tid - kChunk;
+    if (tid < 2 * CH) {
+        const int tt = tid < CH ? tid : tid - CH;
         const int t = t0 + tt;
         if (t < a.T) {
             const int64_t idx = (b * a.T + t) * a.Hv + h;
-            cr.s = tid < kChunk ? a.gate[idx] : a.beta[idx];
+            cr.s = tid < CH ? a.gate[idx] : a.beta[idx];
         }
     }
 }
 
-__device__ __forceinline__ void seq_stage(TokenLds *buf, const ChunkRegs &cr, int tid) {
+template <int CH>
+__device__ __forceinline__ void seq_stage(TokenLds *buf, const ChunkRegs<CH> &cr, int tid) {
 #pragma unroll
-    for (int j = 0; j < kFetchPer; ++j) {
+    for (int j = 0; j < Chunk<CH>::kFetchPer; ++j) {
         const int e = tid + j * kSeqThreads;
-        if (e >= kChunkF4) break;
+        if (e >= Chunk<CH>::kF4) break;
         const int tt = e / kTokF4;
         const int w = e - tt * kTokF4;
         float *dst = w < 32 ? buf[tt].k + 4 * w
@@ -104,10 +108,10 @@ __device__ __forceinline__ void seq_stage(TokenLds *buf, const ChunkRegs &cr, in
                             : buf[tt].v + 4 * (w - 64);
         *reinterpret_cast<f4 *>(dst) = cr.f[j];
     }
-    if (tid < kChunk)
+    if (tid < CH)
         buf[tid].e = expf(cr.s);          // the token's decay factor, computed once
-    else if (tid < 2 * kChunk)
-        buf[tid - kChunk].beta = cr.s;
+    else if (tid < 2 * CH)
+        buf[tid - CH].beta = cr.s;
 }
 
 // Token tt of a chunk: steps 3-5 of tt and, when `next`, steps 1-2 of tt+1
@@ -140,9 +144,11 @@ __device__ __forceinline__ void seq_token(TokenLds *buf, int tt, bool next, cons
     for (int t = 0; t < TPW; ++t) tok.v[rows[t]] = group_sum(o[t]) * kInvSqrtD;
 }
 
+// CH: tokens per LDS chunk; NT: nontemporal state load and store.
+template <int CH, bool NT>
 __global__ __launch_bounds__(kSeqThreads) void k_seq(SeqArgs a) {
     constexpr int TPW = kSeqTilesPerWave;
-    __shared__ TokenLds lds[2][kChunk];
+    __shared__ TokenLds lds[2][CH];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -161,22 +167,22 @@ __global__ __launch_bounds__(kSeqThreads) void k_seq(SeqArgs a) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
         rows[t] = (wave * TPW + t) * kRowsPerTile + grp;
-        load_row<false>(r[t], M + rows[t] * D, c);
+        load_row<NT>(r[t], M + rows[t] * D, c);
     }
 
-    ChunkRegs cr;
+    ChunkRegs<CH> cr;
     seq_fetch(cr, a, b, h, kh, 0, tid);
     seq_stage(lds[0], cr, tid);
     __syncthreads();
 
-    const int n_chunks = (a.T + kChunk - 1) / kChunk;
+    const int n_chunks = (a.T + CH - 1) / CH;
     for (int ch = 0; ch < n_chunks; ++ch) {
         const bool more = ch + 1 < n_chunks;
-        if (more) seq_fetch(cr, a, b, h, kh, (ch + 1) * kChunk, tid);
+        if (more) seq_fetch(cr, a, b, h, kh, (ch + 1) * CH, tid);
 
         TokenLds *buf = lds[ch & 1];
-        const int t0 = ch * kChunk;
-        const int nt = min(kChunk, a.T - t0);
+        const int t0 = ch * CH;
+        const int nt = min(CH, a.T - t0);
 
         // steps 1-2 of the chunk's first token
         VecSlice kv;
@@ -187,17 +193,17 @@ __global__ __launch_bounds__(kSeqThreads) void k_seq(SeqArgs a) {
 #pragma unroll
             for (int t = 0; t < TPW; ++t) p[t] = head_part(r[t], kv, e0);
         }
-        if (nt == kChunk) {
+        if (nt == CH) {
             // full chunk: unrolled, so every LDS address is an immediate offset
 #pragma unroll
-            for (int tt = 0; tt < kChunk; ++tt) seq_token(buf, tt, tt + 1 < kChunk, rows, r, kv, p, c);
+            for (int tt = 0; tt < CH; ++tt) seq_token(buf, tt, tt + 1 < CH, rows, r, kv, p, c);
         } else {
             for (int tt = 0; tt < nt; ++tt) seq_token(buf, tt, tt + 1 < nt, rows, r, kv, p, c);
         }
         __syncthreads();                 // outputs of chunk ch complete in LDS
 
 #pragma unroll
-        for (int j = 0; j < kFlushPer; ++j) {   // flush: float4s of the outputs
+        for (int j = 0; j < Chunk<CH>::kFlushPer; ++j) {   // flush: float4s of the outputs
             const int e = tid + j * kSeqThreads;
             const int tt = e / (D / 4);
             const int col = (e % (D / 4)) * 4;
@@ -210,14 +216,25 @@ __global__ __launch_bounds__(kSeqThreads) void k_seq(SeqArgs a) {
         __syncthreads();                 // chunk ch+1 staged; chunk ch flushed
     }
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) store_row<false>(M + rows[t] * D, r[t], c);
+    for (int t = 0; t < TPW; ++t) store_row<NT>(M + rows[t] * D, r[t], c);
 }
 
 }  // namespace
 
+// Chunk size and state access by sequence length (measured on MI355X):
+// long sequences stage 32 tokens per chunk and keep the plain state access;
+// short ones are dominated by the state transfer, which the nontemporal hint
+// speeds up by up to ~15 %, and by the last, partial chunk, which a smaller
+// chunk (fully unrolled more often) shortens.
 hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
     const int64_t heads = static_cast<int64_t>(a.B) * a.Hv;
-    k_seq<<<dim3(static_cast<unsigned>(heads)), dim3(kSeqThreads), 0, s>>>(a);
+    const dim3 grid(static_cast<unsigned>(heads)), block(kSeqThreads);
+    if (a.T < 16)
+        k_seq<8, true><<<grid, block, 0, s>>>(a);
+    else if (a.T <= 32)
+        k_seq<16, true><<<grid, block, 0, s>>>(a);
+    else
+        k_seq<32, false><<<grid, block, 0, s>>>(a);
     return hipGetLastError();
 }
 

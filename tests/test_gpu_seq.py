@@ -37,7 +37,10 @@ def token(si, t):
     return {n: np.ascontiguousarray(x[:, t]) for n, x in si.items()}
 
 
-@pytest.mark.parametrize("B,T,Hv,Hk", [(1, 1, 32, 16), (2, 5, 32, 16), (1, 17, 32, 16),
+# T covers every route: 1 (the single-step kernel), < 16 (8-token chunks,
+# full and partial), 16..32 (16-token chunks) and longer (32-token chunks).
+@pytest.mark.parametrize("B,T,Hv,Hk", [(1, 1, 32, 16), (2, 5, 32, 16), (2, 8, 32, 16),
+                                       (1, 17, 32, 16), (1, 24, 32, 16), (2, 32, 32, 16),
                                        (3, 33, 4, 2), (2, 16, 1, 1), (1, 48, 64, 16)])
 def test_seq_matches_oracle(g, orc, B, T, Hv, Hk):
     print(f"\n  gdn_seq B={B} T={T} Hv={Hv} Hk={Hk}", flush=True)
@@ -52,12 +55,13 @@ def test_seq_matches_oracle(g, orc, B, T, Hv, Hk):
     ref.assert_close("out", og, want, 1e-5)
 
 
-def test_seq_is_bitwise_repeated_step(g):
+@pytest.mark.parametrize("T", [2, 8, 15, 24, 32, 37])
+def test_seq_is_bitwise_repeated_step(g, T):
     """T tokens in one gdn_seq == T gdn_step calls, bit for bit (both paths
-    share the per-row arithmetic)."""
+    share the per-row arithmetic), for every chunk size."""
     import torch
-    print("\n  gdn_seq == repeated gdn_step", flush=True)
-    B, T = 2, 37
+    print(f"\n  gdn_seq == repeated gdn_step, T={T}", flush=True)
+    B = 2
     si = gi.step_inputs(3100, 0, B, T=T)
     M = gi.state(3100, 0, B)
     Ms, os_ = run_seq(g, si, M)
