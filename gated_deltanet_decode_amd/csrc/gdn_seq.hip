@@ -7,15 +7,20 @@ namespace gdn {
 namespace {
 
 // -------------------------------------------------------------- gdn_seq
-// One workgroup per (sequence, value head): 8 waves x 2 tiles, so the whole
-// 64 KiB head state lives in VGPRs (32 floats per lane) for all T tokens and
-// is read and written once per call.  The per-token inputs (k, q, v,
-// exp(gate), beta: 1.5 KiB per token) are staged through LDS in chunks of
-// CH tokens (8, 16 or 32 by sequence length), double-buffered (97 KiB of LDS
-// for CH = 32; gfx950 allows 160 KiB per workgroup): the global loads of
-// chunk c+1 are issued before chunk c is computed and written to LDS after
-// it, so their latency hides behind CH tokens of arithmetic.  Outputs overwrite the consumed v entries in LDS
-// (row j's v is read only by row j's lanes, before its output exists) and are
+// One workgroup per (sequence, value head), or per half head for short
+// sequences, of waves holding 2 tiles each: the head's state lives in VGPRs
+// (32 floats per lane) for all T tokens and is read and written once per
+// call.  Rows never exchange data, so a head splits across workgroups
+// freely; each part stages the head's k and q and flushes only its own rows'
+// outputs.
+//
+// The per-token inputs (k, q, v, exp(gate), beta: 1.5 KiB per token) are
+// staged through LDS in chunks of CH tokens (8, 16 or 32 by sequence length),
+// double-buffered (97 KiB of LDS for CH = 32; gfx950 allows 160 KiB per
+// workgroup): the global loads of chunk c+1 are issued before chunk c is
+// computed and written to LDS after it, so their latency hides behind CH
+// tokens of arithmetic.  Outputs overwrite the consumed v entries in LDS (row
+// j's v is read only by row j's lanes, before its output exists) and are
 // flushed to HBM with coalesced 16-byte stores once per chunk.  Two barriers
 // per chunk; none per token.
 //
@@ -24,14 +29,8 @@ namespace {
 // key dot product of token t+1, so only the key reduction sits on the
 // critical path between tokens.  Full chunks are unrolled, so every LDS
 // address is an immediate offset and no loop bookkeeping runs per token.
-// The kernel is VALU-issue bound (measured: VALU busy ~97 %), so every
+// Long sequences are VALU-issue bound (measured: VALU busy ~97 %), so every
 // instruction per token counts.
-#ifndef GDN_SEQ_TILES_PER_WAVE
-#define GDN_SEQ_TILES_PER_WAVE 2
-#endif
-constexpr int kSeqTilesPerWave = GDN_SEQ_TILES_PER_WAVE;
-constexpr int kSeqWaves = kTilesPerHead / kSeqTilesPerWave;   // 8
-constexpr int kSeqThreads = kSeqWaves * 64;                   // 512
 
 struct alignas(16) TokenLds {
     float k[D];
@@ -46,32 +45,32 @@ static_assert(sizeof(TokenLds) % 16 == 0, "float4 aligned token slots");
 // float4 loads per token: k (32) + q (32) + v (32)
 constexpr int kTokF4 = 3 * D / 4;
 
-// Sizes of a chunk of CH tokens (CH = 32: 3072 float4, 6 per thread).
-template <int CH>
+// Sizes of a chunk of CH tokens staged by NTH threads (CH = 32, NTH = 512:
+// 3072 float4, 6 per thread).
+template <int CH, int NTH>
 struct Chunk {
     static constexpr int kF4 = CH * kTokF4;
-    static constexpr int kFetchPer = (kF4 + kSeqThreads - 1) / kSeqThreads;
-    static constexpr int kFlushPer = (CH * D / 4 + kSeqThreads - 1) / kSeqThreads;
-    static_assert(2 * CH <= kSeqThreads, "one thread per gate and per beta");
+    static constexpr int kFetchPer = (kF4 + NTH - 1) / NTH;
+    static_assert(2 * CH <= NTH, "one thread per gate and per beta");
 };
 
-template <int CH>
+template <int CH, int NTH>
 struct ChunkRegs {
-    f4 f[Chunk<CH>::kFetchPer];
+    f4 f[Chunk<CH, NTH>::kFetchPer];
     float s;   // gate or beta of one token (threads 0 .. 2*CH-1)
 };
 
-template <int CH>
-__device__ __forceinline__ void seq_fetch(ChunkRegs<CH> &cr, const SeqArgs &a, int64_t b, int h,
+template <int CH, int NTH>
+__device__ __forceinline__ void seq_fetch(ChunkRegs<CH, NTH> &cr, const SeqArgs &a, int64_t b, int h,
                                           int kh, int t0, int tid) {
 #pragma unroll
-    for (int j = 0; j < Chunk<CH>::kFetchPer; ++j) {
-        const int e = tid + j * kSeqThreads;
+    for (int j = 0; j < Chunk<CH, NTH>::kFetchPer; ++j) {
+        const int e = tid + j * NTH;
         const int tt = e / kTokF4;
         const int w = e - tt * kTokF4;
         const int t = t0 + tt;
         f4 val = {0.f, 0.f, 0.f, 0.f};
-        if (e < Chunk<CH>::kF4 && t < a.T) {
+        if (e < Chunk<CH, NTH>::kF4 && t < a.T) {
             const int64_t bt = b * a.T + t;
             const float *src;
             if (w < 32)
@@ -95,12 +94,12 @@ __device__ __forceinline__ void seq_fetch(ChunkRegs<CH> &cr, const SeqArgs &a, i
     }
 }
 
-template <int CH>
-__device__ __forceinline__ void seq_stage(TokenLds *buf, const ChunkRegs<CH> &cr, int tid) {
+template <int CH, int NTH>
+__device__ __forceinline__ void seq_stage(TokenLds *buf, const ChunkRegs<CH, NTH> &cr, int tid) {
 #pragma unroll
-    for (int j = 0; j < Chunk<CH>::kFetchPer; ++j) {
-        const int e = tid + j * kSeqThreads;
-        if (e >= Chunk<CH>::kF4) break;
+    for (int j = 0; j < Chunk<CH, NTH>::kFetchPer; ++j) {
+        const int e = tid + j * NTH;
+        if (e >= Chunk<CH, NTH>::kF4) break;
         const int tt = e / kTokF4;
         const int w = e - tt * kTokF4;
         float *dst = w < 32 ? buf[tt].k + 4 * w
@@ -144,10 +143,13 @@ __device__ __forceinline__ void seq_token(TokenLds *buf, int tt, bool next, cons
     for (int t = 0; t < TPW; ++t) tok.v[rows[t]] = group_sum(o[t]) * kInvSqrtD;
 }
 
-// CH: tokens per LDS chunk; NT: nontemporal state load and store.
-template <int CH, bool NT>
-__global__ __launch_bounds__(kSeqThreads) void k_seq(SeqArgs a) {
-    constexpr int TPW = kSeqTilesPerWave;
+// CH: tokens per LDS chunk; NT: nontemporal state load and store; a head's
+// 128 rows are split over PARTS workgroups of 16 / (TPW * PARTS) waves with
+// TPW tiles each.
+template <int CH, bool NT, int TPW, int PARTS>
+__global__ __launch_bounds__(64 * 16 / (TPW * PARTS)) void k_seq(SeqArgs a) {
+    constexpr int NTH = 64 * 16 / (TPW * PARTS);
+    constexpr int R = D / PARTS;                  // rows of this workgroup
     __shared__ TokenLds lds[2][CH];
 
     const int tid = threadIdx.x;
@@ -156,7 +158,8 @@ __global__ __launch_bounds__(kSeqThreads) void k_seq(SeqArgs a) {
     const int grp = lane >> 3;
     const int c = lane & 7;
 
-    const int head = blockIdx.x;                  // b * Hv + h
+    const int head = blockIdx.x / PARTS;          // b * Hv + h
+    const int part = blockIdx.x - head * PARTS;
     const int b = head / a.Hv;
     const int h = head - b * a.Hv;
     const int kh = h % a.Hk;
@@ -166,11 +169,11 @@ __global__ __launch_bounds__(kSeqThreads) void k_seq(SeqArgs a) {
     RowSlice r[TPW];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-        rows[t] = (wave * TPW + t) * kRowsPerTile + grp;
+        rows[t] = part * R + (wave * TPW + t) * kRowsPerTile + grp;
         load_row<NT>(r[t], M + rows[t] * D, c);
     }
 
-    ChunkRegs<CH> cr;
+    ChunkRegs<CH, NTH> cr;
     seq_fetch(cr, a, b, h, kh, 0, tid);
     seq_stage(lds[0], cr, tid);
     __syncthreads();
@@ -203,10 +206,10 @@ __global__ __launch_bounds__(kSeqThreads) void k_seq(SeqArgs a) {
         __syncthreads();                 // outputs of chunk ch complete in LDS
 
 #pragma unroll
-        for (int j = 0; j < Chunk<CH>::kFlushPer; ++j) {   // flush: float4s of the outputs
-            const int e = tid + j * kSeqThreads;
-            const int tt = e / (D / 4);
-            const int col = (e % (D / 4)) * 4;
+        for (int j = 0; j < (CH * R / 4 + NTH - 1) / NTH; ++j) {   // flush this part's outputs
+            const int e = tid + j * NTH;
+            const int tt = e / (R / 4);
+            const int col = part * R + (e % (R / 4)) * 4;
             if (tt < nt) {
                 const int64_t o = ((static_cast<int64_t>(b) * a.T + t0 + tt) * a.Hv + h) * D + col;
                 *reinterpret_cast<f4 *>(a.out + o) = *reinterpret_cast<const f4 *>(buf[tt].v + col);
@@ -226,15 +229,24 @@ __global__ __launch_bounds__(kSeqThreads) void k_seq(SeqArgs a) {
 // short ones are dominated by the state transfer, which the nontemporal hint
 // speeds up by up to ~15 %, and by the last, partial chunk, which a smaller
 // chunk (fully unrolled more often) shortens.
+// Launch shape by sequence length (measured on MI355X):
+// - T = 1 runs the single-step kernel (in gdn_api.cpp);
+// - T <= 32: the state transfer dominates; two workgroups of 4 waves per head
+//   (64 rows each) let two heads' halves share a CU, so one's state transfer
+//   overlaps the other's arithmetic (15-24 % faster at B = 256, T = 2..8);
+//   the nontemporal hint speeds the transfer up; chunks of 8 (T < 16) or 16
+//   tokens shorten the last, partial chunk;
+// - longer sequences are VALU-bound: one 8-wave workgroup per head, 32-token
+//   chunks, plain state access (two parts per head measured 40 % slower).
 hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
     const int64_t heads = static_cast<int64_t>(a.B) * a.Hv;
-    const dim3 grid(static_cast<unsigned>(heads)), block(kSeqThreads);
+    const dim3 split(static_cast<unsigned>(heads * 2)), whole(static_cast<unsigned>(heads));
     if (a.T < 16)
-        k_seq<8, true><<<grid, block, 0, s>>>(a);
+        k_seq<8, true, 2, 2><<<split, dim3(256), 0, s>>>(a);
     else if (a.T <= 32)
-        k_seq<16, true><<<grid, block, 0, s>>>(a);
+        k_seq<16, true, 2, 2><<<split, dim3(256), 0, s>>>(a);
     else
-        k_seq<32, false><<<grid, block, 0, s>>>(a);
+        k_seq<32, false, 2, 1><<<whole, dim3(512), 0, s>>>(a);
     return hipGetLastError();
 }
 
