@@ -130,8 +130,10 @@ __global__ __launch_bounds__(W * 64) void k_step(StepArgs a, int n_tiles) {
 // state transfers instead of the four of two separate steps.  Unlike k_step
 // this kernel keeps q with the other loads and computes its tile indices
 // afresh each pass: with one read and two writes per row, fetching q late
-// measured 7 % slower and the incremental walk 1 % slower on MI355X.
-__global__ __launch_bounds__(kStepWaves * 64) void k_pair(PairArgs a, int n_tiles) {
+// measured 7 % slower and the incremental walk 1 % slower on MI355X.  W:
+// waves per workgroup, as in k_step (1 for small launches).
+template <int W>
+__global__ __launch_bounds__(W * 64) void k_pair(PairArgs a, int n_tiles) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int grp = lane >> 3;
@@ -140,9 +142,9 @@ __global__ __launch_bounds__(kStepWaves * 64) void k_pair(PairArgs a, int n_tile
     const int G = gridDim.x;
     const int g = blockIdx.x;
     const int lg = (G % kXcds == 0) ? (g % kXcds) * (G / kXcds) + g / kXcds : g;
-    const int stride = G * kStepWaves;
+    const int stride = G * W;
 
-    for (int u = lg * kStepWaves + wave; u < n_tiles; u += stride) {
+    for (int u = lg * W + wave; u < n_tiles; u += stride) {
         const int head = u / kTilesPerHead;
         const int row = (u % kTilesPerHead) * kRowsPerTile + grp;
         const int b = head / a.Hv;
@@ -200,6 +202,10 @@ constexpr int64_t kMaxGrid = 65536 / kStepWaves;
 // layers), 14 % at B = 2 and 2-4 % at B = 8..16 than the persistent walk on
 // 8-wave workgroups, which wins again from B = 64.
 constexpr int64_t kOneShotTiles = 8192;
+// The same for gdn_pair up to 2048 tiles (B * Hv <= 128): 21 % lower latency
+// at B = 1 (3.4 vs 4.25 us), 14 % at B = 2; from B = 8 the walk is as fast
+// or faster.
+constexpr int64_t kPairOneShotTiles = 2048;
 
 hipError_t launch_step(const StepArgs &a, hipStream_t s) {
     const int64_t tiles = static_cast<int64_t>(a.B) * a.Hv * kTilesPerHead;
@@ -223,11 +229,15 @@ hipError_t launch_step(const StepArgs &a, hipStream_t s) {
 
 hipError_t launch_pair(const PairArgs &a, hipStream_t s) {
     const int64_t tiles = static_cast<int64_t>(a.B) * a.Hv * kTilesPerHead;
+    if (tiles <= kPairOneShotTiles) {
+        k_pair<1><<<dim3(static_cast<unsigned>(tiles)), dim3(64), 0, s>>>(a, static_cast<int>(tiles));
+        return hipGetLastError();
+    }
     int64_t full = device_cus() * static_cast<int64_t>(GDN_STEP_WGS_PER_CU);
     if (full > kMaxGrid) full = kMaxGrid;
     const int64_t need = (tiles + kStepWaves - 1) / kStepWaves;
     const int grid = static_cast<int>(need < full ? need : full);
-    k_pair<<<dim3(grid), dim3(kStepWaves * 64), 0, s>>>(a, static_cast<int>(tiles));
+    k_pair<kStepWaves><<<dim3(grid), dim3(kStepWaves * 64), 0, s>>>(a, static_cast<int>(tiles));
     return hipGetLastError();
 }
 
