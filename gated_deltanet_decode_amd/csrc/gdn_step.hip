@@ -26,35 +26,46 @@ constexpr int kXcds = 8;
 // With a stride of whole heads (an even grid) the row block never changes
 // and (b, h) advance by constants, so the loop carries no integer division
 // (measured ~2 % faster at B = 256 than dividing on every pass).
+//
+// Epochs: workgroups g = e * GE + l (l < GE) walk the tiles of epoch e,
+// [e * E, (e + 1) * E) with E = GE * W * iters, together, like one
+// persistent launch of GE workgroups.  Large launches use many short epochs:
+// the dispatcher starts epoch e + 1's workgroups as epoch e's retire, which
+// keeps the tiles in flight in one contiguous window (one long persistent
+// walk lets the waves drift apart) and overlaps the end of one epoch with
+// the start of the next.  A single epoch is the plain persistent walk.
 struct TileWalk {
-    int u, head, row, b, h;
+    int u, end, head, row, b, h;
     int stride, hstep, db, dh, Hv, grp;
     bool whole;
 
     // Positions this wave (of W per workgroup) on its first tile; false if
-    // it has none.
+    // it has none.  GE: workgroups per epoch; iters: passes per epoch.
     template <int W>
-    __device__ bool init(int n_tiles, int Hv_, int wave, int grp_) {
-        const int G = gridDim.x;
-        const int g = blockIdx.x;
-        const int lg = (G % kXcds == 0) ? (g % kXcds) * (G / kXcds) + g / kXcds : g;
+    __device__ bool init(int n_tiles, int GE, int iters, int Hv_, int wave, int grp_) {
+        const int epoch = blockIdx.x / GE;
+        const int g = blockIdx.x - epoch * GE;
+        const int lg = (GE % kXcds == 0) ? (g % kXcds) * (GE / kXcds) + g / kXcds : g;
+        const int span = GE * W * iters;           // tiles per epoch
+        const int base = epoch * span;
+        end = n_tiles - base < span ? n_tiles : base + span;
         Hv = Hv_;
         grp = grp_;
-        stride = G * W;
-        u = lg * W + wave;
+        stride = GE * W;
+        u = base + lg * W + wave;
         whole = (stride % kTilesPerHead) == 0;
         hstep = stride / kTilesPerHead;
         db = hstep / Hv;
         dh = hstep - db * Hv;
-        if (u >= n_tiles) return false;
+        if (u >= end) return false;
         place();
         return true;
     }
 
-    // Advances to this wave's next tile; false when the walk is done.
-    __device__ bool next(int n_tiles) {
+    // Advances to this wave's next tile; false when its epoch is done.
+    __device__ bool next() {
         u += stride;
-        if (u >= n_tiles) return false;
+        if (u >= end) return false;
         if (whole) {
             head += hstep;
             h += dh;
@@ -86,13 +97,14 @@ struct TileWalk {
 // W: waves per workgroup (kStepWaves for the persistent walk; 1 for small
 // launches, where one wave per tile spreads the few tiles over every CU).
 template <bool kLateQ, int W>
-__global__ __launch_bounds__(W * 64) void k_step(StepArgs a, int n_tiles) {
+__global__ __launch_bounds__(W * 64) void k_step(StepArgs a, int n_tiles, int epoch_wgs,
+                                                 int epoch_iters) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane & 7;
 
     TileWalk w;
-    if (!w.template init<W>(n_tiles, a.Hv, wave, lane >> 3)) return;
+    if (!w.template init<W>(n_tiles, epoch_wgs, epoch_iters, a.Hv, wave, lane >> 3)) return;
     do {
         int kh = w.h;
         while (kh >= a.Hk) kh -= a.Hk;                        // key-head broadcast
@@ -119,7 +131,7 @@ __global__ __launch_bounds__(W * 64) void k_step(StepArgs a, int n_tiles) {
         store_row<true>(Mrow, r, c);
         const float o = group_sum(dot_part(r, qv)) * kInvSqrtD;   // step 5
         if (c == 0) a.out[static_cast<int64_t>(w.head) * D + w.row] = o;
-    } while (w.next(n_tiles));
+    } while (w.next());
 }
 
 // ------------------------------------------------------------- gdn_pair
@@ -207,23 +219,45 @@ constexpr int64_t kOneShotTiles = 8192;
 // or faster.
 constexpr int64_t kPairOneShotTiles = 2048;
 
+// Launches with more passes per wave than this run as epochs of
+// kEpochIters passes (measured per 256 sequences: 172 vs 175 us at B = 512,
+// 169 vs 195 us at B = 9216, where the 36 layers of the B = 256 decode in one
+// call take 6.1 ms against 6.2 ms for 36 separate launches).  Each epoch
+// workgroup reserves 96 KiB of (unused) LDS so that only one fits per CU,
+// as in the persistent walk; more waves per CU measured slower.
+// Epoch launches are kept under 2^22 workgroups (2^31 work-items: the
+// dispatch's grid size is a 32-bit count of work-items); larger ones, states
+// far beyond one GPU's memory, fall back to the persistent walk.
+constexpr int kPersistentIters = 64;
+constexpr int kEpochIters = 4;
+constexpr size_t kEpochLdsBytes = 96 * 1024;
+constexpr int64_t kMaxEpochWgs = int64_t(1) << 22;
+
 hipError_t launch_step(const StepArgs &a, hipStream_t s) {
     const int64_t tiles = static_cast<int64_t>(a.B) * a.Hv * kTilesPerHead;
+    const int nt = static_cast<int>(tiles);
     if (tiles <= kOneShotTiles) {
-        k_step<false, 1><<<dim3(static_cast<unsigned>(tiles)), dim3(64), 0, s>>>(
-            a, static_cast<int>(tiles));
+        k_step<false, 1><<<dim3(static_cast<unsigned>(tiles)), dim3(64), 0, s>>>(a, nt, nt, 1);
         return hipGetLastError();
     }
     int64_t full = device_cus() * static_cast<int64_t>(GDN_STEP_WGS_PER_CU);
     if (full > kMaxGrid) full = kMaxGrid;
     const int64_t need = (tiles + kStepWaves - 1) / kStepWaves;
     const int grid = static_cast<int>(need < full ? need : full);
-    if (tiles > static_cast<int64_t>(grid) * kStepWaves)   // several passes per wave
+    const int64_t passes = (tiles + static_cast<int64_t>(grid) * kStepWaves - 1) /
+                           (static_cast<int64_t>(grid) * kStepWaves);
+    const int64_t span = static_cast<int64_t>(grid) * kStepWaves * kEpochIters;
+    const int64_t epochs = (tiles + span - 1) / span;
+    if (passes > kPersistentIters && grid * epochs <= kMaxEpochWgs) {
+        k_step<true, kStepWaves><<<dim3(static_cast<unsigned>(grid * epochs)),
+                                   dim3(kStepWaves * 64), kEpochLdsBytes, s>>>(a, nt, grid,
+                                                                               kEpochIters);
+    } else if (passes > 1) {
         k_step<true, kStepWaves><<<dim3(grid), dim3(kStepWaves * 64), 0, s>>>(
-            a, static_cast<int>(tiles));
-    else
-        k_step<false, kStepWaves><<<dim3(grid), dim3(kStepWaves * 64), 0, s>>>(
-            a, static_cast<int>(tiles));
+            a, nt, grid, static_cast<int>(passes));
+    } else {
+        k_step<false, kStepWaves><<<dim3(grid), dim3(kStepWaves * 64), 0, s>>>(a, nt, grid, 1);
+    }
     return hipGetLastError();
 }
 

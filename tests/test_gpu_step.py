@@ -48,6 +48,20 @@ def test_step_matches_oracle(g, orc, B, Hv, Hk):
     ref.assert_close("out", og, want, OUT_TOL)
 
 
+def test_step_epoch_launch_matches_oracle(g, orc):
+    # 257 x 33 heads = 135,696 tiles: more than 64 passes of the persistent
+    # grid, so the launch runs as 4-pass epochs; 17 of them, the last one
+    # ragged, with a head count that does not divide the walk's stride.
+    B, Hv, Hk = 257, 33, 11
+    print(f"\n  gdn_step epoch launch B={B} Hv={Hv} Hk={Hk}", flush=True)
+    si = gi.step_inputs(2600, Hv, B, Hv, Hk)
+    M = gi.state(2600, Hv, B, Hv)
+    Mg, og = run_step(g, si, M)
+    want = ref.step_mt(orc, si, M)
+    ref.assert_close("state", Mg, M, STATE_TOL)
+    ref.assert_close("out", og, want, OUT_TOL)
+
+
 def test_step_b1_single_sequence(g, orc):
     """One sequence, one token, the page geometry."""
     c = gi.WORKLOADS["step_b1"]
