@@ -151,7 +151,10 @@ int gdn_seq(const gdn_dims *dims, int32_t B, int32_t T, const float *q, const fl
     clear_error();
     GDN_TRY(check_dims(dims));
     GDN_TRY(check_batch(dims, B, "B"));
-    if (T < 1) return fail(GDN_ERR_SHAPE, "T must be >= 1 (got %d)", T);
+    // 2^30 keeps the kernels' 32-bit token arithmetic (t + chunk length)
+    // clear of overflow; no buffer of that many tokens fits a GPU.
+    if (T < 1 || T > (1 << 30))
+        return fail(GDN_ERR_SHAPE, "T must be in [1, 1073741824] (got %d)", T);
     const size_t f = sizeof(float);
     const size_t BT = static_cast<size_t>(B) * T;
     const size_t nqk = BT * dims->n_k_heads * dims->d_k * f;

@@ -29,6 +29,9 @@ namespace {
 // key dot product of token t+1, so only the key reduction sits on the
 // critical path between tokens.  Full chunks are unrolled, so every LDS
 // address is an immediate offset and no loop bookkeeping runs per token.
+// A wave's two tiles are reduced together (seq_token, pair_sum): per token
+// and lane that is 3 DPP adds for both key sums and 3 for both outputs, one
+// delta and one output, instead of 6 + 6, two and two.
 // Long sequences are VALU-issue bound (measured: VALU busy ~97 %), so every
 // instruction per token counts.
 
@@ -42,70 +45,79 @@ struct alignas(16) TokenLds {
 };
 static_assert(sizeof(TokenLds) % 16 == 0, "float4 aligned token slots");
 
-// float4 loads per token: k (32) + q (32) + v (32)
-constexpr int kTokF4 = 3 * D / 4;
-
-// Sizes of a chunk of CH tokens staged by NTH threads (CH = 32, NTH = 512:
-// 3072 float4, 6 per thread).
+// Chunk staging: every thread fetches float4 column 4 * (tid % 32) of k, q
+// and v for tokens tid / 32 + n * NTH / 32 of the chunk, kSlots tokens per
+// array (CH = 32, NTH = 512: 2 tokens, 6 float4 per thread).  A slot's array
+// and token offset are compile-time constants, so a chunk's addresses are a
+// few pointer increments.
 template <int CH, int NTH>
 struct Chunk {
-    static constexpr int kF4 = CH * kTokF4;
-    static constexpr int kFetchPer = (kF4 + NTH - 1) / NTH;
+    static constexpr int kTokStride = NTH / 32;          // tokens apart of a thread's slots
+    static constexpr int kSlots = CH / kTokStride;       // slots per array
+    static constexpr int kFetchPer = 3 * kSlots;
+    static_assert(NTH % 32 == 0 && CH % kTokStride == 0, "whole token rows per slot");
     static_assert(2 * CH <= NTH, "one thread per gate and per beta");
 };
 
 template <int CH, int NTH>
 struct ChunkRegs {
-    f4 f[Chunk<CH, NTH>::kFetchPer];
+    f4 f[Chunk<CH, NTH>::kFetchPer];   // k slots, then q, then v
     float s;   // gate or beta of one token (threads 0 .. 2*CH-1)
 };
 
-template <int CH, int NTH>
+// kClamp: the chunk may run past token T - 1 (only a sequence's last chunk
+// can); slots past the end load token T - 1 again, which nothing reads (a
+// partial chunk computes, flushes and takes the next key of its first nt
+// tokens only).  Every load is unconditional and in bounds.
+template <int CH, int NTH, bool kClamp>
 __device__ __forceinline__ void seq_fetch(ChunkRegs<CH, NTH> &cr, const SeqArgs &a, int64_t b, int h,
                                           int kh, int t0, int tid) {
+    using C = Chunk<CH, NTH>;
+    const int col = 4 * (tid & 31);
+    const int t = t0 + (tid >> 5);                      // token of slot 0
+    const int64_t bt = b * a.T + t;
+    const int64_t koff = (bt * a.Hk + kh) * D + col;    // k and q share the layout
+    const int64_t voff = (bt * a.Hv + h) * D + col;
+    const int64_t ktok = static_cast<int64_t>(a.Hk) * D;   // one token apart
+    const int64_t vtok = static_cast<int64_t>(a.Hv) * D;
 #pragma unroll
-    for (int j = 0; j < Chunk<CH, NTH>::kFetchPer; ++j) {
-        const int e = tid + j * NTH;
-        const int tt = e / kTokF4;
-        const int w = e - tt * kTokF4;
-        const int t = t0 + tt;
-        f4 val = {0.f, 0.f, 0.f, 0.f};
-        if (e < Chunk<CH, NTH>::kF4 && t < a.T) {
-            const int64_t bt = b * a.T + t;
-            const float *src;
-            if (w < 32)
-                src = a.k + (bt * a.Hk + kh) * D + 4 * w;
-            else if (w < 64)
-                src = a.q + (bt * a.Hk + kh) * D + 4 * (w - 32);
-            else
-                src = a.v + (bt * a.Hv + h) * D + 4 * (w - 64);
-            val = *reinterpret_cast<const f4 *>(src);
-        }
-        cr.f[j] = val;
+    for (int n = 0; n < C::kSlots; ++n) {
+        const int dt = kClamp ? min(t + n * C::kTokStride, a.T - 1) - t : n * C::kTokStride;
+        cr.f[n] = *reinterpret_cast<const f4 *>(a.k + koff + dt * ktok);
+        cr.f[C::kSlots + n] = *reinterpret_cast<const f4 *>(a.q + koff + dt * ktok);
+        cr.f[2 * C::kSlots + n] = *reinterpret_cast<const f4 *>(a.v + voff + dt * vtok);
     }
     cr.s = 0.0f;
     if (tid < 2 * CH) {
         const int tt = tid < CH ? tid : tid - CH;
-        const int t = t0 + tt;
-        if (t < a.T) {
-            const int64_t idx = (b * a.T + t) * a.Hv + h;
-            cr.s = tid < CH ? a.gate[idx] : a.beta[idx];
-        }
+        const int tg = kClamp ? min(t0 + tt, a.T - 1) : t0 + tt;
+        const int64_t idx = (b * a.T + tg) * a.Hv + h;
+        cr.s = tid < CH ? a.gate[idx] : a.beta[idx];
     }
 }
 
 template <int CH, int NTH>
+__device__ __forceinline__ void fetch_chunk(ChunkRegs<CH, NTH> &cr, const SeqArgs &a, int64_t b, int h,
+                                            int kh, int t0, int tid) {
+    // 8-token chunks (sequences under 16 tokens) always clamp: one code path
+    // measured 1-3 % faster at T = 3..6.
+    if (CH > 8 && t0 + CH <= a.T)
+        seq_fetch<CH, NTH, false>(cr, a, b, h, kh, t0, tid);
+    else
+        seq_fetch<CH, NTH, true>(cr, a, b, h, kh, t0, tid);
+}
+
+template <int CH, int NTH>
 __device__ __forceinline__ void seq_stage(TokenLds *buf, const ChunkRegs<CH, NTH> &cr, int tid) {
+    using C = Chunk<CH, NTH>;
+    const int col = 4 * (tid & 31);
+    TokenLds *tok = buf + (tid >> 5);
 #pragma unroll
-    for (int j = 0; j < Chunk<CH, NTH>::kFetchPer; ++j) {
-        const int e = tid + j * NTH;
-        if (e >= Chunk<CH, NTH>::kF4) break;
-        const int tt = e / kTokF4;
-        const int w = e - tt * kTokF4;
-        float *dst = w < 32 ? buf[tt].k + 4 * w
-                   : w < 64 ? buf[tt].q + 4 * (w - 32)
-                            : buf[tt].v + 4 * (w - 64);
-        *reinterpret_cast<f4 *>(dst) = cr.f[j];
+    for (int n = 0; n < C::kSlots; ++n) {
+        TokenLds &tk = tok[n * C::kTokStride];
+        *reinterpret_cast<f4 *>(tk.k + col) = cr.f[n];
+        *reinterpret_cast<f4 *>(tk.q + col) = cr.f[C::kSlots + n];
+        *reinterpret_cast<f4 *>(tk.v + col) = cr.f[2 * C::kSlots + n];
     }
     if (tid < CH)
         buf[tid].e = expf(cr.s);          // the token's decay factor, computed once
@@ -113,42 +125,87 @@ __device__ __forceinline__ void seq_stage(TokenLds *buf, const ChunkRegs<CH, NTH
         buf[tid - CH].beta = cr.s;
 }
 
+// Plain DPP move (no `old` operand to materialise); every lane of the
+// patterns used here has a source lane, so none reads the bound value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+// group_sum() of two rows A and B at once, for a row group whose lanes hold
+// both rows in swapped register slots: lanes 0-3 have A's partial in `own`
+// and B's in `other`, lanes 4-7 the reverse.  Returns A's sum in lanes 0-3
+// and B's in lanes 4-7, with group_sum()'s bits: the first level adds the
+// same pairs of partials (lane i and lane 7-i), and the other two stay
+// within lanes 0-3 or 4-7.
+__device__ __forceinline__ float pair_sum(float own, float other) {
+    float x = own + dpp<0x141>(other);
+    x = x + dpp<0xB1>(x);
+    x = x + dpp<0x4E>(x);
+    return x;
+}
+
+// dst = s ? a : b, element by element.
+__device__ __forceinline__ void select_row(RowSlice &dst, bool s, const RowSlice &a,
+                                           const RowSlice &b) {
+#pragma unroll
+    for (int i = 0; i < kF4PerLane; ++i) {
+        dst.m[i].x = s ? a.m[i].x : b.m[i].x;
+        dst.m[i].y = s ? a.m[i].y : b.m[i].y;
+        dst.m[i].z = s ? a.m[i].z : b.m[i].z;
+        dst.m[i].w = s ? a.m[i].w : b.m[i].w;
+    }
+}
+
 // Token tt of a chunk: steps 3-5 of tt and, when `next`, steps 1-2 of tt+1
 // (kv holds k of token tt on entry and of tt+1 on exit; p the key partials).
-template <int TPW>
-__device__ __forceinline__ void seq_token(TokenLds *buf, int tt, bool next, const int (&rows)[TPW],
-                                          RowSlice (&r)[TPW], VecSlice &kv, float (&p)[TPW],
-                                          int c) {
+// kPair: a lane's two rows sit in swapped slots (slot 0 is row A in lanes 0-3
+// of the row group and row B in lanes 4-7), so pair_sum() reduces both rows
+// with one set of DPP adds, each lane computes the delta of its slot-0 row
+// only and takes the other row's from its mirror lane, and writes one output.
+// Otherwise each slot is reduced on its own.  Both give the same bits.
+template <bool kPair>
+__device__ __forceinline__ void seq_token(TokenLds *buf, int tt, bool next, const int (&rows)[2],
+                                          RowSlice (&r)[2], VecSlice &kv, float (&p)[2], int c) {
     TokenLds &tok = buf[tt];
-    float d[TPW];
+    float d[2];                                                // step 3
+    if (kPair) {
+        d[0] = (tok.v[rows[0]] - pair_sum(p[0], p[1])) * tok.beta;
+        d[1] = dpp_mov<0x141>(d[0]);                           // from lane 7-c: the other row
+    } else {
 #pragma unroll
-    for (int t = 0; t < TPW; ++t)                              // step 3
-        d[t] = (tok.v[rows[t]] - group_sum(p[t])) * tok.beta;
+        for (int t = 0; t < 2; ++t) d[t] = (tok.v[rows[t]] - group_sum(p[t])) * tok.beta;
+    }
     VecSlice qv;
     load_vec(qv, tok.q, c);
-    float o[TPW];
+    float o[2];
     if (next) {
         VecSlice kn;
         load_vec(kn, buf[tt + 1].k, c);
         const float en = buf[tt + 1].e;
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) pass(r[t], d[t], kv, qv, en, kn, o[t], p[t]);
+        for (int t = 0; t < 2; ++t) pass(r[t], d[t], kv, qv, en, kn, o[t], p[t]);
         kv = kn;
     } else {
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) o[t] = body_part(r[t], d[t], kv, qv);
+        for (int t = 0; t < 2; ++t) o[t] = body_part(r[t], d[t], kv, qv);
     }
-    // every lane of the row group holds the same output bits
+    // every lane holding a row in a written slot has the same output bits
+    if (kPair) {
+        tok.v[rows[0]] = pair_sum(o[0], o[1]) * kInvSqrtD;
+    } else {
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) tok.v[rows[t]] = group_sum(o[t]) * kInvSqrtD;
+        for (int t = 0; t < 2; ++t) tok.v[rows[t]] = group_sum(o[t]) * kInvSqrtD;
+    }
 }
 
-// CH: tokens per LDS chunk; NT: nontemporal state load and store; a head's
-// 128 rows are split over PARTS workgroups of 16 / (TPW * PARTS) waves with
-// TPW tiles each.
-template <int CH, bool NT, int TPW, int PARTS>
-__global__ __launch_bounds__(64 * 16 / (TPW * PARTS)) void k_seq(SeqArgs a) {
-    constexpr int NTH = 64 * 16 / (TPW * PARTS);
+// CH: tokens per LDS chunk; NT: nontemporal state load and store; PAIR:
+// paired row reductions (seq_token); a head's 128 rows are split over PARTS
+// workgroups of 8 / PARTS waves with two tiles each.
+template <int CH, bool NT, bool PAIR, int PARTS>
+__global__ __launch_bounds__(64 * 8 / PARTS) void k_seq(SeqArgs a) {
+    constexpr int NTH = 64 * 8 / PARTS;
     constexpr int R = D / PARTS;                  // rows of this workgroup
     __shared__ TokenLds lds[2][CH];
 
@@ -165,23 +222,35 @@ __global__ __launch_bounds__(64 * 16 / (TPW * PARTS)) void k_seq(SeqArgs a) {
     const int kh = h % a.Hk;
 
     float *M = a.state + static_cast<int64_t>(head) * (D * D);
-    int rows[TPW];
-    RowSlice r[TPW];
+    // The wave's two tiles.  The state moves in tile order (whole 128-byte
+    // lines per instruction); with PAIR, lanes 4-7 of each row group swap
+    // the two slots in registers, as seq_token() expects.  rows[] is per slot.
+    const bool swap = PAIR && c >= 4;
+    int tile_row[2], rows[2];
+    RowSlice r[2];
+    {
+        RowSlice m[2];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        rows[t] = part * R + (wave * TPW + t) * kRowsPerTile + grp;
-        load_row<NT>(r[t], M + rows[t] * D, c);
+        for (int t = 0; t < 2; ++t) {
+            tile_row[t] = part * R + (wave * 2 + t) * kRowsPerTile + grp;
+            load_row<NT>(m[t], M + tile_row[t] * D, c);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            rows[t] = swap ? tile_row[t ^ 1] : tile_row[t];
+            select_row(r[t], swap, m[t ^ 1], m[t]);
+        }
     }
 
     ChunkRegs<CH, NTH> cr;
-    seq_fetch(cr, a, b, h, kh, 0, tid);
+    fetch_chunk(cr, a, b, h, kh, 0, tid);
     seq_stage(lds[0], cr, tid);
     __syncthreads();
 
     const int n_chunks = (a.T + CH - 1) / CH;
     for (int ch = 0; ch < n_chunks; ++ch) {
         const bool more = ch + 1 < n_chunks;
-        if (more) seq_fetch(cr, a, b, h, kh, (ch + 1) * CH, tid);
+        if (more) fetch_chunk(cr, a, b, h, kh, (ch + 1) * CH, tid);
 
         TokenLds *buf = lds[ch & 1];
         const int t0 = ch * CH;
@@ -190,18 +259,18 @@ __global__ __launch_bounds__(64 * 16 / (TPW * PARTS)) void k_seq(SeqArgs a) {
         // steps 1-2 of the chunk's first token
         VecSlice kv;
         load_vec(kv, buf[0].k, c);
-        float p[TPW];
+        float p[2];
         {
             const float e0 = buf[0].e;
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) p[t] = head_part(r[t], kv, e0);
+            for (int t = 0; t < 2; ++t) p[t] = head_part(r[t], kv, e0);
         }
         if (nt == CH) {
             // full chunk: unrolled, so every LDS address is an immediate offset
 #pragma unroll
-            for (int tt = 0; tt < CH; ++tt) seq_token(buf, tt, tt + 1 < CH, rows, r, kv, p, c);
+            for (int tt = 0; tt < CH; ++tt) seq_token<PAIR>(buf, tt, tt + 1 < CH, rows, r, kv, p, c);
         } else {
-            for (int tt = 0; tt < nt; ++tt) seq_token(buf, tt, tt + 1 < nt, rows, r, kv, p, c);
+            for (int tt = 0; tt < nt; ++tt) seq_token<PAIR>(buf, tt, tt + 1 < nt, rows, r, kv, p, c);
         }
         __syncthreads();                 // outputs of chunk ch complete in LDS
 
@@ -219,7 +288,11 @@ __global__ __launch_bounds__(64 * 16 / (TPW * PARTS)) void k_seq(SeqArgs a) {
         __syncthreads();                 // chunk ch+1 staged; chunk ch flushed
     }
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) store_row<NT>(M + rows[t] * D, r[t], c);
+    for (int t = 0; t < 2; ++t) {
+        RowSlice m;
+        select_row(m, swap, r[t ^ 1], r[t]);
+        store_row<NT>(M + tile_row[t] * D, m, c);
+    }
 }
 
 }  // namespace
@@ -237,16 +310,20 @@ __global__ __launch_bounds__(64 * 16 / (TPW * PARTS)) void k_seq(SeqArgs a) {
 //   the nontemporal hint speeds the transfer up; chunks of 8 (T < 16) or 16
 //   tokens shorten the last, partial chunk;
 // - longer sequences are VALU-bound: one 8-wave workgroup per head, 32-token
-//   chunks, plain state access (two parts per head measured 40 % slower).
+//   chunks, plain state access (two parts per head measured 40 % slower);
+// - paired row reductions from 16 tokens on (5-10 % faster there).  In the
+//   8-token-chunk kernel they raise the register count so that two instead
+//   of three workgroups fit on a CU, which measured slower (B = 256, T = 8:
+//   230 against 196 us).
 hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
     const int64_t heads = static_cast<int64_t>(a.B) * a.Hv;
     const dim3 split(static_cast<unsigned>(heads * 2)), whole(static_cast<unsigned>(heads));
     if (a.T < 16)
-        k_seq<8, true, 2, 2><<<split, dim3(256), 0, s>>>(a);
+        k_seq<8, true, false, 2><<<split, dim3(256), 0, s>>>(a);
     else if (a.T <= 32)
-        k_seq<16, true, 2, 2><<<split, dim3(256), 0, s>>>(a);
+        k_seq<16, true, true, 2><<<split, dim3(256), 0, s>>>(a);
     else
-        k_seq<32, false, 2, 1><<<whole, dim3(512), 0, s>>>(a);
+        k_seq<32, false, true, 1><<<whole, dim3(512), 0, s>>>(a);
     return hipGetLastError();
 }
 

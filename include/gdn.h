@@ -24,7 +24,7 @@
  *   - Inputs are read-only; `state` and `conv_state` are updated in place.
  *     Outputs must not overlap any input or state buffer.
  *   - Supported on the GPU path: d_k = d_v = 128, n_k_heads >= 1,
- *     n_v_heads a multiple of n_k_heads, B >= 1, T >= 1,
+ *     n_v_heads a multiple of n_k_heads, B >= 1, 1 <= T <= 1073741824,
  *     B * n_v_heads <= 134213631.
  *   - Results are bitwise deterministic for identical inputs, independent of
  *     B and of the other sequences in the batch.  gdn_seq over T tokens is

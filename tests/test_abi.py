@@ -103,6 +103,8 @@ def test_seq_validation(g):
                                     aa["beta"], aa["gate"], aa["state"], aa["out"], None)
     expect(g, f(0, a), -2, "T")
     expect(g, f(-1, a), -2, "T")
+    expect(g, f((1 << 30) + 1, a), -2, "T")
+    expect(g, f(2**31 - 1, a), -2, "T")
     expect(g, f(4, dict(a, gate=None)), -1, "gate")
     expect(g, f(4, dict(a, v=a["v"] + 4)), -3, "v")
     expect(g, f(1, dict(a, out=a["state"] - 16)), -4, "out")
