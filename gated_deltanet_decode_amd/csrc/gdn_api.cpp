@@ -7,11 +7,32 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
 
 #include "gdn_launch.hpp"
+
+namespace gdn {
+
+// A value that never changes; relaxed atomics make concurrent first calls
+// from several host threads well defined.
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+}  // namespace gdn
 
 namespace {
 

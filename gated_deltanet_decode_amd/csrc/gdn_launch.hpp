@@ -125,6 +125,10 @@ struct TailFusedArgs {
 // 1 or 2, conv kernel 4, gated-norm group equal to the head dimension).
 bool tail_fused_supported(int32_t Hv, int32_t Hk, int32_t K, int32_t group);
 
+// Compute units of the current device, read once per device and cached
+// (256 on MI355X; 256 too if the query fails).
+int device_cus();
+
 hipError_t launch_step(const StepArgs &a, hipStream_t s);
 hipError_t launch_tail_fused(const TailFusedArgs &a, hipStream_t s);
 hipError_t launch_seq(const SeqArgs &a, hipStream_t s);

@@ -202,9 +202,10 @@ __device__ __forceinline__ void seq_token(TokenLds *buf, int tt, bool next, cons
 
 // CH: tokens per LDS chunk; NT: nontemporal state load and store; PAIR:
 // paired row reductions (seq_token); a head's 128 rows are split over PARTS
-// workgroups of 8 / PARTS waves with two tiles each.
-template <int CH, bool NT, bool PAIR, int PARTS>
-__global__ __launch_bounds__(64 * 8 / PARTS) void k_seq(SeqArgs a) {
+// workgroups of 8 / PARTS waves with two tiles each; WPS: waves per SIMD the
+// register allocation must allow (3 caps it at 168 VGPRs).
+template <int CH, bool NT, bool PAIR, int PARTS, int WPS>
+__global__ __launch_bounds__(64 * 8 / PARTS, WPS) void k_seq(SeqArgs a) {
     constexpr int NTH = 64 * 8 / PARTS;
     constexpr int R = D / PARTS;                  // rows of this workgroup
     __shared__ TokenLds lds[2][CH];
@@ -297,33 +298,40 @@ __global__ __launch_bounds__(64 * 8 / PARTS) void k_seq(SeqArgs a) {
 
 }  // namespace
 
-// Chunk size and state access by sequence length (measured on MI355X):
-// long sequences stage 32 tokens per chunk and keep the plain state access;
-// short ones are dominated by the state transfer, which the nontemporal hint
-// speeds up by up to ~15 %, and by the last, partial chunk, which a smaller
-// chunk (fully unrolled more often) shortens.
-// Launch shape by sequence length (measured on MI355X):
-// - T = 1 runs the single-step kernel (in gdn_api.cpp);
-// - T <= 32: the state transfer dominates; two workgroups of 4 waves per head
-//   (64 rows each) let two heads' halves share a CU, so one's state transfer
-//   overlaps the other's arithmetic (15-24 % faster at B = 256, T = 2..8);
-//   the nontemporal hint speeds the transfer up; chunks of 8 (T < 16) or 16
-//   tokens shorten the last, partial chunk;
-// - longer sequences are VALU-bound: one 8-wave workgroup per head, 32-token
-//   chunks, plain state access (two parts per head measured 40 % slower);
-// - paired row reductions from 16 tokens on (5-10 % faster there).  In the
-//   8-token-chunk kernel they raise the register count so that two instead
-//   of three workgroups fit on a CU, which measured slower (B = 256, T = 8:
-//   230 against 196 us).
+// Launch shape (measured on MI355X, 256 CUs, 32 heads):
+// - T = 1 runs the single-step kernel (in gdn_api.cpp).
+// - T <= 64: half heads (two workgroups of 4 waves, 64 rows each, per head),
+//   so that several share a CU and one's state transfer overlaps the
+//   others' arithmetic; nontemporal state access; 8-token chunks below 16
+//   tokens, 16-token chunks from there.  Whole heads are 3-30 % slower here
+//   except at B = 6..8 and T near 64 (up to 4 % faster; not special-cased).
+//   With few heads, paired reductions: fewer instructions, and occupancy
+//   does not matter.  With many, unpaired reductions and registers for three
+//   workgroups per CU: the 8-token kernel needs 168 VGPRs unpaired, 181
+//   paired (two per CU); the 16-token kernel is held to 168 (a few spill).
+//   Thresholds: T < 16, paired up to `CUs` heads (2-5 % faster at B <= 8,
+//   5-25 % slower from B = 32); T >= 16, paired up to 2 x CUs heads (best
+//   up to B = 16; from B = 24 unpaired is 1-20 % faster).
+// - Longer sequences: whole heads, one 8-wave workgroup per head, 32-token
+//   chunks, plain state access, paired reductions.  They are VALU-bound, and
+//   half heads would duplicate the staging (40 % slower at B = 8, T = 4096).
 hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
     const int64_t heads = static_cast<int64_t>(a.B) * a.Hv;
+    const int64_t cus = device_cus();
     const dim3 split(static_cast<unsigned>(heads * 2)), whole(static_cast<unsigned>(heads));
-    if (a.T < 16)
-        k_seq<8, true, false, 2><<<split, dim3(256), 0, s>>>(a);
-    else if (a.T <= 32)
-        k_seq<16, true, true, 2><<<split, dim3(256), 0, s>>>(a);
-    else
-        k_seq<32, false, true, 1><<<whole, dim3(512), 0, s>>>(a);
+    if (a.T < 16) {
+        if (heads <= cus)
+            k_seq<8, true, true, 2, 1><<<split, dim3(256), 0, s>>>(a);
+        else
+            k_seq<8, true, false, 2, 1><<<split, dim3(256), 0, s>>>(a);
+    } else if (a.T <= 64) {
+        if (heads <= 2 * cus)
+            k_seq<16, true, true, 2, 1><<<split, dim3(256), 0, s>>>(a);
+        else
+            k_seq<16, true, false, 2, 3><<<split, dim3(256), 0, s>>>(a);
+    } else {
+        k_seq<32, false, true, 1, 1><<<whole, dim3(512), 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 

@@ -1,8 +1,6 @@
 // gdn_step.hip - gdn_step and gdn_pair: the HBM-streaming one- and
 // two-position kernels (persistent tile walk over the state).
 
-#include <atomic>
-
 #include "gdn_device.hpp"
 
 namespace gdn {
@@ -186,23 +184,6 @@ __global__ __launch_bounds__(W * 64) void k_pair(PairArgs a, int n_tiles) {
 #ifndef GDN_STEP_WGS_PER_CU
 #define GDN_STEP_WGS_PER_CU 1
 #endif
-
-// Compute units of the current device, read once per device and cached (a
-// value that never changes; relaxed atomics make concurrent first calls
-// from several host threads well defined).
-static int device_cus() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int n = cache[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n <= 0)
-            n = 256;
-        cache[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
 
 // The walks' 32-bit tile index may run one stride (grid x kStepWaves) past
 // the last tile; the C ABI leaves 65536 of headroom below INT32_MAX, so the
