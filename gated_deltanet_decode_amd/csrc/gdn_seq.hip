@@ -29,11 +29,11 @@ namespace {
 // key dot product of token t+1, so only the key reduction sits on the
 // critical path between tokens.  Full chunks are unrolled, so every LDS
 // address is an immediate offset and no loop bookkeeping runs per token.
-// A wave's two tiles are reduced together (seq_token, pair_sum): per token
-// and lane that is 3 DPP adds for both key sums and 3 for both outputs, one
-// delta and one output, instead of 6 + 6, two and two.
-// Long sequences are VALU-issue bound (measured: VALU busy ~97 %), so every
-// instruction per token counts.
+// With PAIR, a wave's two tiles are reduced together (seq_token, pair_sum):
+// per token and lane that is 3 DPP adds for both key sums and 3 for both
+// outputs, one delta and one output, instead of 6 + 6, two and two.
+// Long sequences are VALU-issue bound (measured: VALU instructions issue
+// 81-96 % of the time), so every instruction per token counts.
 
 struct alignas(16) TokenLds {
     float k[D];
