@@ -82,6 +82,28 @@ def test_graph_capture_step_seq_pair_tail(g):
             {"M": M, "cs": ti["conv_state"]}, {"y": torch.empty((B, 4096), device="cuda")})
 
 
+def test_graph_capture_large_launch_shapes(g):
+    """The launch shapes that only large calls take: gdn_seq with more half
+    heads than fit two per CU (the 16-token kernel held to three workgroups
+    per CU, which spills a few registers to scratch) and gdn_step beyond 64
+    passes of the tile walk (epochs, with a dynamic LDS reservation)."""
+    import torch
+    print("\n  graph capture: seq B=24 T=20, step B=300 (epochs)", flush=True)
+    B = 24
+    ss = {n: dev(x) for n, x in gi.step_inputs(6004, 0, B, T=20).items()}
+    M = dev(gi.state(6004, 0, B))
+    _replay_matches_eager(
+        lambda st, o: g.seq(ss["q"], ss["k"], ss["v"], ss["beta"], ss["gate"], st["M"], o["out"]),
+        {"M": M}, {"out": torch.empty((B, 20, 32, 128), device="cuda")})
+    del M
+    B = 300                                   # 300 x 32 x 16 = 153,600 tiles
+    si = {n: dev(x) for n, x in gi.step_inputs(6005, 0, B).items()}
+    M = dev(gi.state(6005, 0, B))
+    _replay_matches_eager(
+        lambda st, o: g.step(si["q"], si["k"], si["v"], si["beta"], si["gate"], st["M"], o["out"]),
+        {"M": M}, {"out": torch.empty((B, 32, 128), device="cuda")})
+
+
 def test_graph_capture_gate_transform_and_tail_ba(g):
     import torch
     print("\n  graph capture: gate transform, tail from raw gates", flush=True)
