@@ -124,6 +124,33 @@ def inplace_probe(torch, stream, buf, reps=5):
     return 2 * nbytes / (ms / 1e3) / 1e9
 
 
+def fma_probe(torch, stream, workgroups, threads, iters=20000, reps=3):
+    """Non-packed FP32 FMA rate (TFLOP/s) of independent fmaf chains with no
+    memory traffic, at `workgroups` x `threads` threads: the VALU ceiling at
+    that number of waves per CU."""
+    import ctypes
+    from gated_deltanet_decode_amd._build import PROBE_LIBRARY
+    lib = ctypes.CDLL(PROBE_LIBRARY)
+    lib.gdn_probe_fma.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_void_p]
+    n = workgroups * threads
+    out = torch.empty(n, device="cuda")
+
+    def once():
+        assert lib.gdn_probe_fma(out.data_ptr(), n, workgroups, threads, iters,
+                                 stream.cuda_stream) == 0
+    once()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(reps):
+        once()
+    e.record(stream)
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    return 2.0 * n * iters * 16 / (ms / 1e3) / 1e12
+
+
 def copy_probe(torch, stream, nbytes=1 << 30, reps=5):
     """Bandwidth of a plain device-to-device copy (read + write bytes / s)."""
     import ctypes
@@ -435,10 +462,19 @@ def extra_measurements(torch, g, stream, only=None):
                                   stream=stream), 5)
         upd = 8 * 4096 * HV
         flops = upd * D * D * 7  # decay mul + 3 FMA per element
+        tf = flops / (ms / 1e3) / 1e12
+        # the VALU ceiling measured at the kernel's own occupancy (one 8-wave
+        # workgroup per CU, as this launch) and at 16 waves per CU
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        probe8 = fma_probe(torch, stream, cus, 512)
+        probe16 = fma_probe(torch, stream, 4 * cus, 256)
         res["seq_b8_t4096"] = {"ms": ms, "state_updates_per_s": upd / (ms / 1e3),
-                                       "TFLOPs": flops / (ms / 1e3) / 1e12,
-                                       "frac_fp32_vector_nonpacked_78.6": flops / (ms / 1e3) / 78.6e12,
-                                       "frac_fp32_vector_157.3": flops / (ms / 1e3) / 157.3e12}
+                                       "TFLOPs": tf,
+                                       "frac_fp32_vector_nonpacked_78.6": tf / 78.6,
+                                       "frac_fp32_vector_157.3": tf / 157.3,
+                                       "fma_probe_TFLOPs_8_waves_per_cu": probe8,
+                                       "fma_probe_TFLOPs_16_waves_per_cu": probe16,
+                                       "frac_of_fma_probe_same_occupancy": tf / probe8}
 
     # tail_b32: layer tail B=32
     if want("tail_b32"):

@@ -13,7 +13,7 @@ SOURCES = [os.path.join(CSRC, f) for f in
 # Measurement aids (a copy of known size and an in-place read-modify-write with
 # the step kernel's access pattern), built as their own library.
 PROBE_LIBRARY = os.path.join(CSRC, "libgdn_probe.so")
-PROBE_SOURCES = [os.path.join(CSRC, "hbm_probe.hip")]
+PROBE_SOURCES = [os.path.join(CSRC, "probes.hip")]
 ARCH = "gfx950"
 
 # Packed FP32 instructions are switched off for the device code; hipcc's host

@@ -1,11 +1,14 @@
-// hbm_probe.hip - measurement aids, not part of the decode path:
+// probes.hip - measurement aids, not part of the decode path:
 //  - a plain device-to-device copy of known size: the benchmark times it to
 //    report the copy bandwidth this GPU sustains, and hardware-counter runs
 //    use its known byte count to calibrate the FETCH_SIZE / WRITE_SIZE
 //    counters;
 //  - an in-place read-modify-write with the state step's memory pattern and
 //    none of its arithmetic: the rate the step's access pattern alone
-//    reaches, the practical ceiling for the step kernel.
+//    reaches, the practical ceiling for the step kernel;
+//  - a stream of independent non-packed FP32 FMAs with no memory traffic:
+//    the issue rate the VALU sustains at a given number of waves per CU, the
+//    practical ceiling for the multi-token kernel.
 
 #include <hip/hip_runtime.h>
 
@@ -53,6 +56,27 @@ __global__ __launch_bounds__(kProbeWaves * 64) void k_inplace_probe(f4 *buf, int
     }
 }
 
+
+// kFmaChains independent fmaf chains per lane, iterated `iters` times; one
+// float per thread is stored at the end so nothing is optimised away.  Built,
+// like every kernel here, without packed FP32 instructions: each fmaf is one
+// v_fmac_f32 (wave64) instruction.
+constexpr int kFmaChains = 16;
+
+__global__ void k_fma_probe(float *out, int iters, float x, float y) {
+    float acc[kFmaChains];
+#pragma unroll
+    for (int i = 0; i < kFmaChains; ++i) acc[i] = threadIdx.x * 1e-3f + i;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < kFmaChains; ++i) acc[i] = fmaf(acc[i], x, y);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kFmaChains; ++i) s += acc[i];
+    out[static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x] = s;
+}
+
 int device_cus() {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
@@ -92,6 +116,21 @@ int gdn_probe_inplace(void *buf, size_t bytes, unsigned key, void *stream) {
     (void)hipGetLastError();
     k_inplace_probe<<<dim3(grid), dim3(kProbeWaves * 64), 0, static_cast<hipStream_t>(stream)>>>(
         static_cast<f4 *>(buf), tiles, key);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// Runs `workgroups` x `threads` threads (threads a multiple of 64, at most
+// 1024), each doing iters x 16 FP32 FMAs, and writes one float per thread to
+// `out` (device memory holding at least workgroups x threads floats) on
+// `stream`.  Returns 0, -1 on bad arguments, -6 when the launch fails.
+int gdn_probe_fma(float *out, size_t out_floats, int workgroups, int threads, int iters,
+                  void *stream) {
+    if (!out || workgroups < 1 || threads < 64 || threads > 1024 || threads % 64 != 0 ||
+        iters < 1 || out_floats < static_cast<size_t>(workgroups) * static_cast<size_t>(threads))
+        return -1;
+    (void)hipGetLastError();
+    k_fma_probe<<<dim3(workgroups), dim3(threads), 0, static_cast<hipStream_t>(stream)>>>(
+        out, iters, 0.999f, 1e-3f);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

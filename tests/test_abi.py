@@ -269,3 +269,11 @@ def test_probe_library_rejects_bad_arguments():
     assert lib.gdn_probe_inplace(BASE + 8, 4096, 0, None) == -1
     assert lib.gdn_probe_copy(None, BASE, 16, None) == -1
     assert lib.gdn_probe_copy(BASE, BASE + (1 << 20), 20, None) == -1
+    lib.gdn_probe_fma.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_void_p]
+    assert lib.gdn_probe_fma(None, 1 << 20, 256, 512, 10, None) == -1      # no buffer
+    assert lib.gdn_probe_fma(BASE, 1 << 20, 256, 500, 10, None) == -1      # not whole waves
+    assert lib.gdn_probe_fma(BASE, 1 << 20, 256, 2048, 10, None) == -1     # over 1024 threads
+    assert lib.gdn_probe_fma(BASE, 1 << 20, 0, 512, 10, None) == -1        # no workgroup
+    assert lib.gdn_probe_fma(BASE, 1 << 20, 256, 512, 0, None) == -1       # no iteration
+    assert lib.gdn_probe_fma(BASE, 256 * 512 - 1, 256, 512, 10, None) == -1  # buffer too small
