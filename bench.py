@@ -521,7 +521,7 @@ def extra_measurements(torch, g, stream, only=None):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+        print(f"bench.py: measures one GPU only (--gpus {args.gpus} requested); "
               "the decode step has no cross-GPU exchange and shards by sequence", file=sys.stderr)
         sys.exit(2)
     import torch

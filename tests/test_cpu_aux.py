@@ -88,3 +88,13 @@ def test_package_fails_loudly_without_its_library(tmp_path):
     r = subprocess.run([sys.executable, "-c", "import gated_deltanet_decode_amd"],
                        cwd=tmp_path, capture_output=True, text=True, timeout=120)
     assert r.returncode != 0 and "ImportError" in r.stderr and "not built" in r.stderr
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus N > 1 exits with a message before
+    touching a GPU."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
