@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 10100 /* 1.1.0 */
+#define GDN_VERSION 10101 /* 1.1.1 */
 
 #define GDN_OK 0
 #define GDN_ERR_NULL (-1)      /* a required pointer is NULL                  */
