@@ -176,6 +176,11 @@ int gdn_seq(const gdn_dims *dims, int32_t B, int32_t T, const float *q, const fl
     // clear of overflow; no buffer of that many tokens fits a GPU.
     if (T < 1 || T > (1 << 30))
         return fail(GDN_ERR_SHAPE, "T must be in [1, 1073741824] (got %d)", T);
+    // the launch must fit the dispatch's 32-bit work-item count
+    if (static_cast<int64_t>(B) * dims->n_v_heads * gdn::kSeqThreadsPerHead > UINT32_MAX)
+        return fail(GDN_ERR_SHAPE, "gdn_seq: B * n_v_heads = %lld exceeds %lld",
+                    (long long)(static_cast<int64_t>(B) * dims->n_v_heads),
+                    (long long)(UINT32_MAX / gdn::kSeqThreadsPerHead));
     const size_t f = sizeof(float);
     const size_t BT = static_cast<size_t>(B) * T;
     const size_t nqk = BT * dims->n_k_heads * dims->d_k * f;
@@ -311,6 +316,11 @@ int layer_tail(const char *name, const gdn_dims *dims, const gdn_tail_params *pa
     const int64_t C = 2 * static_cast<int64_t>(dims->n_k_heads) * dims->d_k + nvw;
     if (C * B > INT32_MAX / 2)
         return fail(GDN_ERR_SHAPE, "B * channels = %lld too large", (long long)(C * B));
+    // one gated-norm workgroup per sequence and group: its launch must fit the
+    // dispatch's 32-bit work-item count
+    if (static_cast<int64_t>(B) * (nvw / params->norm_group) * gdn::kGatedNormThreads > UINT32_MAX)
+        return fail(GDN_ERR_SHAPE, "B * n_v_heads * d_v / norm_group = %lld groups too many",
+                    (long long)(static_cast<int64_t>(B) * (nvw / params->norm_group)));
 
     const size_t f = sizeof(float);
     const size_t nx = static_cast<size_t>(B) * C * f;

@@ -72,6 +72,14 @@ struct PrestateArgs {
     int32_t n_qk;      // channels of Q plus K (2 * Hk * d_k); these get L2-normalised
 };
 
+// Threads per workgroup of the gated-norm kernel (one workgroup per sequence
+// and group); the API checks that its launch fits the 32-bit dispatch grid.
+constexpr int kGatedNormThreads = 128;
+
+// Work-items of a gdn_seq launch per head (two 256-thread halves or one
+// 512-thread workgroup).
+constexpr int kSeqThreadsPerHead = 512;
+
 struct GatedNormArgs {
     const float *o;
     const float *z;

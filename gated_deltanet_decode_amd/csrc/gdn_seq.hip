@@ -315,6 +315,9 @@ __global__ __launch_bounds__(64 * 8 / PARTS, WPS) void k_seq(SeqArgs a) {
 // - Longer sequences: whole heads, one 8-wave workgroup per head, 32-token
 //   chunks, plain state access, paired reductions.  They are VALU-bound, and
 //   half heads would duplicate the staging (40 % slower at B = 8, T = 4096).
+static_assert(2 * 256 == kSeqThreadsPerHead && 512 == kSeqThreadsPerHead,
+              "the API bounds B * Hv by this launch's work-items per head");
+
 hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
     const int64_t heads = static_cast<int64_t>(a.B) * a.Hv;
     const int64_t cus = device_cus();

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(D) void k_prestate(PrestateArgs a) {
 }
 
 // Gated RMSNorm x SiLU(z) over one group of one row.
-constexpr int kNormThreads = 128;
+constexpr int kNormThreads = kGatedNormThreads;
 __global__ __launch_bounds__(kNormThreads) void k_gated_norm(GatedNormArgs a) {
     __shared__ float scratch[kNormThreads / 64];
     const int groups = a.n / a.group;

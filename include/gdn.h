@@ -25,7 +25,10 @@
  *     Outputs must not overlap any input or state buffer.
  *   - Supported on the GPU path: d_k = d_v = 128, n_k_heads >= 1,
  *     n_v_heads a multiple of n_k_heads, B >= 1, 1 <= T <= 1073741824,
- *     B * n_v_heads <= 134213631.
+ *     B * n_v_heads <= 134213631 (gdn_seq: <= 8388607).  Launches must fit
+ *     the dispatch's 32-bit work-item count; the limits here and in
+ *     gdn_layer_tail guarantee it (a state that large would not fit in
+ *     memory anyway).
  *   - Results are bitwise deterministic for identical inputs, independent of
  *     B and of the other sequences in the batch.  gdn_seq over T tokens is
  *     bitwise equal to T calls of gdn_step.
@@ -158,6 +161,8 @@ int gdn_pair(const gdn_dims *dims, int32_t B,
  *   workspace  device scratch of gdn_layer_tail_workspace_bytes() bytes
  *              (16-byte aligned; may be NULL when both dbg buffers are given;
  *              the single-launch path leaves it untouched)
+ * Size limits (GDN_ERR_SHAPE beyond): B * C <= 1073741823 and
+ * B * n_v_heads * d_v / norm_group <= 33554431 (gated-norm groups).
  */
 int gdn_layer_tail(const gdn_dims *dims, const gdn_tail_params *params, int32_t B,
                    const float *x, const float *conv_w, float *conv_state,

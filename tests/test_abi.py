@@ -105,6 +105,10 @@ def test_seq_validation(g):
     expect(g, f(-1, a), -2, "T")
     expect(g, f((1 << 30) + 1, a), -2, "T")
     expect(g, f(2**31 - 1, a), -2, "T")
+    # 2^23 heads: 512 work-items each would overflow the 32-bit dispatch grid
+    big = lambda Bv: g.lib.gdn_seq(ctypes.byref(d), Bv, 4, a["q"], a["k"], a["v"], a["beta"],
+                                   a["gate"], a["state"], a["out"], None)
+    expect(g, big((1 << 23) // HV), -2, "gdn_seq: B * n_v_heads")
     expect(g, f(4, dict(a, gate=None)), -1, "gate")
     expect(g, f(4, dict(a, v=a["v"] + 4)), -3, "v")
     expect(g, f(1, dict(a, out=a["state"] - 16)), -4, "out")
@@ -155,6 +159,9 @@ def test_tail_validation(g):
     expect(g, f(pp=g.TailParams(4, 128, -1.0)), -2, "norm_eps")
     expect(g, f(pp=g.TailParams(4, 128, float("nan"))), -2, "norm_eps")
     expect(g, f(Bv=0), -2, "B")
+    # one-element groups at B = 8193: 8193 * 4096 gated-norm workgroups of 128
+    # threads would overflow the 32-bit dispatch grid
+    expect(g, f(pp=g.TailParams(4, 1, 1e-6), Bv=8193), -2, "groups too many")
     expect(g, f(ws_bytes=need - 4), -5, "workspace")
     expect(g, f(ws=None), -5, "workspace")
     expect(g, f(cs=base["cs"] + 4), -3, "conv_state")
