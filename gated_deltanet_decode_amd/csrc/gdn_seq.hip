@@ -315,7 +315,13 @@ __global__ __launch_bounds__(64 * 8 / PARTS, WPS) void k_seq(SeqArgs a) {
 // - Longer sequences: whole heads, one 8-wave workgroup per head, 32-token
 //   chunks, plain state access, paired reductions.  They are VALU-bound, and
 //   half heads would duplicate the staging (40 % slower at B = 8, T = 4096).
-static_assert(2 * 256 == kSeqThreadsPerHead && 512 == kSeqThreadsPerHead,
+//   With fewer heads than CUs, though, whole heads leave CUs idle: a head
+//   is then split over 8, 4 or 2 workgroups (of 1, 2 or 4 waves; 16-token
+//   chunks for the one-wave parts) while that still fits the CUs, 16-20 %
+//   faster at B = 1, 2, 4 (e.g. 1.74 -> 1.39 ms at B = 1, T = 4096).  Below
+//   65 tokens the split measured no better than the routes above.
+static_assert(8 * 64 == kSeqThreadsPerHead && 4 * 128 == kSeqThreadsPerHead &&
+                  2 * 256 == kSeqThreadsPerHead && 512 == kSeqThreadsPerHead,
               "the API bounds B * Hv by this launch's work-items per head");
 
 hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
@@ -332,6 +338,12 @@ hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
             k_seq<16, true, true, 2, 1><<<split, dim3(256), 0, s>>>(a);
         else
             k_seq<16, true, false, 2, 3><<<split, dim3(256), 0, s>>>(a);
+    } else if (8 * heads <= cus) {
+        k_seq<16, false, true, 8, 1><<<dim3(static_cast<unsigned>(heads * 8)), dim3(64), 0, s>>>(a);
+    } else if (4 * heads <= cus) {
+        k_seq<32, false, true, 4, 1><<<dim3(static_cast<unsigned>(heads * 4)), dim3(128), 0, s>>>(a);
+    } else if (2 * heads <= cus) {
+        k_seq<32, false, true, 2, 1><<<split, dim3(256), 0, s>>>(a);
     } else {
         k_seq<32, false, true, 1, 1><<<whole, dim3(512), 0, s>>>(a);
     }
