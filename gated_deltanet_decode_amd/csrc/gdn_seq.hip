@@ -165,48 +165,50 @@ __device__ __forceinline__ void select_row(RowSlice &dst, bool s, const RowSlice
 // with one set of DPP adds, each lane computes the delta of its slot-0 row
 // only and takes the other row's from its mirror lane, and writes one output.
 // Otherwise each slot is reduced on its own.  Both give the same bits.
-template <bool kPair>
-__device__ __forceinline__ void seq_token(TokenLds *buf, int tt, bool next, const int (&rows)[2],
-                                          RowSlice (&r)[2], VecSlice &kv, float (&p)[2], int c) {
+template <bool kPair, int TPW>
+__device__ __forceinline__ void seq_token(TokenLds *buf, int tt, bool next, const int (&rows)[TPW],
+                                          RowSlice (&r)[TPW], VecSlice &kv, float (&p)[TPW],
+                                          int c) {
+    static_assert(!kPair || TPW == 2, "pairing needs two tiles per wave");
     TokenLds &tok = buf[tt];
-    float d[2];                                                // step 3
-    if (kPair) {
+    float d[TPW];                                              // step 3
+    if constexpr (kPair) {
         d[0] = (tok.v[rows[0]] - pair_sum(p[0], p[1])) * tok.beta;
         d[1] = dpp_mov<0x141>(d[0]);                           // from lane 7-c: the other row
     } else {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) d[t] = (tok.v[rows[t]] - group_sum(p[t])) * tok.beta;
+        for (int t = 0; t < TPW; ++t) d[t] = (tok.v[rows[t]] - group_sum(p[t])) * tok.beta;
     }
     VecSlice qv;
     load_vec(qv, tok.q, c);
-    float o[2];
+    float o[TPW];
     if (next) {
         VecSlice kn;
         load_vec(kn, buf[tt + 1].k, c);
         const float en = buf[tt + 1].e;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) pass(r[t], d[t], kv, qv, en, kn, o[t], p[t]);
+        for (int t = 0; t < TPW; ++t) pass(r[t], d[t], kv, qv, en, kn, o[t], p[t]);
         kv = kn;
     } else {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) o[t] = body_part(r[t], d[t], kv, qv);
+        for (int t = 0; t < TPW; ++t) o[t] = body_part(r[t], d[t], kv, qv);
     }
     // every lane holding a row in a written slot has the same output bits
-    if (kPair) {
+    if constexpr (kPair) {
         tok.v[rows[0]] = pair_sum(o[0], o[1]) * kInvSqrtD;
     } else {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) tok.v[rows[t]] = group_sum(o[t]) * kInvSqrtD;
+        for (int t = 0; t < TPW; ++t) tok.v[rows[t]] = group_sum(o[t]) * kInvSqrtD;
     }
 }
 
 // CH: tokens per LDS chunk; NT: nontemporal state load and store; PAIR:
 // paired row reductions (seq_token); a head's 128 rows are split over PARTS
-// workgroups of 8 / PARTS waves with two tiles each; WPS: waves per SIMD the
-// register allocation must allow (3 caps it at 168 VGPRs).
-template <int CH, bool NT, bool PAIR, int PARTS, int WPS>
-__global__ __launch_bounds__(64 * 8 / PARTS, WPS) void k_seq(SeqArgs a) {
-    constexpr int NTH = 64 * 8 / PARTS;
+// workgroups of 16 / (TPW * PARTS) waves with TPW tiles each; WPS: waves per
+// SIMD the register allocation must allow (3 caps it at 168 VGPRs).
+template <int CH, bool NT, bool PAIR, int PARTS, int WPS, int TPW = 2>
+__global__ __launch_bounds__(64 * 16 / (TPW * PARTS), WPS) void k_seq(SeqArgs a) {
+    constexpr int NTH = 64 * 16 / (TPW * PARTS);
     constexpr int R = D / PARTS;                  // rows of this workgroup
     __shared__ TokenLds lds[2][CH];
 
@@ -227,9 +229,9 @@ __global__ __launch_bounds__(64 * 8 / PARTS, WPS) void k_seq(SeqArgs a) {
     // lines per instruction); with PAIR, lanes 4-7 of each row group swap
     // the two slots in registers, as seq_token() expects.  rows[] is per slot.
     const bool swap = PAIR && c >= 4;
-    int tile_row[2], rows[2];
-    RowSlice r[2];
-    {
+    int tile_row[TPW], rows[TPW];
+    RowSlice r[TPW];
+    if constexpr (TPW == 2) {
         RowSlice m[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -240,6 +242,13 @@ __global__ __launch_bounds__(64 * 8 / PARTS, WPS) void k_seq(SeqArgs a) {
         for (int t = 0; t < 2; ++t) {
             rows[t] = swap ? tile_row[t ^ 1] : tile_row[t];
             select_row(r[t], swap, m[t ^ 1], m[t]);
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            tile_row[t] = part * R + (wave * TPW + t) * kRowsPerTile + grp;
+            rows[t] = tile_row[t];
+            load_row<NT>(r[t], M + tile_row[t] * D, c);
         }
     }
 
@@ -260,18 +269,18 @@ __global__ __launch_bounds__(64 * 8 / PARTS, WPS) void k_seq(SeqArgs a) {
         // steps 1-2 of the chunk's first token
         VecSlice kv;
         load_vec(kv, buf[0].k, c);
-        float p[2];
+        float p[TPW];
         {
             const float e0 = buf[0].e;
 #pragma unroll
-            for (int t = 0; t < 2; ++t) p[t] = head_part(r[t], kv, e0);
+            for (int t = 0; t < TPW; ++t) p[t] = head_part(r[t], kv, e0);
         }
         if (nt == CH) {
             // full chunk: unrolled, so every LDS address is an immediate offset
 #pragma unroll
-            for (int tt = 0; tt < CH; ++tt) seq_token<PAIR>(buf, tt, tt + 1 < CH, rows, r, kv, p, c);
+            for (int tt = 0; tt < CH; ++tt) seq_token<PAIR, TPW>(buf, tt, tt + 1 < CH, rows, r, kv, p, c);
         } else {
-            for (int tt = 0; tt < nt; ++tt) seq_token<PAIR>(buf, tt, tt + 1 < nt, rows, r, kv, p, c);
+            for (int tt = 0; tt < nt; ++tt) seq_token<PAIR, TPW>(buf, tt, tt + 1 < nt, rows, r, kv, p, c);
         }
         __syncthreads();                 // outputs of chunk ch complete in LDS
 
@@ -288,11 +297,16 @@ __global__ __launch_bounds__(64 * 8 / PARTS, WPS) void k_seq(SeqArgs a) {
         if (more) seq_stage(lds[(ch + 1) & 1], cr, tid);
         __syncthreads();                 // chunk ch+1 staged; chunk ch flushed
     }
+    if constexpr (TPW == 2) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        RowSlice m;
-        select_row(m, swap, r[t ^ 1], r[t]);
-        store_row<NT>(M + tile_row[t] * D, m, c);
+        for (int t = 0; t < 2; ++t) {
+            RowSlice m;
+            select_row(m, swap, r[t ^ 1], r[t]);
+            store_row<NT>(M + tile_row[t] * D, m, c);
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) store_row<NT>(M + tile_row[t] * D, r[t], c);
     }
 }
 
@@ -316,12 +330,17 @@ __global__ __launch_bounds__(64 * 8 / PARTS, WPS) void k_seq(SeqArgs a) {
 //   chunks, plain state access, paired reductions.  They are VALU-bound, and
 //   half heads would duplicate the staging (40 % slower at B = 8, T = 4096).
 //   With fewer heads than CUs, though, whole heads leave CUs idle: a head
-//   is then split over 8, 4 or 2 workgroups (of 1, 2 or 4 waves; 16-token
-//   chunks for the one-wave parts) while that still fits the CUs, 16-20 %
-//   faster at B = 1, 2, 4 (e.g. 1.74 -> 1.39 ms at B = 1, T = 4096).  Below
-//   65 tokens the split measured no better than the routes above.
-static_assert(8 * 64 == kSeqThreadsPerHead && 4 * 128 == kSeqThreadsPerHead &&
-                  2 * 256 == kSeqThreadsPerHead && 512 == kSeqThreadsPerHead,
+//   is then split over 4 or 2 workgroups (of 2 or 4 waves) while that still
+//   fits the CUs, 16-20 % faster at B = 2, 4 (1.84 -> 1.47 ms at B = 4,
+//   T = 4096).  Up to CUs / 8 heads (B = 1) each of 16 one-wave workgroups
+//   takes a single tile (unpaired, 16-token chunks): a lone wave on its SIMD
+//   issues one instruction per 4 cycles, so halving its rows nearly halves
+//   its instruction stream (1.74 -> 1.07 ms at B = 1, T = 4096; with two
+//   tiles per wave, 1.39 ms).  More than two such one-wave workgroups per CU
+//   measured 50-120 % slower.  Below 65 tokens the splits measured no better
+//   than the routes above.
+static_assert(4 * 128 == kSeqThreadsPerHead && 2 * 256 == kSeqThreadsPerHead &&
+                  512 == kSeqThreadsPerHead,
               "the API bounds B * Hv by this launch's work-items per head");
 
 hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
@@ -339,7 +358,9 @@ hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
         else
             k_seq<16, true, false, 2, 3><<<split, dim3(256), 0, s>>>(a);
     } else if (8 * heads <= cus) {
-        k_seq<16, false, true, 8, 1><<<dim3(static_cast<unsigned>(heads * 8)), dim3(64), 0, s>>>(a);
+        // 16 one-wave parts of one tile each (1024 work-items per head; taken
+        // only for heads <= CUs / 8)
+        k_seq<16, false, false, 16, 1, 1><<<dim3(static_cast<unsigned>(heads * 16)), dim3(64), 0, s>>>(a);
     } else if (4 * heads <= cus) {
         k_seq<32, false, true, 4, 1><<<dim3(static_cast<unsigned>(heads * 4)), dim3(128), 0, s>>>(a);
     } else if (2 * heads <= cus) {
