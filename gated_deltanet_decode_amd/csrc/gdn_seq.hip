@@ -329,18 +329,20 @@ __global__ __launch_bounds__(64 * 16 / (TPW * PARTS), WPS) void k_seq(SeqArgs a)
 // - Longer sequences: whole heads, one 8-wave workgroup per head, 32-token
 //   chunks, plain state access, paired reductions.  They are VALU-bound, and
 //   half heads would duplicate the staging (40 % slower at B = 8, T = 4096).
-//   With fewer heads than CUs, though, whole heads leave CUs idle: a head
-//   is then split over 4 or 2 workgroups (of 2 or 4 waves) while that still
-//   fits the CUs, 16-20 % faster at B = 2, 4 (1.84 -> 1.47 ms at B = 4,
-//   T = 4096).  Up to CUs / 8 heads (B = 1) each of 16 one-wave workgroups
-//   takes a single tile (unpaired, 16-token chunks): a lone wave on its SIMD
-//   issues one instruction per 4 cycles, so halving its rows nearly halves
-//   its instruction stream (1.74 -> 1.07 ms at B = 1, T = 4096; with two
-//   tiles per wave, 1.39 ms).  More than two such one-wave workgroups per CU
-//   measured 50-120 % slower.  Below 65 tokens the splits measured no better
-//   than the routes above.
-static_assert(4 * 128 == kSeqThreadsPerHead && 2 * 256 == kSeqThreadsPerHead &&
-                  512 == kSeqThreadsPerHead,
+//   With fewer heads than CUs, though, whole heads leave CUs idle, and a
+//   head is split while the parts still fit the CUs:
+//   - up to CUs / 8 heads (B = 1): 16 one-wave workgroups of one tile each
+//     (unpaired, 16-token chunks).  A lone wave on its SIMD issues one
+//     instruction per 4 cycles, so halving its rows nearly halves its
+//     instruction stream: 1.74 -> 1.07 ms at B = 1, T = 4096 (1.39 ms with
+//     two tiles per wave);
+//   - up to CUs / 4 heads (B = 2): 8 two-wave workgroups, one tile per wave:
+//     1.76 -> 1.21 ms at T = 4096 (1.40 ms with 4 parts of two tiles);
+//   - up to CUs / 2 heads (B = 3, 4): 2 parts of four two-tile waves (paired,
+//     32-token chunks): 1.84 -> 1.47 ms at B = 4, T = 4096; one-tile parts
+//     there measured 20 % slower.
+//   Below 65 tokens the splits measured no better than the routes above.
+static_assert(2 * 256 == kSeqThreadsPerHead && 512 == kSeqThreadsPerHead,
               "the API bounds B * Hv by this launch's work-items per head");
 
 hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
@@ -362,7 +364,9 @@ hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
         // only for heads <= CUs / 8)
         k_seq<16, false, false, 16, 1, 1><<<dim3(static_cast<unsigned>(heads * 16)), dim3(64), 0, s>>>(a);
     } else if (4 * heads <= cus) {
-        k_seq<32, false, true, 4, 1><<<dim3(static_cast<unsigned>(heads * 4)), dim3(128), 0, s>>>(a);
+        // 8 two-wave parts of one tile per wave (1024 work-items per head;
+        // heads <= CUs / 4)
+        k_seq<16, false, false, 8, 1, 1><<<dim3(static_cast<unsigned>(heads * 8)), dim3(128), 0, s>>>(a);
     } else if (2 * heads <= cus) {
         k_seq<32, false, true, 2, 1><<<split, dim3(256), 0, s>>>(a);
     } else {

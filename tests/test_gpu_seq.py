@@ -41,9 +41,9 @@ def token(si, t):
 # kernel); T < 16 (half heads, 8-token chunks, full and partial) with paired
 # reductions up to 256 heads and unpaired beyond (B = 12: 384 heads);
 # 16 <= T <= 64 (half heads, 16-token chunks) paired up to 512 heads and
-# unpaired beyond (B = 24: 768 heads); beyond 64 tokens, heads split over 8,
-# 4 or 2 workgroups while they fit the CUs (B = 1, 2, 3) and whole heads
-# (B = 8).
+# unpaired beyond (B = 24: 768 heads); beyond 64 tokens, heads split over 16
+# one-tile waves (B = 1), 8 parts of two one-tile waves (B = 2) or 2 parts
+# (B = 3) while they fit the CUs, and whole heads (B = 8).
 @pytest.mark.parametrize("B,T,Hv,Hk", [(1, 1, 32, 16), (2, 5, 32, 16), (2, 8, 32, 16),
                                        (1, 17, 32, 16), (1, 24, 32, 16), (2, 32, 32, 16),
                                        (3, 33, 4, 2), (2, 16, 1, 1), (1, 48, 64, 16),
@@ -68,7 +68,7 @@ def test_seq_matches_oracle(g, orc, B, T, Hv, Hk):
 def test_seq_is_bitwise_repeated_step(g, B, T):
     """T tokens in one gdn_seq == T gdn_step calls, bit for bit (both paths
     share the per-row arithmetic), for every route: half heads with 8- and
-    16-token chunks, paired and unpaired, heads split in 8, 4 or 2 parts, and
+    16-token chunks, paired and unpaired, heads split in 16, 8 or 2 parts, and
     whole heads."""
     import torch
     print(f"\n  gdn_seq == repeated gdn_step, B={B} T={T}", flush=True)
