@@ -54,11 +54,30 @@ def seq_mt(o: oracle.Oracle, si: dict, M: np.ndarray, threads: int = THREADS) ->
 
 
 def max_err(got, want):
+    """(max absolute error, max relative error); NaN or Inf anywhere gives
+    inf, so that max() over several results cannot drop it."""
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
     d = np.abs(got - want)
     rel = d / np.maximum(np.abs(want), 1e-30)
-    return float(d.max(initial=0.0)), float(rel.max(initial=0.0))
+    a, r = float(d.max(initial=0.0)), float(rel.max(initial=0.0))
+    return (a if np.isfinite(a) else np.inf), (r if np.isfinite(r) else np.inf)
+
+
+def max_abs_err(got, want, chunk=1 << 24):
+    """Max |got - want| over large float32 arrays, in chunks and in float32
+    (the difference of two binary32 values within a factor 2 of each other is
+    exact); NaN or Inf anywhere gives inf."""
+    g = np.asarray(got).reshape(-1)
+    w = np.asarray(want).reshape(-1)
+    assert g.shape == w.shape
+    worst = 0.0
+    for i in range(0, g.size, chunk):
+        m = float(np.max(np.abs(g[i:i + chunk] - w[i:i + chunk]), initial=0.0))
+        if not np.isfinite(m):
+            return np.inf
+        worst = max(worst, m)
+    return worst
 
 
 def assert_close(name, got, want, atol):
