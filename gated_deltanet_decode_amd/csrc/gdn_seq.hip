@@ -225,9 +225,11 @@ __global__ __launch_bounds__(64 * 16 / (TPW * PARTS), WPS) void k_seq(SeqArgs a)
     const int kh = h % a.Hk;
 
     float *M = a.state + static_cast<int64_t>(head) * (D * D);
-    // The wave's two tiles.  The state moves in tile order (whole 128-byte
+    // The wave's TPW tiles.  The state moves in tile order (whole 128-byte
     // lines per instruction); with PAIR, lanes 4-7 of each row group swap
     // the two slots in registers, as seq_token() expects.  rows[] is per slot.
+    // (Two-tile kernels keep the swap path even unpaired, where it swaps
+    // nothing: the code it compiles to is the measured one.)
     const bool swap = PAIR && c >= 4;
     int tile_row[TPW], rows[TPW];
     RowSlice r[TPW];
