@@ -316,6 +316,13 @@ __global__ __launch_bounds__(64 * 16 / (TPW * PARTS), WPS) void k_seq(SeqArgs a)
 
 // Launch shape (measured on MI355X, 256 CUs, 32 heads):
 // - T = 1 runs the single-step kernel (in gdn_api.cpp).
+// - At most CUs / 4 heads (B <= 2), any T: heads split into one-tile waves,
+//   16 one-wave workgroups per head (B = 1) or 8 of two waves (B = 2), so a
+//   wave's instruction stream per token is short; 8-token chunks with
+//   nontemporal state access below 16 tokens, 16-token chunks and plain
+//   access from there.  Against the half-head routes below, device time
+//   per call (graph replays): B = 1 T = 2 4.44 -> 4.17 us, T = 8 6.26 ->
+//   5.06, T = 15 9.42 -> 7.84, T = 64 24.7 -> 19.2; B = 2 7-17 % faster.
 // - T <= 64: half heads (two workgroups of 4 waves, 64 rows each, per head),
 //   so that several share a CU and one's state transfer overlaps the
 //   others' arithmetic; nontemporal state access; 8-token chunks below 16
@@ -333,17 +340,15 @@ __global__ __launch_bounds__(64 * 16 / (TPW * PARTS), WPS) void k_seq(SeqArgs a)
 //   half heads would duplicate the staging (40 % slower at B = 8, T = 4096).
 //   With fewer heads than CUs, though, whole heads leave CUs idle, and a
 //   head is split while the parts still fit the CUs:
-//   - up to CUs / 8 heads (B = 1): 16 one-wave workgroups of one tile each
-//     (unpaired, 16-token chunks).  A lone wave on its SIMD issues one
-//     instruction per 4 cycles, so halving its rows nearly halves its
+//   - B = 1, 2: the one-tile splits above.  A lone wave on its SIMD issues
+//     one instruction per 4 cycles, so halving its rows nearly halves its
 //     instruction stream: 1.74 -> 1.07 ms at B = 1, T = 4096 (1.39 ms with
-//     two tiles per wave);
-//   - up to CUs / 4 heads (B = 2): 8 two-wave workgroups, one tile per wave:
-//     1.76 -> 1.21 ms at T = 4096 (1.40 ms with 4 parts of two tiles);
+//     two tiles per wave); 1.76 -> 1.21 ms at B = 2 (1.40 ms with 4 parts of
+//     two tiles);
 //   - up to CUs / 2 heads (B = 3, 4): 2 parts of four two-tile waves (paired,
 //     32-token chunks): 1.84 -> 1.47 ms at B = 4, T = 4096; one-tile parts
-//     there measured 20 % slower.
-//   Below 65 tokens the splits measured no better than the routes above.
+//     there measured 20 % slower, and two-tile splits no better than the
+//     half-head routes below 65 tokens.
 static_assert(2 * 256 == kSeqThreadsPerHead && 512 == kSeqThreadsPerHead,
               "the API bounds B * Hv by this launch's work-items per head");
 
@@ -351,7 +356,23 @@ hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
     const int64_t heads = static_cast<int64_t>(a.B) * a.Hv;
     const int64_t cus = device_cus();
     const dim3 split(static_cast<unsigned>(heads * 2)), whole(static_cast<unsigned>(heads));
-    if (a.T < 16) {
+    if (8 * heads <= cus) {
+        // 16 one-wave parts of one tile each (1024 work-items per head; taken
+        // only for heads <= CUs / 8)
+        const dim3 grid(static_cast<unsigned>(heads * 16)), block(64);
+        if (a.T < 16)
+            k_seq<8, true, false, 16, 1, 1><<<grid, block, 0, s>>>(a);
+        else
+            k_seq<16, false, false, 16, 1, 1><<<grid, block, 0, s>>>(a);
+    } else if (4 * heads <= cus) {
+        // 8 two-wave parts of one tile per wave (1024 work-items per head;
+        // heads <= CUs / 4)
+        const dim3 grid(static_cast<unsigned>(heads * 8)), block(128);
+        if (a.T < 16)
+            k_seq<8, true, false, 8, 1, 1><<<grid, block, 0, s>>>(a);
+        else
+            k_seq<16, false, false, 8, 1, 1><<<grid, block, 0, s>>>(a);
+    } else if (a.T < 16) {
         if (heads <= cus)
             k_seq<8, true, true, 2, 1><<<split, dim3(256), 0, s>>>(a);
         else
@@ -361,14 +382,6 @@ hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
             k_seq<16, true, true, 2, 1><<<split, dim3(256), 0, s>>>(a);
         else
             k_seq<16, true, false, 2, 3><<<split, dim3(256), 0, s>>>(a);
-    } else if (8 * heads <= cus) {
-        // 16 one-wave parts of one tile each (1024 work-items per head; taken
-        // only for heads <= CUs / 8)
-        k_seq<16, false, false, 16, 1, 1><<<dim3(static_cast<unsigned>(heads * 16)), dim3(64), 0, s>>>(a);
-    } else if (4 * heads <= cus) {
-        // 8 two-wave parts of one tile per wave (1024 work-items per head;
-        // heads <= CUs / 4)
-        k_seq<16, false, false, 8, 1, 1><<<dim3(static_cast<unsigned>(heads * 8)), dim3(128), 0, s>>>(a);
     } else if (2 * heads <= cus) {
         k_seq<32, false, true, 2, 1><<<split, dim3(256), 0, s>>>(a);
     } else {

@@ -38,18 +38,21 @@ def token(si, t):
 
 
 # B, T cover every route on a 256-CU MI355X: T = 1 (the single-step
-# kernel); T < 16 (half heads, 8-token chunks, full and partial) with paired
-# reductions up to 256 heads and unpaired beyond (B = 12: 384 heads);
-# 16 <= T <= 64 (half heads, 16-token chunks) paired up to 512 heads and
-# unpaired beyond (B = 24: 768 heads); beyond 64 tokens, heads split over 16
-# one-tile waves (B = 1), 8 parts of two one-tile waves (B = 2) or 2 parts
-# (B = 3) while they fit the CUs, and whole heads (B = 8).
+# kernel); up to 64 heads (B = 1, 2), heads split into 16 one-wave or 8
+# two-wave workgroups of one tile per wave, with 8-token chunks below 16
+# tokens and 16-token chunks from there; otherwise T < 16 (half heads,
+# 8-token chunks, full and partial) paired up to 256 heads (B = 4, 8) and
+# unpaired beyond (B = 12: 384 heads); 16 <= T <= 64 (half heads, 16-token
+# chunks) paired up to 512 heads (B = 8) and unpaired beyond (B = 24: 768
+# heads); beyond 64 tokens, 2 parts per head while they fit the CUs (B = 3)
+# and whole heads (B = 8).
 @pytest.mark.parametrize("B,T,Hv,Hk", [(1, 1, 32, 16), (2, 5, 32, 16), (2, 8, 32, 16),
                                        (1, 17, 32, 16), (1, 24, 32, 16), (2, 32, 32, 16),
                                        (3, 33, 4, 2), (2, 16, 1, 1), (1, 48, 64, 16),
                                        (1, 64, 32, 16), (2, 65, 32, 16), (8, 24, 32, 16),
                                        (12, 9, 32, 16), (24, 20, 32, 16), (1, 70, 32, 16),
-                                       (3, 70, 32, 16), (8, 66, 32, 16)])
+                                       (3, 70, 32, 16), (8, 66, 32, 16), (1, 7, 32, 16),
+                                       (4, 5, 32, 16), (8, 40, 32, 16)])
 def test_seq_matches_oracle(g, orc, B, T, Hv, Hk):
     print(f"\n  gdn_seq B={B} T={T} Hv={Hv} Hk={Hk}", flush=True)
     si = gi.step_inputs(3000 + T, 0, B, Hv, Hk, T=T)
@@ -64,7 +67,8 @@ def test_seq_matches_oracle(g, orc, B, T, Hv, Hk):
 
 
 @pytest.mark.parametrize("B,T", [(2, 2), (2, 8), (2, 15), (2, 24), (2, 32), (2, 37), (2, 65),
-                                 (12, 9), (24, 20), (1, 70), (3, 70), (8, 66)])
+                                 (12, 9), (24, 20), (1, 70), (3, 70), (8, 66), (1, 9), (1, 24),
+                                 (4, 8), (8, 32)])
 def test_seq_is_bitwise_repeated_step(g, B, T):
     """T tokens in one gdn_seq == T gdn_step calls, bit for bit (both paths
     share the per-row arithmetic), for every route: half heads with 8- and
