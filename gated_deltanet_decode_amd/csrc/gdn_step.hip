@@ -141,20 +141,25 @@ __global__ __launch_bounds__(W * 64) void k_step(StepArgs a, int n_tiles, int ep
 // this kernel keeps q with the other loads and computes its tile indices
 // afresh each pass: with one read and two writes per row, fetching q late
 // measured 7 % slower and the incremental walk 1 % slower on MI355X.  W:
-// waves per workgroup, as in k_step (1 for small launches).
+// waves per workgroup, as in k_step (1 for small launches).  Workgroups are
+// grouped in epochs of GE as in k_step's walk: epoch e walks tiles
+// [e * span, (e + 1) * span), span = GE * W * iters.
 template <int W>
-__global__ __launch_bounds__(W * 64) void k_pair(PairArgs a, int n_tiles) {
+__global__ __launch_bounds__(W * 64) void k_pair(PairArgs a, int n_tiles, int GE, int iters) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int grp = lane >> 3;
     const int c = lane & 7;
 
-    const int G = gridDim.x;
-    const int g = blockIdx.x;
-    const int lg = (G % kXcds == 0) ? (g % kXcds) * (G / kXcds) + g / kXcds : g;
-    const int stride = G * W;
+    const int epoch = blockIdx.x / GE;
+    const int g = blockIdx.x - epoch * GE;
+    const int lg = (GE % kXcds == 0) ? (g % kXcds) * (GE / kXcds) + g / kXcds : g;
+    const int stride = GE * W;
+    const int span = stride * iters;
+    const int base = epoch * span;
+    const int end = n_tiles - base < span ? n_tiles : base + span;
 
-    for (int u = lg * W + wave; u < n_tiles; u += stride) {
+    for (int u = base + lg * W + wave; u < end; u += stride) {
         const int head = u / kTilesPerHead;
         const int row = (u % kTilesPerHead) * kRowsPerTile + grp;
         const int b = head / a.Hv;
@@ -242,17 +247,34 @@ hipError_t launch_step(const StepArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The pair kernel runs its persistent walk in epochs of kEpochIters passes
+// at every size (one epoch, the plain walk, when it has at most that many
+// passes): measured per 256 sequences, 257 against 265-271 us at B = 256,
+// 255 against 285-295 us at B = 512..2048, and 6-7 % faster at B = 64, 128.
+// Its read-once-write-twice traffic gains from the epochs' tighter window
+// where the step's read-once-write-once traffic does not (at B <= 256).
 hipError_t launch_pair(const PairArgs &a, hipStream_t s) {
     const int64_t tiles = static_cast<int64_t>(a.B) * a.Hv * kTilesPerHead;
+    const int nt = static_cast<int>(tiles);
     if (tiles <= kPairOneShotTiles) {
-        k_pair<1><<<dim3(static_cast<unsigned>(tiles)), dim3(64), 0, s>>>(a, static_cast<int>(tiles));
+        k_pair<1><<<dim3(static_cast<unsigned>(tiles)), dim3(64), 0, s>>>(a, nt, nt, 1);
         return hipGetLastError();
     }
     int64_t full = device_cus() * static_cast<int64_t>(GDN_STEP_WGS_PER_CU);
     if (full > kMaxGrid) full = kMaxGrid;
     const int64_t need = (tiles + kStepWaves - 1) / kStepWaves;
     const int grid = static_cast<int>(need < full ? need : full);
-    k_pair<kStepWaves><<<dim3(grid), dim3(kStepWaves * 64), 0, s>>>(a, static_cast<int>(tiles));
+    const int64_t span = static_cast<int64_t>(grid) * kStepWaves * kEpochIters;
+    const int64_t epochs = (tiles + span - 1) / span;
+    if (epochs > 1 && grid * epochs <= kMaxEpochWgs) {
+        k_pair<kStepWaves><<<dim3(static_cast<unsigned>(grid * epochs)), dim3(kStepWaves * 64),
+                             kEpochLdsBytes, s>>>(a, nt, grid, kEpochIters);
+    } else {
+        const int64_t passes = (tiles + static_cast<int64_t>(grid) * kStepWaves - 1) /
+                               (static_cast<int64_t>(grid) * kStepWaves);
+        k_pair<kStepWaves><<<dim3(grid), dim3(kStepWaves * 64), 0, s>>>(
+            a, nt, grid, static_cast<int>(passes));
+    }
     return hipGetLastError();
 }
 

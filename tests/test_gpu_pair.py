@@ -34,7 +34,10 @@ def run_pair(g, si, M):
     return Md.cpu().numpy(), Mn.cpu().numpy(), out.cpu().numpy()
 
 
-@pytest.mark.parametrize("B,Hv,Hk", [(1, 32, 16), (3, 32, 16), (2, 4, 2), (64, 32, 16)])
+# B = 1, 3: one wave per tile; B = 5: one epoch of the walk; B = 64: four
+# epochs; B = 70 x 33 heads: 36,960 tiles in 5 epochs, the last ragged.
+@pytest.mark.parametrize("B,Hv,Hk", [(1, 32, 16), (3, 32, 16), (2, 4, 2), (5, 32, 16),
+                                     (64, 32, 16), (70, 33, 11)])
 def test_pair_matches_oracle(g, orc, B, Hv, Hk):
     print(f"\n  gdn_pair B={B} Hv={Hv} Hk={Hk}", flush=True)
     si = gi.step_inputs(5000 + B, 0, B, Hv, Hk, T=2)
