@@ -461,7 +461,10 @@ def extra_measurements(torch, g, stream, only=None):
         ms = timeit(lambda: g.seq(si["q"], si["k"], si["v"], si["beta"], si["gate"], M, o,
                                   stream=stream), 5)
         upd = 8 * 4096 * HV
-        flops = upd * D * D * 7  # decay mul + 3 FMA per element
+        # 6 flop per state element: the rank-1 update and the two dot
+        # products (three FMA); the decay multiplies a per-group scale
+        # instead of every element (7 with the per-element multiply)
+        flops = upd * D * D * 6
         tf = flops / (ms / 1e3) / 1e12
         # the VALU ceiling measured at the kernel's own occupancy (one 8-wave
         # workgroup per CU, as this launch) and at 16 waves per CU

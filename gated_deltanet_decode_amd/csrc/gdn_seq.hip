@@ -14,7 +14,8 @@ namespace {
 // freely; each part stages the head's k and q and flushes only its own rows'
 // outputs.
 //
-// The per-token inputs (k, q, v, exp(gate), beta: 1.5 KiB per token) are
+// The per-token inputs (k, q, v, exp(gate), beta, and for the scaled decay
+// below two per-token factors: 1.5 KiB per token) are
 // staged through LDS in chunks of CH tokens (8, 16 or 32 by sequence length),
 // double-buffered (97 KiB of LDS for CH = 32; gfx950 allows 160 KiB per
 // workgroup): the global loads of chunk c+1 are issued before chunk c is
@@ -33,7 +34,8 @@ namespace {
 // per token and lane that is 3 DPP adds for both key sums and 3 for both
 // outputs, one delta and one output, instead of 6 + 6, two and two.
 // Long sequences are VALU-issue bound (measured: VALU instructions issue
-// 81-96 % of the time), so every instruction per token counts.
+// 81-96 % of the time), so every instruction per token counts: 16- and
+// 32-token chunks also carry the decay as a scale (scaled decay, below).
 
 struct alignas(16) TokenLds {
     float k[D];
@@ -41,7 +43,8 @@ struct alignas(16) TokenLds {
     float v[D];       // v on entry; the token's output once computed
     float e;          // exp(gate)
     float beta;
-    float pad[2];
+    float w;          // scaled decay: beta / c_t
+    float os;         // scaled decay: c_t / sqrt(d)
 };
 static_assert(sizeof(TokenLds) % 16 == 0, "float4 aligned token slots");
 
@@ -62,14 +65,15 @@ struct Chunk {
 template <int CH, int NTH>
 struct ChunkRegs {
     f4 f[Chunk<CH, NTH>::kFetchPer];   // k slots, then q, then v
-    float s;   // gate or beta of one token (threads 0 .. 2*CH-1)
+    float s;    // gate or beta of one token (threads 0 .. 2*CH-1); with the
+    float s2;   // scaled decay, thread t < CH holds token t's gate and beta
 };
 
 // kClamp: the chunk may run past token T - 1 (only a sequence's last chunk
 // can); slots past the end load token T - 1 again, which nothing reads (a
 // partial chunk computes, flushes and takes the next key of its first nt
 // tokens only).  Every load is unconditional and in bounds.
-template <int CH, int NTH, bool kClamp>
+template <int CH, int NTH, bool kClamp, bool SC>
 __device__ __forceinline__ void seq_fetch(ChunkRegs<CH, NTH> &cr, const SeqArgs &a, int64_t b, int h,
                                           int kh, int t0, int tid) {
     using C = Chunk<CH, NTH>;
@@ -88,7 +92,15 @@ __device__ __forceinline__ void seq_fetch(ChunkRegs<CH, NTH> &cr, const SeqArgs 
         cr.f[2 * C::kSlots + n] = *reinterpret_cast<const f4 *>(a.v + voff + dt * vtok);
     }
     cr.s = 0.0f;
-    if (tid < 2 * CH) {
+    cr.s2 = 0.0f;
+    if constexpr (SC) {
+        if (tid < CH) {
+            const int tg = kClamp ? min(t0 + tid, a.T - 1) : t0 + tid;
+            const int64_t idx = (b * a.T + tg) * a.Hv + h;
+            cr.s = a.gate[idx];
+            cr.s2 = a.beta[idx];
+        }
+    } else if (tid < 2 * CH) {
         const int tt = tid < CH ? tid : tid - CH;
         const int tg = kClamp ? min(t0 + tt, a.T - 1) : t0 + tt;
         const int64_t idx = (b * a.T + tg) * a.Hv + h;
@@ -96,19 +108,56 @@ __device__ __forceinline__ void seq_fetch(ChunkRegs<CH, NTH> &cr, const SeqArgs 
     }
 }
 
-template <int CH, int NTH>
+template <int CH, int NTH, bool SC>
 __device__ __forceinline__ void fetch_chunk(ChunkRegs<CH, NTH> &cr, const SeqArgs &a, int64_t b, int h,
                                             int kh, int t0, int tid) {
     // 8-token chunks (sequences under 16 tokens) always clamp: one code path
     // measured 1-3 % faster at T = 3..6.
     if (CH > 8 && t0 + CH <= a.T)
-        seq_fetch<CH, NTH, false>(cr, a, b, h, kh, t0, tid);
+        seq_fetch<CH, NTH, false, SC>(cr, a, b, h, kh, t0, tid);
     else
-        seq_fetch<CH, NTH, true>(cr, a, b, h, kh, t0, tid);
+        seq_fetch<CH, NTH, true, SC>(cr, a, b, h, kh, t0, tid);
 }
 
-template <int CH, int NTH>
-__device__ __forceinline__ void seq_stage(TokenLds *buf, const ChunkRegs<CH, NTH> &cr, int tid) {
+// Scaled decay.  The decay multiplies every state element by the same
+// factor, so within a group of kScaleGroup tokens the registers may hold
+// S / c_t, with c_t the product of the group's decays up to token t: a
+// token's decay then changes c_t instead of the registers, the key product
+// is c_t (S / c_t) . k, the delta is applied as delta / c_t, and the output
+// is c_t (S / c_t) . q.  That takes the decay multiply, one of the four VALU
+// instructions per element and token, off the registers; c of the group's
+// last token is multiplied back in at its end.  Staging computes c_t (a
+// prefix product over the group's lanes), w_t = beta_t / c_t and
+// c_t / sqrt(d) once per group, so a token's delta is
+// v w - ((S / c_t) . k) beta and its output scale one multiply.
+// A group runs scaled only when it is complete, all its gates are <= 0 (no
+// NaN) and its decay product is >= kMinScale (2^-63), so c_t stays normal
+// and S / c_t far from overflow; otherwise it runs with the per-token
+// multiply.  Groups are counted from the call's first token in every launch
+// shape, so results do not depend on the shape (or on B); but a scaled
+// group's rounding differs from the per-token multiply, so its results are
+// not bitwise those of gdn_step.
+constexpr int kScaleGroup = 16;
+constexpr float kMinScale = 0x1p-63f;
+
+// DPP move that keeps `old` in lanes without a source (row shifts).
+template <int CTRL>
+__device__ __forceinline__ float dpp_or(float old, float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                                 __builtin_bit_cast(int, x), CTRL,
+                                                                 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float lane_value(float x, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
+// Stages a fetched chunk into LDS.  With SC, info[2 g] says whether group g
+// of the chunk may run scaled (1 or 0) and info[2 g + 1] is its decay
+// product.
+template <int CH, int NTH, bool SC>
+__device__ __forceinline__ void seq_stage(TokenLds *buf, float *info, const ChunkRegs<CH, NTH> &cr,
+                                          int tid) {
     using C = Chunk<CH, NTH>;
     const int col = 4 * (tid & 31);
     TokenLds *tok = buf + (tid >> 5);
@@ -119,10 +168,45 @@ __device__ __forceinline__ void seq_stage(TokenLds *buf, const ChunkRegs<CH, NTH
         *reinterpret_cast<f4 *>(tk.q + col) = cr.f[C::kSlots + n];
         *reinterpret_cast<f4 *>(tk.v + col) = cr.f[2 * C::kSlots + n];
     }
-    if (tid < CH)
-        buf[tid].e = expf(cr.s);          // the token's decay factor, computed once
-    else if (tid < 2 * CH)
-        buf[tid - CH].beta = cr.s;
+    if constexpr (SC) {
+        static_assert(kScaleGroup == 16 && CH % kScaleGroup == 0 && CH <= 64,
+                      "a group is one row of 16 lanes of wave 0");
+        if (tid < 64) {                   // wave 0: lane t < CH holds token t's gate and beta
+            const bool mine = tid < CH;
+            const float g = mine ? cr.s : 0.0f;
+            const float e = expf(g);      // the token's decay factor (1 past the chunk)
+            float c = e;                  // inclusive prefix product over each row of 16
+            c *= dpp_or<0x111>(1.0f, c);  // row_shr:1
+            c *= dpp_or<0x112>(1.0f, c);  // row_shr:2
+            c *= dpp_or<0x114>(1.0f, c);  // row_shr:4
+            c *= dpp_or<0x118>(1.0f, c);  // row_shr:8
+            // every lane of wave 0 takes part in the ballot and the reads
+            const uint64_t bad = __ballot(!(g <= 0.0f));           // positive or NaN gates
+            float last[CH / kScaleGroup];
+#pragma unroll
+            for (int gi = 0; gi < CH / kScaleGroup; ++gi) last[gi] = lane_value(c, gi * 16 + 15);
+            if (mine) {
+                TokenLds &tk = buf[tid];
+                tk.e = e;
+                tk.beta = cr.s2;
+                tk.w = cr.s2 / c;
+                tk.os = c * kInvSqrtD;
+            }
+            if (tid == 0) {
+#pragma unroll
+                for (int gi = 0; gi < CH / kScaleGroup; ++gi) {
+                    const bool ok = ((bad >> (gi * 16)) & 0xFFFFu) == 0 && last[gi] >= kMinScale;
+                    info[2 * gi] = ok ? 1.0f : 0.0f;
+                    info[2 * gi + 1] = last[gi];
+                }
+            }
+        }
+    } else {
+        if (tid < CH)
+            buf[tid].e = expf(cr.s);      // the token's decay factor, computed once
+        else if (tid < 2 * CH)
+            buf[tid - CH].beta = cr.s;
+    }
 }
 
 // Plain DPP move (no `old` operand to materialise); every lane of the
@@ -158,6 +242,36 @@ __device__ __forceinline__ void select_row(RowSlice &dst, bool s, const RowSlice
     }
 }
 
+// pass() without the decay multiply (the scaled form).
+__device__ __forceinline__ void pass_scaled(RowSlice &r, float d, const VecSlice &k,
+                                            const VecSlice &q, const VecSlice &kn, float &o,
+                                            float &p) {
+    o = 0.0f;
+    p = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kF4PerLane; ++i) {
+#define GDN_PASS_LANE(X)                          \
+        r.m[i].X = fmaf(d, k.x[i].X, r.m[i].X);   \
+        o = fmaf(r.m[i].X, q.x[i].X, o);          \
+        p = fmaf(r.m[i].X, kn.x[i].X, p);
+        GDN_PASS_LANE(x)
+        GDN_PASS_LANE(y)
+        GDN_PASS_LANE(z)
+        GDN_PASS_LANE(w)
+#undef GDN_PASS_LANE
+    }
+}
+
+__device__ __forceinline__ void scale_row(RowSlice &r, float f) {
+#pragma unroll
+    for (int i = 0; i < kF4PerLane; ++i) {
+        r.m[i].x *= f;
+        r.m[i].y *= f;
+        r.m[i].z *= f;
+        r.m[i].w *= f;
+    }
+}
+
 // Token tt of a chunk: steps 3-5 of tt and, when `next`, steps 1-2 of tt+1
 // (kv holds k of token tt on entry and of tt+1 on exit; p the key partials).
 // kPair: a lane's two rows sit in swapped slots (slot 0 is row A in lanes 0-3
@@ -165,20 +279,31 @@ __device__ __forceinline__ void select_row(RowSlice &dst, bool s, const RowSlice
 // with one set of DPP adds, each lane computes the delta of its slot-0 row
 // only and takes the other row's from its mirror lane, and writes one output.
 // Otherwise each slot is reduced on its own.  Both give the same bits.
-template <bool kPair, int TPW>
+// kScaled: the registers hold S / c_t (scaled decay above); kFold: see below.
+template <bool kPair, int TPW, bool kScaled, bool kFold = false>
 __device__ __forceinline__ void seq_token(TokenLds *buf, int tt, bool next, const int (&rows)[TPW],
                                           RowSlice (&r)[TPW], VecSlice &kv, float (&p)[TPW],
-                                          int c) {
+                                          int c, float fold = 1.0f) {
     static_assert(!kPair || TPW == 2, "pairing needs two tiles per wave");
     TokenLds &tok = buf[tt];
     float d[TPW];                                              // step 3
-    if constexpr (kPair) {
+    if constexpr (kScaled) {
+        // v w - ((S / c) . k) beta = (v - S . k) beta / c = delta / c
+        if constexpr (kPair) {
+            d[0] = fmaf(-pair_sum(p[0], p[1]), tok.beta, tok.v[rows[0]] * tok.w);
+            d[1] = dpp_mov<0x141>(d[0]);
+        } else {
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) d[t] = fmaf(-group_sum(p[t]), tok.beta, tok.v[rows[t]] * tok.w);
+        }
+    } else if constexpr (kPair) {
         d[0] = (tok.v[rows[0]] - pair_sum(p[0], p[1])) * tok.beta;
         d[1] = dpp_mov<0x141>(d[0]);                           // from lane 7-c: the other row
     } else {
 #pragma unroll
         for (int t = 0; t < TPW; ++t) d[t] = (tok.v[rows[t]] - group_sum(p[t])) * tok.beta;
     }
+    const float oscale = kScaled ? tok.os : kInvSqrtD;
     VecSlice qv;
     load_vec(qv, tok.q, c);
     float o[TPW];
@@ -186,8 +311,19 @@ __device__ __forceinline__ void seq_token(TokenLds *buf, int tt, bool next, cons
         VecSlice kn;
         load_vec(kn, buf[tt + 1].k, c);
         const float en = buf[tt + 1].e;
+        if constexpr (kFold) {
+            // last token of a scaled group followed by another: the registers
+            // take the group's c back (the same bits as body_part(), then
+            // scale_row(), then the next group's dot_part())
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) pass(r[t], d[t], kv, qv, en, kn, o[t], p[t]);
+            for (int t = 0; t < TPW; ++t) pass(r[t], d[t], kv, qv, fold, kn, o[t], p[t]);
+        } else if constexpr (kScaled) {
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) pass_scaled(r[t], d[t], kv, qv, kn, o[t], p[t]);
+        } else {
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) pass(r[t], d[t], kv, qv, en, kn, o[t], p[t]);
+        }
         kv = kn;
     } else {
 #pragma unroll
@@ -195,22 +331,81 @@ __device__ __forceinline__ void seq_token(TokenLds *buf, int tt, bool next, cons
     }
     // every lane holding a row in a written slot has the same output bits
     if constexpr (kPair) {
-        tok.v[rows[0]] = pair_sum(o[0], o[1]) * kInvSqrtD;
+        tok.v[rows[0]] = pair_sum(o[0], o[1]) * oscale;
     } else {
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) tok.v[rows[t]] = group_sum(o[t]) * kInvSqrtD;
+        for (int t = 0; t < TPW; ++t) tok.v[rows[t]] = group_sum(o[t]) * oscale;
     }
+}
+
+// Tokens [0, nt) of the CH staged tokens at buf, with the per-token decay
+// multiply: steps 1-2 of the first, then seq_token() for each; when nt == CH
+// the loop is unrolled, so every LDS address is an immediate offset.
+template <int CH, bool PAIR, int TPW>
+__device__ __forceinline__ void seq_chunk(TokenLds *buf, int nt, const int (&rows)[TPW],
+                                          RowSlice (&r)[TPW], int c) {
+    VecSlice kv;
+    load_vec(kv, buf[0].k, c);
+    float p[TPW];
+    const float e0 = buf[0].e;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) p[t] = head_part(r[t], kv, e0);
+    if (nt == CH) {
+#pragma unroll
+        for (int tt = 0; tt < CH; ++tt)
+            seq_token<PAIR, TPW, false>(buf, tt, tt + 1 < CH, rows, r, kv, p, c);
+    } else {
+        for (int tt = 0; tt < nt; ++tt)
+            seq_token<PAIR, TPW, false>(buf, tt, tt + 1 < nt, rows, r, kv, p, c);
+    }
+}
+
+// A complete group of kScaleGroup tokens with the scaled decay.  On entry
+// the registers hold the state before the group's first token, which is
+// S / c_0 of the decayed state (c_0 = e_0).  `carried`: kv and p already
+// hold that token's key and key partials (the previous group folded with a
+// pipelined pass).  `next_scaled`: the group after it (at buf[kScaleGroup],
+// in the same chunk) runs scaled too; the last token then folds c back in
+// with the next token's key product in the same sweep and leaves kv and p
+// for it.  On exit the registers hold the state after the group.
+template <bool PAIR, int TPW>
+__device__ __forceinline__ void seq_group_scaled(TokenLds *buf, const float *info, bool carried,
+                                                 bool next_scaled, const int (&rows)[TPW],
+                                                 RowSlice (&r)[TPW], int c, VecSlice &kv,
+                                                 float (&p)[TPW]) {
+    constexpr int N = kScaleGroup;
+    if (!carried) {
+        load_vec(kv, buf[0].k, c);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) p[t] = dot_part(r[t], kv);
+    }
+#pragma unroll
+    for (int tt = 0; tt < N - 1; ++tt) seq_token<PAIR, TPW, true>(buf, tt, true, rows, r, kv, p, c);
+    const float last = info[1];
+    if (next_scaled) {
+        seq_token<PAIR, TPW, true, true>(buf, N - 1, true, rows, r, kv, p, c, last);
+    } else {
+        seq_token<PAIR, TPW, true>(buf, N - 1, false, rows, r, kv, p, c);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) scale_row(r[t], last);
+    }
+}
+
+__device__ __forceinline__ bool group_scaled(const float *info, int gi) {
+    return __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, info[2 * gi])) != 0;
 }
 
 // CH: tokens per LDS chunk; NT: nontemporal state load and store; PAIR:
 // paired row reductions (seq_token); a head's 128 rows are split over PARTS
 // workgroups of 16 / (TPW * PARTS) waves with TPW tiles each; WPS: waves per
-// SIMD the register allocation must allow (3 caps it at 168 VGPRs).
-template <int CH, bool NT, bool PAIR, int PARTS, int WPS, int TPW = 2>
+// SIMD the register allocation must allow (3 caps it at 168 VGPRs); SC: the
+// scaled decay.
+template <int CH, bool NT, bool PAIR, int PARTS, int WPS, int TPW = 2, bool SC = false>
 __global__ __launch_bounds__(64 * 16 / (TPW * PARTS), WPS) void k_seq(SeqArgs a) {
     constexpr int NTH = 64 * 16 / (TPW * PARTS);
     constexpr int R = D / PARTS;                  // rows of this workgroup
     __shared__ TokenLds lds[2][CH];
+    __shared__ float info[2][2 * (CH / 8)];       // per buffer, with SC (seq_stage)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -255,34 +450,43 @@ __global__ __launch_bounds__(64 * 16 / (TPW * PARTS), WPS) void k_seq(SeqArgs a)
     }
 
     ChunkRegs<CH, NTH> cr;
-    fetch_chunk(cr, a, b, h, kh, 0, tid);
-    seq_stage(lds[0], cr, tid);
+    fetch_chunk<CH, NTH, SC>(cr, a, b, h, kh, 0, tid);
+    seq_stage<CH, NTH, SC>(lds[0], info[0], cr, tid);
     __syncthreads();
 
     const int n_chunks = (a.T + CH - 1) / CH;
     for (int ch = 0; ch < n_chunks; ++ch) {
         const bool more = ch + 1 < n_chunks;
-        if (more) fetch_chunk(cr, a, b, h, kh, (ch + 1) * CH, tid);
+        if (more) fetch_chunk<CH, NTH, SC>(cr, a, b, h, kh, (ch + 1) * CH, tid);
 
         TokenLds *buf = lds[ch & 1];
         const int t0 = ch * CH;
         const int nt = min(CH, a.T - t0);
 
-        // steps 1-2 of the chunk's first token
-        VecSlice kv;
-        load_vec(kv, buf[0].k, c);
-        float p[TPW];
-        {
-            const float e0 = buf[0].e;
+        if constexpr (SC) {
+            // group by group: complete groups that pass the check run scaled
+            constexpr int G = CH / kScaleGroup;
+            const float *inf = info[ch & 1];
+            VecSlice kv;
+            float p[TPW];
+            bool carried = false;
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) p[t] = head_part(r[t], kv, e0);
-        }
-        if (nt == CH) {
-            // full chunk: unrolled, so every LDS address is an immediate offset
-#pragma unroll
-            for (int tt = 0; tt < CH; ++tt) seq_token<PAIR, TPW>(buf, tt, tt + 1 < CH, rows, r, kv, p, c);
+            for (int gi = 0; gi < G; ++gi) {
+                const int ng = min(kScaleGroup, nt - gi * kScaleGroup);
+                if (ng <= 0) break;
+                TokenLds *gb = buf + gi * kScaleGroup;
+                if (ng == kScaleGroup && group_scaled(inf, gi)) {
+                    const bool next_scaled = gi + 1 < G && nt - (gi + 1) * kScaleGroup >= kScaleGroup &&
+                                             group_scaled(inf, gi + 1);
+                    seq_group_scaled<PAIR, TPW>(gb, inf + 2 * gi, carried, next_scaled, rows, r, c, kv, p);
+                    carried = next_scaled;
+                } else {
+                    seq_chunk<kScaleGroup, PAIR, TPW>(gb, ng, rows, r, c);
+                    carried = false;
+                }
+            }
         } else {
-            for (int tt = 0; tt < nt; ++tt) seq_token<PAIR, TPW>(buf, tt, tt + 1 < nt, rows, r, kv, p, c);
+            seq_chunk<CH, PAIR, TPW>(buf, nt, rows, r, c);
         }
         __syncthreads();                 // outputs of chunk ch complete in LDS
 
@@ -296,7 +500,7 @@ __global__ __launch_bounds__(64 * 16 / (TPW * PARTS), WPS) void k_seq(SeqArgs a)
                 *reinterpret_cast<f4 *>(a.out + o) = *reinterpret_cast<const f4 *>(buf[tt].v + col);
             }
         }
-        if (more) seq_stage(lds[(ch + 1) & 1], cr, tid);
+        if (more) seq_stage<CH, NTH, SC>(lds[(ch + 1) & 1], info[(ch + 1) & 1], cr, tid);
         __syncthreads();                 // chunk ch+1 staged; chunk ch flushed
     }
     if constexpr (TPW == 2) {
@@ -349,6 +553,12 @@ __global__ __launch_bounds__(64 * 16 / (TPW * PARTS), WPS) void k_seq(SeqArgs a)
 //     32-token chunks): 1.84 -> 1.47 ms at B = 4, T = 4096; one-tile parts
 //     there measured 20 % slower, and two-tile splits no better than the
 //     half-head routes below 65 tokens.
+// - 16- and 32-token chunks run their groups with the scaled decay (SC):
+//   per call, B = 8 T = 4096 1.77 -> 1.67 ms, B = 1 T = 4096 1.03 -> 0.93,
+//   B = 4 T = 4096 1.36 -> 1.26, B = 64 T = 64 248 -> 219 us, B = 256
+//   T = 64 1.00 -> 0.89 ms (graph replays).  Folding c once per 32 tokens
+//   where a chunk has 32 was another 1-2 % faster but makes the bits depend
+//   on the launch shape.  8-token chunks (T < 16) keep the per-token form.
 static_assert(2 * 256 == kSeqThreadsPerHead && 512 == kSeqThreadsPerHead,
               "the API bounds B * Hv by this launch's work-items per head");
 
@@ -363,7 +573,7 @@ hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
         if (a.T < 16)
             k_seq<8, true, false, 16, 1, 1><<<grid, block, 0, s>>>(a);
         else
-            k_seq<16, false, false, 16, 1, 1><<<grid, block, 0, s>>>(a);
+            k_seq<16, false, false, 16, 1, 1, true><<<grid, block, 0, s>>>(a);
     } else if (4 * heads <= cus) {
         // 8 two-wave parts of one tile per wave (1024 work-items per head;
         // heads <= CUs / 4)
@@ -371,7 +581,7 @@ hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
         if (a.T < 16)
             k_seq<8, true, false, 8, 1, 1><<<grid, block, 0, s>>>(a);
         else
-            k_seq<16, false, false, 8, 1, 1><<<grid, block, 0, s>>>(a);
+            k_seq<16, false, false, 8, 1, 1, true><<<grid, block, 0, s>>>(a);
     } else if (a.T < 16) {
         if (heads <= cus)
             k_seq<8, true, true, 2, 1><<<split, dim3(256), 0, s>>>(a);
@@ -379,13 +589,13 @@ hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
             k_seq<8, true, false, 2, 1><<<split, dim3(256), 0, s>>>(a);
     } else if (a.T <= 64) {
         if (heads <= 2 * cus)
-            k_seq<16, true, true, 2, 1><<<split, dim3(256), 0, s>>>(a);
+            k_seq<16, true, true, 2, 1, 2, true><<<split, dim3(256), 0, s>>>(a);
         else
-            k_seq<16, true, false, 2, 3><<<split, dim3(256), 0, s>>>(a);
+            k_seq<16, true, false, 2, 3, 2, true><<<split, dim3(256), 0, s>>>(a);
     } else if (2 * heads <= cus) {
-        k_seq<32, false, true, 2, 1><<<split, dim3(256), 0, s>>>(a);
+        k_seq<32, false, true, 2, 1, 2, true><<<split, dim3(256), 0, s>>>(a);
     } else {
-        k_seq<32, false, true, 1, 1><<<whole, dim3(512), 0, s>>>(a);
+        k_seq<32, false, true, 1, 1, 2, true><<<whole, dim3(512), 0, s>>>(a);
     }
     return hipGetLastError();
 }

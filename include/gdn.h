@@ -30,8 +30,8 @@
  *     gdn_layer_tail guarantee it (a state that large would not fit in
  *     memory anyway).
  *   - Results are bitwise deterministic for identical inputs, independent of
- *     B and of the other sequences in the batch.  gdn_seq over T tokens is
- *     bitwise equal to T calls of gdn_step.
+ *     B and of the other sequences in the batch.  gdn_seq over T < 16 tokens
+ *     is bitwise equal to T calls of gdn_step (longer calls: see gdn_seq).
  *   - NaN and Inf inputs are not checked; they propagate.
  *
  * Errors: every call returns GDN_OK (0) or a negative code.  Argument errors
@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 10101 /* 1.1.1 */
+#define GDN_VERSION 10200 /* 1.2.0 */
 
 #define GDN_OK 0
 #define GDN_ERR_NULL (-1)      /* a required pointer is NULL                  */
@@ -109,7 +109,18 @@ int gdn_step(const gdn_dims *dims, int32_t B,
  *   state  [B][n_v_heads][d_v][d_k]   in: state before token 0, out: after T-1
  *   out    [B][T][n_v_heads][d_v]
  * The state stays on chip for all T tokens: it is read once and written once
- * per call.  Splitting T into consecutive calls gives bitwise the same result.
+ * per call.
+ * Tokens are taken in groups of 16 counted from token 0.  A complete group
+ * whose gates are all <= 0 and whose decay product (the product of
+ * exp(gate) over the group) is at least 2^-63 runs with the decay carried
+ * as one scale c for the whole state, which holds S / c during the group:
+ * the step's arithmetic without the decay multiply on each state element,
+ * rounded differently from gdn_step (the same recurrence to float32
+ * rounding, not the same bits).  Every other group, and a trailing partial
+ * one, multiplies per token as gdn_step does: a call in which no group
+ * qualifies (T < 16, or decay stronger than that floor) is bitwise equal to
+ * T gdn_step calls.  Splitting T into consecutive calls at multiples of 16
+ * tokens gives bitwise the same result.
  */
 int gdn_seq(const gdn_dims *dims, int32_t B, int32_t T,
             const float *q, const float *k, const float *v,

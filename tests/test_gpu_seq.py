@@ -66,19 +66,18 @@ def test_seq_matches_oracle(g, orc, B, T, Hv, Hk):
     ref.assert_close("out", og, want, 1e-5)
 
 
-@pytest.mark.parametrize("B,T", [(2, 2), (2, 8), (2, 15), (2, 24), (2, 32), (2, 37), (2, 65),
-                                 (12, 9), (24, 20), (1, 70), (3, 70), (8, 66), (1, 9), (1, 24),
-                                 (4, 8), (8, 32)])
-def test_seq_is_bitwise_repeated_step(g, B, T):
-    """T tokens in one gdn_seq == T gdn_step calls, bit for bit (both paths
-    share the per-row arithmetic), for every route: half heads with 8- and
-    16-token chunks, paired and unpaired, heads split in 16, 8 or 2 parts, and
-    whole heads."""
+def strong_decay(si):
+    """Gates <= -3 everywhere: every 16-token group's decay product is at
+    most e^-48, below the scaled form's 2^-63 floor, so every group runs with
+    the per-token decay multiply."""
+    si = dict(si)
+    si["gate"] = (si["gate"] - np.float32(3.0)).astype(np.float32)
+    return si
+
+
+def repeated_steps(g, si, M):
     import torch
-    print(f"\n  gdn_seq == repeated gdn_step, B={B} T={T}", flush=True)
-    si = gi.step_inputs(3100, 0, B, T=T)
-    M = gi.state(3100, 0, B)
-    Ms, os_ = run_seq(g, si, M)
+    B, T = si["q"].shape[:2]
     Md = dev(M)
     outs = []
     for t in range(T):
@@ -87,14 +86,109 @@ def test_seq_is_bitwise_repeated_step(g, B, T):
         g.step(tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], Md, o)
         outs.append(o)
     torch.cuda.synchronize()
-    assert np.array_equal(Md.cpu().numpy(), Ms), "state differs"
-    assert np.array_equal(torch.stack(outs, 1).cpu().numpy(), os_), "outputs differ"
+    return Md.cpu().numpy(), torch.stack(outs, 1).cpu().numpy()
 
 
-def test_seq_chunked_resume_is_bitwise(g):
-    """Checkpoint/resume: seq(T) == seq(T1) then seq(T - T1) from the saved state."""
-    print("\n  gdn_seq chunked resume", flush=True)
-    B, T, T1 = 3, 40, 13
+@pytest.mark.parametrize("B,T", [(2, 2), (2, 8), (2, 15), (2, 24), (2, 32), (2, 37), (2, 65),
+                                 (12, 9), (24, 20), (1, 70), (3, 70), (8, 66), (1, 9), (1, 24),
+                                 (4, 8), (8, 32), (2, 16), (4, 64)])
+def test_seq_is_bitwise_repeated_step(g, B, T):
+    """T tokens in one gdn_seq == T gdn_step calls, bit for bit, whenever no
+    group runs scaled: below 16 tokens always, and from 16 tokens on with
+    strong decay (every group under the scaled form's floor).  Both paths
+    share the per-row arithmetic.  Every route: half heads with 8- and
+    16-token chunks, paired and unpaired, heads split in 16, 8 or 2 parts,
+    and whole heads."""
+    print(f"\n  gdn_seq == repeated gdn_step, B={B} T={T}", flush=True)
+    si = gi.step_inputs(3100, 0, B, T=T)
+    if T >= 16:
+        si = strong_decay(si)
+    M = gi.state(3100, 0, B)
+    Ms, os_ = run_seq(g, si, M)
+    Md, od = repeated_steps(g, si, M)
+    assert np.array_equal(Md, Ms), "state differs"
+    assert np.array_equal(od, os_), "outputs differ"
+
+
+def mixed_groups(si):
+    """Gates that send the 16-token groups down both paths in one call:
+    group 1 holds a full forget (gate = -1e4, exp = 0) and group 2 a positive
+    gate (0.3), so both run with the per-token multiply; every other complete
+    group runs scaled, and a trailing partial group with the multiply."""
+    si = dict(si)
+    gate = si["gate"].copy()
+    T = gate.shape[1]
+    if T > 20:
+        gate[:, 20] = -1e4
+    if T > 40:
+        gate[:, 40] = 0.3
+    si["gate"] = gate
+    return si
+
+
+# sequence 0 of each batch size below runs through a different launch shape
+# (B = 1: 16 one-tile parts, 16-token chunks; B = 2: 8 parts; B = 3: 2 parts,
+# 32-token chunks; B = 8: whole heads, 32-token chunks; T <= 64 with B = 4:
+# paired half heads; B = 24: unpaired half heads, 16-token chunks)
+@pytest.mark.parametrize("T,Bs", [(100, (1, 2, 3, 8)), (64, (1, 2, 4, 24)), (37, (1, 4, 24))])
+def test_seq_bits_do_not_depend_on_launch_shape(g, orc, T, Bs):
+    """The scaled groups are counted from the call's first token in every
+    launch shape, and a fold inside a 32-token chunk (pipelined with the next
+    token's key product) gives the bits of one at a chunk's end: a sequence's
+    results are bitwise the same whatever B (and so the launch shape) it runs
+    in.  T = 100 mixes the paths: scaled then per-token within a chunk
+    (groups 0, 1), per-token then scaled (2, 3), two scaled (4, 5), and a
+    partial group (6); all checked against the oracle."""
+    print(f"\n  gdn_seq launch-shape independence T={T} B={Bs}", flush=True)
+    res = {}
+    for B in Bs:
+        si = mixed_groups(gi.step_inputs(3500, 0, B, T=T))
+        M = gi.state(3500, 0, B)
+        res[B] = run_seq(g, si, M)
+    first = res[Bs[0]]
+    for B in Bs[1:]:
+        assert np.array_equal(res[B][0][:1], first[0][:1]), f"state of sequence 0 differs at B={B}"
+        assert np.array_equal(res[B][1][:1], first[1][:1]), f"outputs of sequence 0 differ at B={B}"
+    si = mixed_groups(gi.step_inputs(3500, 0, 1, T=T))
+    M = gi.state(3500, 0, 1)
+    want = ref.seq_mt(orc, si, M)
+    ref.assert_close("state", first[0], M, 1e-6)
+    ref.assert_close("out", first[1], want, 1e-5)
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_seq_scaled_group_floor(g, orc, B):
+    """The 2^-63 floor on a group's decay product.  Gates of -2.7 (product
+    e^-43.2, above it) run scaled, with the registers holding S / c up to
+    6e18 |S|: within tolerance of the oracle, and not bitwise the per-token
+    path.  Gates of -2.75 (e^-44, below it) run with the per-token multiply:
+    bitwise equal to repeated gdn_step."""
+    T = 32
+    for gate, scaled in ((-2.7, True), (-2.75, False)):
+        print(f"\n  gdn_seq B={B} T={T} gate={gate}", flush=True)
+        si = gi.step_inputs(3600, 0, B, T=T)
+        si["gate"] = np.full_like(si["gate"], np.float32(gate))
+        M = gi.state(3600, 0, B)
+        Ms, os_ = run_seq(g, si, M)
+        Md, od = repeated_steps(g, si, M)
+        if scaled:
+            assert not (np.array_equal(Md, Ms) and np.array_equal(od, os_)), \
+                "a scaled group gave the per-token bits (not taken?)"
+            Mo = M.copy()
+            want = ref.seq_mt(orc, si, Mo)
+            ref.assert_close("state", Ms, Mo, 1e-6)
+            ref.assert_close("out", os_, want, 1e-5)
+        else:
+            assert np.array_equal(Md, Ms) and np.array_equal(od, os_), "per-token group not bitwise"
+
+
+@pytest.mark.parametrize("T,T1", [(40, 16), (40, 32), (80, 48), (12, 5)])
+def test_seq_chunked_resume_is_bitwise(g, T, T1):
+    """Checkpoint/resume: seq(T) == seq(T1) then seq(T - T1) from the saved
+    state, bit for bit, when T1 is a multiple of 16 (the scaled groups line
+    up) or T < 16."""
+    print(f"\n  gdn_seq chunked resume T={T} T1={T1}", flush=True)
+    B = 3
     si = gi.step_inputs(3200, 0, B, T=T)
     M = gi.state(3200, 0, B)
     Mfull, ofull = run_seq(g, si, M)
@@ -103,6 +197,23 @@ def test_seq_chunked_resume_is_bitwise(g):
     M1, o1 = run_seq(g, a, M)
     M2, o2 = run_seq(g, b, M1)
     assert np.array_equal(M2, Mfull) and np.array_equal(np.concatenate([o1, o2], 1), ofull)
+
+
+def test_seq_resume_at_any_token_matches_oracle(g, orc):
+    """Resume at a token that is not a multiple of 16: the groups shift, so
+    the bits may differ from one call, but both match the oracle."""
+    print("\n  gdn_seq resume at token 13", flush=True)
+    B, T, T1 = 3, 40, 13
+    si = gi.step_inputs(3200, 0, B, T=T)
+    M = gi.state(3200, 0, B)
+    a = {n: np.ascontiguousarray(x[:, :T1]) for n, x in si.items()}
+    b = {n: np.ascontiguousarray(x[:, T1:]) for n, x in si.items()}
+    M1, o1 = run_seq(g, a, M)
+    M2, o2 = run_seq(g, b, M1)
+    Mo = M.copy()
+    want = ref.seq_mt(orc, si, Mo)
+    ref.assert_close("state", M2, Mo, 1e-6)
+    ref.assert_close("out", np.concatenate([o1, o2], 1), want, 1e-5)
 
 
 def test_seq_contraction_from_zero_state(g, orc):
