@@ -6,6 +6,7 @@ C entry points:
 
     step(q, k, v, beta, gate, state, out)        -> gdn_step
     seq(q, k, v, beta, gate, state, out)         -> gdn_seq
+    seq(..., exact=True)                         -> gdn_seq_exact
     pair(q, k, v, beta, gate, state, state_next, out) -> gdn_pair
     layer_tail(x, conv_w, conv_state, beta, gate, state, z, norm_w, y, ...)
                                                  -> gdn_layer_tail
@@ -75,6 +76,8 @@ lib.gdn_step.restype = ctypes.c_int
 lib.gdn_step.argtypes = [_DP, _i32] + [_vp] * 7 + [_vp]
 lib.gdn_seq.restype = ctypes.c_int
 lib.gdn_seq.argtypes = [_DP, _i32, _i32] + [_vp] * 7 + [_vp]
+lib.gdn_seq_exact.restype = ctypes.c_int
+lib.gdn_seq_exact.argtypes = [_DP, _i32, _i32] + [_vp] * 7 + [_vp]
 lib.gdn_pair.restype = ctypes.c_int
 lib.gdn_pair.argtypes = [_DP, _i32] + [_vp] * 8 + [_vp]
 lib.gdn_layer_tail.restype = ctypes.c_int
@@ -155,12 +158,13 @@ def step(q, k, v, beta, gate, state, out, stream=None) -> None:
         _ptr(out, "out", (B, d.n_v_heads, d.d_v)), _stream(stream)))
 
 
-def seq(q, k, v, beta, gate, state, out, stream=None) -> None:
-    """gdn_seq: q,k [B][T][Hk][dk], v [B][T][Hv][dv], beta/gate [B][T][Hv],
-    state [B][Hv][dv][dk] (in/out), out [B][T][Hv][dv]."""
+def seq(q, k, v, beta, gate, state, out, stream=None, exact=False) -> None:
+    """gdn_seq (gdn_seq_exact with exact=True): q,k [B][T][Hk][dk],
+    v [B][T][Hv][dv], beta/gate [B][T][Hv], state [B][Hv][dv][dk] (in/out),
+    out [B][T][Hv][dv]."""
     B, T = q.shape[0], q.shape[1]
     d = _dims_of(q, v)
-    _check(lib.gdn_seq(
+    _check((lib.gdn_seq_exact if exact else lib.gdn_seq)(
         ctypes.byref(d), B, T,
         _ptr(q, "q", (B, T, d.n_k_heads, d.d_k)), _ptr(k, "k", (B, T, d.n_k_heads, d.d_k)),
         _ptr(v, "v", (B, T, d.n_v_heads, d.d_v)),

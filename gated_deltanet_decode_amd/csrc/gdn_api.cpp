@@ -122,53 +122,10 @@ int hip_status(hipError_t e, const char *what) {
     return GDN_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int gdn_version(void) { return GDN_VERSION; }
-
-const char *gdn_last_error(void) { return g_error; }
-
-int gdn_step(const gdn_dims *dims, int32_t B, const float *q, const float *k, const float *v,
-             const float *beta, const float *gate, float *state, float *out, void *stream) {
-    clear_error();
-    GDN_TRY(check_dims(dims));
-    GDN_TRY(check_batch(dims, B, "B"));
-    const size_t f = sizeof(float);
-    const size_t nqk = static_cast<size_t>(B) * dims->n_k_heads * dims->d_k * f;
-    const size_t nv = static_cast<size_t>(B) * dims->n_v_heads * dims->d_v * f;
-    const size_t nh = static_cast<size_t>(B) * dims->n_v_heads * f;
-    const size_t ns = static_cast<size_t>(B) * dims->n_v_heads * dims->d_v * dims->d_k * f;
-    const Buf vec[] = {{"q", q, nqk}, {"k", k, nqk}, {"v", v, nv}, {"state", state, ns},
-                       {"out", out, nv}};
-    const Buf sc[] = {{"beta", beta, nh}, {"gate", gate, nh}};
-    GDN_TRY(check_ptrs(vec, 5, 16));
-    GDN_TRY(check_ptrs(sc, 2, 4));
-    const Buf all[] = {vec[0], vec[1], vec[2], vec[3], vec[4], sc[0], sc[1]};
-    const Buf outs[] = {vec[3], vec[4]};  // state and out are written
-    GDN_TRY(check_alias(outs, 2, all, 7));
-
-    gdn::StepArgs a{};
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.beta = beta;
-    a.gate = gate;
-    a.state = state;
-    a.out = out;
-    a.qk_bstride = static_cast<int64_t>(dims->n_k_heads) * dims->d_k;
-    a.v_bstride = static_cast<int64_t>(dims->n_v_heads) * dims->d_v;
-    a.B = B;
-    a.Hv = dims->n_v_heads;
-    a.Hk = dims->n_k_heads;
-    (void)hipGetLastError();  // do not report an earlier, unrelated error
-    return hip_status(gdn::launch_step(a, static_cast<hipStream_t>(stream)), "gdn_step launch");
-}
-
-int gdn_seq(const gdn_dims *dims, int32_t B, int32_t T, const float *q, const float *k,
-            const float *v, const float *beta, const float *gate, float *state, float *out,
-            void *stream) {
+// gdn_seq and gdn_seq_exact: checks, then the launch (exact: no scaled groups).
+int seq_call(const char *name, bool exact, const gdn_dims *dims, int32_t B, int32_t T,
+             const float *q, const float *k, const float *v, const float *beta,
+             const float *gate, float *state, float *out, void *stream) {
     clear_error();
     GDN_TRY(check_dims(dims));
     GDN_TRY(check_batch(dims, B, "B"));
@@ -178,7 +135,7 @@ int gdn_seq(const gdn_dims *dims, int32_t B, int32_t T, const float *q, const fl
         return fail(GDN_ERR_SHAPE, "T must be in [1, 1073741824] (got %d)", T);
     // the launch must fit the dispatch's 32-bit work-item count
     if (static_cast<int64_t>(B) * dims->n_v_heads * gdn::kSeqThreadsPerHead > UINT32_MAX)
-        return fail(GDN_ERR_SHAPE, "gdn_seq: B * n_v_heads = %lld exceeds %lld",
+        return fail(GDN_ERR_SHAPE, "%s: B * n_v_heads = %lld exceeds %lld", name,
                     (long long)(static_cast<int64_t>(B) * dims->n_v_heads),
                     (long long)(UINT32_MAX / gdn::kSeqThreadsPerHead));
     const size_t f = sizeof(float);
@@ -226,9 +183,65 @@ int gdn_seq(const gdn_dims *dims, int32_t B, int32_t T, const float *q, const fl
         sa.B = B;
         sa.Hv = dims->n_v_heads;
         sa.Hk = dims->n_k_heads;
-        return hip_status(gdn::launch_step(sa, s), "gdn_seq launch");
+        return hip_status(gdn::launch_step(sa, s), name);
     }
-    return hip_status(gdn::launch_seq(a, s), "gdn_seq launch");
+    return hip_status(gdn::launch_seq(a, s, exact), name);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_version(void) { return GDN_VERSION; }
+
+const char *gdn_last_error(void) { return g_error; }
+
+int gdn_step(const gdn_dims *dims, int32_t B, const float *q, const float *k, const float *v,
+             const float *beta, const float *gate, float *state, float *out, void *stream) {
+    clear_error();
+    GDN_TRY(check_dims(dims));
+    GDN_TRY(check_batch(dims, B, "B"));
+    const size_t f = sizeof(float);
+    const size_t nqk = static_cast<size_t>(B) * dims->n_k_heads * dims->d_k * f;
+    const size_t nv = static_cast<size_t>(B) * dims->n_v_heads * dims->d_v * f;
+    const size_t nh = static_cast<size_t>(B) * dims->n_v_heads * f;
+    const size_t ns = static_cast<size_t>(B) * dims->n_v_heads * dims->d_v * dims->d_k * f;
+    const Buf vec[] = {{"q", q, nqk}, {"k", k, nqk}, {"v", v, nv}, {"state", state, ns},
+                       {"out", out, nv}};
+    const Buf sc[] = {{"beta", beta, nh}, {"gate", gate, nh}};
+    GDN_TRY(check_ptrs(vec, 5, 16));
+    GDN_TRY(check_ptrs(sc, 2, 4));
+    const Buf all[] = {vec[0], vec[1], vec[2], vec[3], vec[4], sc[0], sc[1]};
+    const Buf outs[] = {vec[3], vec[4]};  // state and out are written
+    GDN_TRY(check_alias(outs, 2, all, 7));
+
+    gdn::StepArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.gate = gate;
+    a.state = state;
+    a.out = out;
+    a.qk_bstride = static_cast<int64_t>(dims->n_k_heads) * dims->d_k;
+    a.v_bstride = static_cast<int64_t>(dims->n_v_heads) * dims->d_v;
+    a.B = B;
+    a.Hv = dims->n_v_heads;
+    a.Hk = dims->n_k_heads;
+    (void)hipGetLastError();  // do not report an earlier, unrelated error
+    return hip_status(gdn::launch_step(a, static_cast<hipStream_t>(stream)), "gdn_step launch");
+}
+
+int gdn_seq(const gdn_dims *dims, int32_t B, int32_t T, const float *q, const float *k,
+            const float *v, const float *beta, const float *gate, float *state, float *out,
+            void *stream) {
+    return seq_call("gdn_seq", false, dims, B, T, q, k, v, beta, gate, state, out, stream);
+}
+
+int gdn_seq_exact(const gdn_dims *dims, int32_t B, int32_t T, const float *q, const float *k,
+                  const float *v, const float *beta, const float *gate, float *state, float *out,
+                  void *stream) {
+    return seq_call("gdn_seq_exact", true, dims, B, T, q, k, v, beta, gate, state, out, stream);
 }
 
 int gdn_pair(const gdn_dims *dims, int32_t B, const float *q, const float *k, const float *v,

@@ -139,7 +139,8 @@ int device_cus();
 
 hipError_t launch_step(const StepArgs &a, hipStream_t s);
 hipError_t launch_tail_fused(const TailFusedArgs &a, hipStream_t s);
-hipError_t launch_seq(const SeqArgs &a, hipStream_t s);
+// exact: every token multiplies the decay into the state (no scaled groups).
+hipError_t launch_seq(const SeqArgs &a, hipStream_t s, bool exact);
 hipError_t launch_pair(const PairArgs &a, hipStream_t s);
 hipError_t launch_prestate(const PrestateArgs &a, hipStream_t s);
 hipError_t launch_gated_norm(const GatedNormArgs &a, hipStream_t s);

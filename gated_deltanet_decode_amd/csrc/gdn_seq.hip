@@ -562,7 +562,11 @@ __global__ __launch_bounds__(64 * 16 / (TPW * PARTS), WPS) void k_seq(SeqArgs a)
 static_assert(2 * 256 == kSeqThreadsPerHead && 512 == kSeqThreadsPerHead,
               "the API bounds B * Hv by this launch's work-items per head");
 
-hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
+namespace {
+
+// SC: the 16- and 32-token kernels run qualifying groups scaled.
+template <bool SC>
+hipError_t launch_seq_as(const SeqArgs &a, hipStream_t s) {
     const int64_t heads = static_cast<int64_t>(a.B) * a.Hv;
     const int64_t cus = device_cus();
     const dim3 split(static_cast<unsigned>(heads * 2)), whole(static_cast<unsigned>(heads));
@@ -573,7 +577,7 @@ hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
         if (a.T < 16)
             k_seq<8, true, false, 16, 1, 1><<<grid, block, 0, s>>>(a);
         else
-            k_seq<16, false, false, 16, 1, 1, true><<<grid, block, 0, s>>>(a);
+            k_seq<16, false, false, 16, 1, 1, SC><<<grid, block, 0, s>>>(a);
     } else if (4 * heads <= cus) {
         // 8 two-wave parts of one tile per wave (1024 work-items per head;
         // heads <= CUs / 4)
@@ -581,7 +585,7 @@ hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
         if (a.T < 16)
             k_seq<8, true, false, 8, 1, 1><<<grid, block, 0, s>>>(a);
         else
-            k_seq<16, false, false, 8, 1, 1, true><<<grid, block, 0, s>>>(a);
+            k_seq<16, false, false, 8, 1, 1, SC><<<grid, block, 0, s>>>(a);
     } else if (a.T < 16) {
         if (heads <= cus)
             k_seq<8, true, true, 2, 1><<<split, dim3(256), 0, s>>>(a);
@@ -589,15 +593,21 @@ hipError_t launch_seq(const SeqArgs &a, hipStream_t s) {
             k_seq<8, true, false, 2, 1><<<split, dim3(256), 0, s>>>(a);
     } else if (a.T <= 64) {
         if (heads <= 2 * cus)
-            k_seq<16, true, true, 2, 1, 2, true><<<split, dim3(256), 0, s>>>(a);
+            k_seq<16, true, true, 2, 1, 2, SC><<<split, dim3(256), 0, s>>>(a);
         else
-            k_seq<16, true, false, 2, 3, 2, true><<<split, dim3(256), 0, s>>>(a);
+            k_seq<16, true, false, 2, 3, 2, SC><<<split, dim3(256), 0, s>>>(a);
     } else if (2 * heads <= cus) {
-        k_seq<32, false, true, 2, 1, 2, true><<<split, dim3(256), 0, s>>>(a);
+        k_seq<32, false, true, 2, 1, 2, SC><<<split, dim3(256), 0, s>>>(a);
     } else {
-        k_seq<32, false, true, 1, 1, 2, true><<<whole, dim3(512), 0, s>>>(a);
+        k_seq<32, false, true, 1, 1, 2, SC><<<whole, dim3(512), 0, s>>>(a);
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_seq(const SeqArgs &a, hipStream_t s, bool exact) {
+    return exact ? launch_seq_as<false>(a, s) : launch_seq_as<true>(a, s);
 }
 
 }  // namespace gdn

@@ -30,8 +30,9 @@
  *     gdn_layer_tail guarantee it (a state that large would not fit in
  *     memory anyway).
  *   - Results are bitwise deterministic for identical inputs, independent of
- *     B and of the other sequences in the batch.  gdn_seq over T < 16 tokens
- *     is bitwise equal to T calls of gdn_step (longer calls: see gdn_seq).
+ *     B and of the other sequences in the batch.  gdn_seq_exact over T
+ *     tokens is bitwise equal to T calls of gdn_step; so is gdn_seq for
+ *     T < 16 (longer calls: see gdn_seq).
  *   - NaN and Inf inputs are not checked; they propagate.
  *
  * Errors: every call returns GDN_OK (0) or a negative code.  Argument errors
@@ -126,6 +127,19 @@ int gdn_seq(const gdn_dims *dims, int32_t B, int32_t T,
             const float *q, const float *k, const float *v,
             const float *beta, const float *gate,
             float *state, float *out, void *stream);
+
+/*
+ * gdn_seq_exact - gdn_seq with no scaled groups: every token multiplies the
+ * decay into the state as gdn_step does, so the results are bitwise equal to
+ * T gdn_step calls at any T, and to any split of T into consecutive calls
+ * (docs.rs "Module linear_core", gdn_forward_batch: elementwise identical to
+ * single steps).  Same arguments, layout, limits and errors as gdn_seq; on
+ * long sequences it is 5-12 % slower.
+ */
+int gdn_seq_exact(const gdn_dims *dims, int32_t B, int32_t T,
+                  const float *q, const float *k, const float *v,
+                  const float *beta, const float *gate,
+                  float *state, float *out, void *stream);
 
 /*
  * gdn_pair - two consecutive positions for B sequences, fused for speculative

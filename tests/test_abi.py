@@ -96,19 +96,21 @@ def test_step_validation(g):
     expect(g, call_step(g, d, B, dict(a, state=a["k"] - 16)), -4, "state")
 
 
-def test_seq_validation(g):
+@pytest.mark.parametrize("name", ["gdn_seq", "gdn_seq_exact"])
+def test_seq_validation(g, name):
     a, _ = addrs()
     d = g.Dims(HV, HK, D, D)
-    f = lambda T, aa: g.lib.gdn_seq(ctypes.byref(d), B, T, aa["q"], aa["k"], aa["v"],
-                                    aa["beta"], aa["gate"], aa["state"], aa["out"], None)
+    fn = getattr(g.lib, name)
+    f = lambda T, aa: fn(ctypes.byref(d), B, T, aa["q"], aa["k"], aa["v"],
+                         aa["beta"], aa["gate"], aa["state"], aa["out"], None)
     expect(g, f(0, a), -2, "T")
     expect(g, f(-1, a), -2, "T")
     expect(g, f((1 << 30) + 1, a), -2, "T")
     expect(g, f(2**31 - 1, a), -2, "T")
     # 2^23 heads: 512 work-items each would overflow the 32-bit dispatch grid
-    big = lambda Bv: g.lib.gdn_seq(ctypes.byref(d), Bv, 4, a["q"], a["k"], a["v"], a["beta"],
-                                   a["gate"], a["state"], a["out"], None)
-    expect(g, big((1 << 23) // HV), -2, "gdn_seq: B * n_v_heads")
+    big = lambda Bv: fn(ctypes.byref(d), Bv, 4, a["q"], a["k"], a["v"], a["beta"],
+                        a["gate"], a["state"], a["out"], None)
+    expect(g, big((1 << 23) // HV), -2, f"{name}: B * n_v_heads")
     expect(g, f(4, dict(a, gate=None)), -1, "gate")
     expect(g, f(4, dict(a, v=a["v"] + 4)), -3, "v")
     expect(g, f(1, dict(a, out=a["state"] - 16)), -4, "out")

@@ -23,12 +23,12 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def run_seq(g, si, M):
+def run_seq(g, si, M, exact=False):
     import torch
     t = {n: dev(x) for n, x in si.items()}
     Md = dev(M)
     out = torch.empty(si["v"].shape, dtype=torch.float32, device="cuda")
-    g.seq(t["q"], t["k"], t["v"], t["beta"], t["gate"], Md, out)
+    g.seq(t["q"], t["k"], t["v"], t["beta"], t["gate"], Md, out, exact=exact)
     torch.cuda.synchronize()
     return Md.cpu().numpy(), out.cpu().numpy()
 
@@ -108,6 +108,40 @@ def test_seq_is_bitwise_repeated_step(g, B, T):
     Md, od = repeated_steps(g, si, M)
     assert np.array_equal(Md, Ms), "state differs"
     assert np.array_equal(od, os_), "outputs differ"
+
+
+@pytest.mark.parametrize("B,T", [(2, 24), (2, 32), (2, 37), (2, 65), (24, 20), (1, 70), (3, 70),
+                                 (8, 66), (1, 24), (8, 32), (4, 64), (1, 16)])
+def test_seq_exact_is_bitwise_repeated_step(g, B, T):
+    """gdn_seq_exact: T tokens == T gdn_step calls, bit for bit, at any T and
+    with ordinary gates (no scaled groups), in every launch shape that takes
+    16 or more tokens."""
+    print(f"\n  gdn_seq_exact == repeated gdn_step, B={B} T={T}", flush=True)
+    si = gi.step_inputs(3150, 0, B, T=T)
+    M = gi.state(3150, 0, B)
+    Ms, os_ = run_seq(g, si, M, exact=True)
+    Md, od = repeated_steps(g, si, M)
+    assert np.array_equal(Md, Ms), "state differs"
+    assert np.array_equal(od, os_), "outputs differ"
+
+
+def test_seq_exact_matches_oracle_and_resumes_anywhere(g, orc):
+    """gdn_seq_exact against the oracle, and split at token 13 (not a
+    multiple of 16) it is still bitwise one call."""
+    print("\n  gdn_seq_exact B=3 T=40, resume at 13", flush=True)
+    B, T, T1 = 3, 40, 13
+    si = gi.step_inputs(3250, 0, B, T=T)
+    M = gi.state(3250, 0, B)
+    Mfull, ofull = run_seq(g, si, M, exact=True)
+    a = {n: np.ascontiguousarray(x[:, :T1]) for n, x in si.items()}
+    b = {n: np.ascontiguousarray(x[:, T1:]) for n, x in si.items()}
+    M1, o1 = run_seq(g, a, M, exact=True)
+    M2, o2 = run_seq(g, b, M1, exact=True)
+    assert np.array_equal(M2, Mfull) and np.array_equal(np.concatenate([o1, o2], 1), ofull)
+    Mo = M.copy()
+    want = ref.seq_mt(orc, si, Mo)
+    ref.assert_close("state", Mfull, Mo, 1e-6)
+    ref.assert_close("out", ofull, want, 1e-5)
 
 
 def mixed_groups(si):
