@@ -25,10 +25,10 @@
  *     Outputs must not overlap any input or state buffer.
  *   - Supported on the GPU path: d_k = d_v = 128, n_k_heads >= 1,
  *     n_v_heads a multiple of n_k_heads, B >= 1, 1 <= T <= 1073741824,
- *     B * n_v_heads <= 134213631 (gdn_seq: <= 8388607).  Launches must fit
- *     the dispatch's 32-bit work-item count; the limits here and in
- *     gdn_layer_tail guarantee it (a state that large would not fit in
- *     memory anyway).
+ *     B * n_v_heads <= 134213631 (gdn_seq, gdn_seq_exact: <= 8388607).
+ *     Launches must fit the dispatch's 32-bit work-item count; the limits
+ *     here and in gdn_layer_tail guarantee it (a state that large would not
+ *     fit in memory anyway).
  *   - Results are bitwise deterministic for identical inputs, independent of
  *     B and of the other sequences in the batch.  gdn_seq_exact over T
  *     tokens is bitwise equal to T calls of gdn_step; so is gdn_seq for

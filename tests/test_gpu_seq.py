@@ -300,3 +300,35 @@ def test_seq_more_heads_than_compute_units(g, orc):
     want = ref.seq_mt(orc, si, M)
     ref.assert_close("state", Mg, M, 1e-6)
     ref.assert_close("out", og, want, 1e-5)
+
+
+def test_seq_nan_isolation(g):
+    """NaN inputs stay where the recurrence puts them (B=3, T=70: 32-token
+    chunks, scaled groups).
+    - A NaN in v (sequence 0, head 2, row 7, token 40) reaches that state row
+      and that row's outputs from token 40 on; everything else is bitwise
+      the clean run.
+    - A NaN gate (sequence 1, head 5, token 20) fails its group's check, so
+      that group multiplies per token, and the NaN decay reaches the whole
+      head from token 20 on; the head's first group is bitwise the clean run
+      and every other head and sequence is bitwise the clean run."""
+    print("\n  gdn_seq NaN isolation B=3 T=70", flush=True)
+    B, T = 3, 70
+    si = gi.step_inputs(3700, 0, B, T=T)
+    M = gi.state(3700, 0, B)
+    clean_M, clean_o = run_seq(g, si, M)
+    si["v"][0, 40, 2, 7] = np.nan
+    si["gate"][1, 20, 5] = np.nan
+    Mg, og = run_seq(g, si, M)
+    assert np.all(np.isnan(Mg[0, 2, 7])) and np.all(np.isnan(og[0, 40:, 2, 7]))
+    assert np.all(np.isnan(Mg[1, 5])) and np.all(np.isnan(og[1, 20:, 5]))
+    assert np.all(np.isfinite(og[1, 16:20, 5]))
+    assert np.array_equal(og[1, :16, 5], clean_o[1, :16, 5])
+    keep_M = np.ones(Mg.shape[:3], bool)
+    keep_M[0, 2, 7] = False
+    keep_M[1, 5, :] = False
+    assert np.array_equal(Mg[keep_M], clean_M[keep_M]), "state changed outside the NaN's reach"
+    keep_o = np.ones(og.shape, bool)
+    keep_o[0, 40:, 2, 7] = False
+    keep_o[1, 16:, 5, :] = False
+    assert np.array_equal(og[keep_o], clean_o[keep_o]), "outputs changed outside the NaN's reach"
