@@ -460,7 +460,8 @@ def extra_measurements(torch, g, stream, only=None):
         o = torch.empty((8, 4096, HV, D), device="cuda")
         # gdn_seq, and gdn_seq_exact (the decay multiplied into the state on
         # every token): timed in alternation after a joint warmup, best of 3
-        # rounds of 5 calls each (the clock under this VALU load drifts)
+        # rounds of 5 calls each (the clock ramps up over the first ~10 calls
+        # after the GPU has idled while the host generated the inputs)
         run = lambda exact: g.seq(si["q"], si["k"], si["v"], si["beta"], si["gate"], M, o,
                                   stream=stream, exact=exact)
         for _ in range(5):
@@ -476,6 +477,7 @@ def extra_measurements(torch, g, stream, only=None):
         # instead of every element (7 with the per-element multiply)
         flops = upd * D * D * 6
         tf = flops / (ms / 1e3) / 1e12
+        tf7 = upd * D * D * 7 / (ms / 1e3) / 1e12
         # the VALU ceiling measured at the kernel's own occupancy (one 8-wave
         # workgroup per CU, as this launch) and at 16 waves per CU
         cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -488,7 +490,10 @@ def extra_measurements(torch, g, stream, only=None):
                                        "fma_probe_TFLOPs_8_waves_per_cu": probe8,
                                        "fma_probe_TFLOPs_16_waves_per_cu": probe16,
                                        "frac_of_fma_probe_same_occupancy": tf / probe8,
-                                       "exact_ms": ms_exact}
+                                       "exact_ms": ms_exact,
+                                       "TFLOPs_at_7_flop_per_element": tf7,
+                                       "exact_TFLOPs_at_7_flop_per_element":
+                                           upd * D * D * 7 / (ms_exact / 1e3) / 1e12}
 
     # tail_b32: layer tail B=32
     if want("tail_b32"):
