@@ -5,7 +5,8 @@
  *   1. pure decay (beta = 0):       M' = exp(gate) M,   out = exp(gate) M q / sqrt(128)
  *   2. delta rule (beta=1, gate=0, unit k):  M' k = v  for every value head
  *   3. full forget (gate = -1e4):   M' = beta v k^T
- *   4. gdn_seq over 3 tokens == 3 gdn_step calls, bit for bit
+ *   4. gdn_seq over 3 tokens == 3 gdn_step calls, bit for bit, and
+ *      gdn_seq_exact over 20 tokens == 20 gdn_step calls
  *   5. argument errors: GDN_ERR_ALIGN / GDN_ERR_ALIAS before any work
  *   6. gdn_gate_transform: sigmoid(0) = 1/2 exactly, sigmoid(ln 3) = 3/4,
  *      gate = -ln 2 at a zero softplus argument, exp(gate) = 1 - beta when
@@ -144,9 +145,14 @@ int main(void) {
                 }
             }
 
-    /* 4. gdn_seq over 3 tokens == 3 gdn_step calls, bit for bit */
-    {
-        const int T = 3;
+    /* 4. gdn_seq over 3 tokens == 3 gdn_step calls, bit for bit; the same
+     *    for gdn_seq_exact over 20 tokens (past the 16-token groups) */
+    typedef int (*seq_fn)(const gdn_dims *, int32_t, int32_t, const float *, const float *,
+                          const float *, const float *, const float *, float *, float *, void *);
+    const seq_fn seq_fns[2] = {gdn_seq, gdn_seq_exact};
+    const int seq_T[2] = {3, 20};
+    for (int which = 0; which < 2; ++which) {
+        const int T = seq_T[which];
         float *qs, *ks, *vs, *bs, *gs, *os, *Ms;
         HIP_OK(hipMalloc((void **)&qs, (size_t)B * T * HK * D * 4));
         HIP_OK(hipMalloc((void **)&ks, (size_t)B * T * HK * D * 4));
@@ -167,7 +173,8 @@ int main(void) {
             }
         upload(&d, q, k, v, beta, gate, M);
         HIP_OK(hipMemcpy(Ms, M, NS * 4, hipMemcpyHostToDevice));
-        if (gdn_seq(&dims, B, T, qs, ks, vs, bs, gs, Ms, os, NULL) != GDN_OK) return fail(gdn_last_error(), 0);
+        if (seq_fns[which](&dims, B, T, qs, ks, vs, bs, gs, Ms, os, NULL) != GDN_OK)
+            return fail(gdn_last_error(), 0);
         for (int t = 0; t < T; ++t)
             if (gdn_step(&dims, B, d.q, d.k, d.v, d.beta, d.gate, d.M, d.out, NULL) != GDN_OK)
                 return fail(gdn_last_error(), 0);
@@ -175,7 +182,8 @@ int main(void) {
         HIP_OK(hipMemcpy(M2, d.M, NS * 4, hipMemcpyDeviceToHost));
         float *Mseq = malloc(NS * 4);
         HIP_OK(hipMemcpy(Mseq, Ms, NS * 4, hipMemcpyDeviceToHost));
-        if (memcmp(M2, Mseq, NS * 4) != 0) return fail("gdn_seq != 3 x gdn_step", 0);
+        if (memcmp(M2, Mseq, NS * 4) != 0)
+            return fail(which ? "gdn_seq_exact != 20 x gdn_step" : "gdn_seq != 3 x gdn_step", 0);
         free(Mseq);
         hipFree(qs); hipFree(ks); hipFree(vs); hipFree(bs); hipFree(gs); hipFree(os); hipFree(Ms);
     }
