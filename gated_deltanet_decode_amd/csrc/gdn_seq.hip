@@ -132,7 +132,8 @@ __device__ __forceinline__ void fetch_chunk(ChunkRegs<CH, NTH> &cr, const SeqArg
 // v w - ((S / c_t) . k) beta and its output scale one multiply.
 // A group runs scaled only when it is complete, all its gates are <= 0 (no
 // NaN) and its decay product is >= kMinScale (2^-63), so c_t stays normal
-// and S / c_t far from overflow; otherwise it runs with the per-token
+// and S / c_t at most 2^63.5 |S| (finite for |S| up to about 1e19; larger
+// states need the per-token form); otherwise it runs with the per-token
 // multiply.  Groups are counted from the call's first token in every launch
 // shape, so results do not depend on the shape (or on B); but a scaled
 // group's rounding differs from the per-token multiply, so its results are

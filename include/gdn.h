@@ -121,7 +121,9 @@ int gdn_step(const gdn_dims *dims, int32_t B,
  * one, multiplies per token as gdn_step does: a call in which no group
  * qualifies (T < 16, or decay stronger than that floor) is bitwise equal to
  * T gdn_step calls.  Splitting T into consecutive calls at multiples of 16
- * tokens gives bitwise the same result.
+ * tokens gives bitwise the same result.  Inside a scaled group the state is
+ * held up to 2^63.5 times larger, so states or values beyond about 1e19 in
+ * magnitude overflow there; gdn_seq_exact has the full float32 range.
  */
 int gdn_seq(const gdn_dims *dims, int32_t B, int32_t T,
             const float *q, const float *k, const float *v,
