@@ -486,8 +486,29 @@ __global__ __launch_bounds__(64 * 16 / (TPW * PARTS), WPS) void k_seq(SeqArgs a)
                     carried = false;
                 }
             }
-        } else {
+        } else if constexpr (CH < 32 && TPW == 2) {
             seq_chunk<CH, PAIR, TPW>(buf, nt, rows, r, c);
+        } else {
+            // seq_chunk()'s steps written out here: the long-sequence kernels
+            // (32-token chunks, one-tile waves) compile to a faster schedule
+            // this way (2-5 % at T = 1024-4096); the half-head kernels to a
+            // faster one through seq_chunk() (4-6 % at T <= 64, many heads)
+            VecSlice kv;
+            load_vec(kv, buf[0].k, c);
+            float p[TPW];
+            {
+                const float e0 = buf[0].e;
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) p[t] = head_part(r[t], kv, e0);
+            }
+            if (nt == CH) {
+#pragma unroll
+                for (int tt = 0; tt < CH; ++tt)
+                    seq_token<PAIR, TPW, false>(buf, tt, tt + 1 < CH, rows, r, kv, p, c);
+            } else {
+                for (int tt = 0; tt < nt; ++tt)
+                    seq_token<PAIR, TPW, false>(buf, tt, tt + 1 < nt, rows, r, kv, p, c);
+            }
         }
         __syncthreads();                 // outputs of chunk ch complete in LDS
 
