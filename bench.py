@@ -389,8 +389,15 @@ def extra_measurements(torch, g, stream, only=None):
     want = lambda c: only is None or only == c
 
     def timeit(fn, reps):
-        for _ in range(2):
+        # warm up for at least 30 ms of GPU work: after the host has spent
+        # time generating inputs the GPU clock ramps up over ~20 ms of load
+        t_end = time.perf_counter() + 0.03
+        n = 0
+        while n < 2 or time.perf_counter() < t_end:
             fn()
+            n += 1
+            if n % 4 == 0:
+                torch.cuda.synchronize()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         s.record(stream)
