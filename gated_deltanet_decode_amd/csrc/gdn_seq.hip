@@ -580,7 +580,8 @@ __global__ __launch_bounds__(64 * 16 / (TPW * PARTS), WPS) void k_seq(SeqArgs a)
 //   B = 4 T = 4096 1.36 -> 1.26, B = 64 T = 64 248 -> 219 us, B = 256
 //   T = 64 1.00 -> 0.89 ms (graph replays).  Folding c once per 32 tokens
 //   where a chunk has 32 was another 1-2 % faster but makes the bits depend
-//   on the launch shape.  8-token chunks (T < 16) keep the per-token form.
+//   on the launch shape.  8-token chunks (T < 16) keep the per-token form,
+//   and gdn_seq_exact (launch_seq's `exact`) runs every chunk per token.
 static_assert(2 * 256 == kSeqThreadsPerHead && 512 == kSeqThreadsPerHead,
               "the API bounds B * Hv by this launch's work-items per head");
 
