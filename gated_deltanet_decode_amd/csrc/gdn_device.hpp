@@ -2,9 +2,12 @@
 // of the decode path: the row layout, the DPP reduction and the per-row
 // arithmetic of the state update.  Included by the kernel sources only.
 //
-// The per-token update (Red Lite dev15c, "Pinned llama.cpp semantics"):
-//   M *= exp(gate); sk = M k; delta = (v - sk) beta; M += delta k^T;
-//   out = M q / sqrt(128)     on the transposed state M[j][i] = S[i][j].
+// The per-token update (Red Lite dev15c, "Pinned llama.cpp semantics") on the
+// transposed state M = S^T (M[j][i] = S[i][j]), with e = exp(gate):
+//   M' = e M + beta (v - e M k) k^T,   out = M' q / sqrt(128).
+// Row j of it, the unit every kernel here works on: the decay of the row,
+// its key product sk = (e M[j]) . k, the correction delta = (v[j] - sk) beta,
+// the rank-1 update e M[j] + delta k, and the read-out M'[j] . q / sqrt(128).
 //
 // Work decomposition.  Row j of a head's state depends only on that row,
 // on the head's k and q, and on v[j], beta and gate: rows never exchange
@@ -21,8 +24,10 @@
 //
 // All kernels share this arithmetic (row_token() or the parts it is split
 // into below), so a row's arithmetic is the same in the single-step kernel,
-// the multi-token kernel and the tail: a T-token gdn_seq is bitwise equal to
-// T gdn_step calls.
+// the multi-token kernels and the tail: gdn_seq_exact over T tokens is
+// bitwise equal to T gdn_step calls, and so is gdn_seq wherever it does not
+// carry a 16-token group's decay as one scale (the scaled-decay note in
+// gdn_seq.hip says when it does).
 //
 // No MFMA: the update is a sequence of rank-1 updates and matrix-vector
 // products (one multiply-add per state element per operation), which is
@@ -116,7 +121,7 @@ __device__ __forceinline__ float dot_part(const RowSlice &r, const VecSlice &w) 
     return p;
 }
 
-// Step 4 alone: the rank-1 update M[j] += d k^T of this lane's columns.
+// The rank-1 update alone: M[j] += d k^T on this lane's columns.
 __device__ __forceinline__ void update_part(RowSlice &r, float d, const VecSlice &k) {
 #pragma unroll
     for (int i = 0; i < kF4PerLane; ++i) {
@@ -127,27 +132,29 @@ __device__ __forceinline__ void update_part(RowSlice &r, float d, const VecSlice
     }
 }
 
-// One token on one state row j (steps 1-5), in the page's order.
+// One token on one state row j: decay, key product, correction, rank-1
+// update, then the read-out from the updated row.
 // Returns out[j].
 __device__ __forceinline__ float row_token(RowSlice &r, const VecSlice &k, const VecSlice &q,
                                            float e, float beta, float vj) {
 #pragma unroll
-    for (int i = 0; i < kF4PerLane; ++i) {           // 1. decay
+    for (int i = 0; i < kF4PerLane; ++i) {           // decay
         r.m[i].x *= e;
         r.m[i].y *= e;
         r.m[i].z *= e;
         r.m[i].w *= e;
     }
-    const float sk = group_sum(dot_part(r, k));       // 2. sk = M[j] . k
-    const float d = (vj - sk) * beta;                 // 3. delta
-    update_part(r, d, k);                             // 4. rank-1 update
-    return group_sum(dot_part(r, q)) * kInvSqrtD;     // 5. output, updated state
+    const float sk = group_sum(dot_part(r, k));       // key product M[j] . k
+    const float d = (vj - sk) * beta;                 // correction delta
+    update_part(r, d, k);                             // rank-1 update
+    return group_sum(dot_part(r, q)) * kInvSqrtD;     // read-out, updated row
 }
 
 // The same arithmetic split into parts, for kernels that interleave it with
-// memory traffic or with the next token: head_part() is steps 1-2 of a token
-// (decay, then the key partial), update_part() step 4, body_part() steps 4-5,
-// and pass() steps 4-5 of token t with steps 1-2 of token t+1 in one sweep
+// memory traffic or with the next token: head_part() is the decay and key
+// partial of a token, update_part() its rank-1 update, body_part() the rank-1
+// update and read-out partial, and pass() the rank-1 update and read-out of
+// token t with the decay and key partial of token t+1 in one sweep
 // over the row.  Every element sees exactly the operations of row_token(),
 // in the same order, and the partial sums accumulate in the same element
 // order, so the results are bitwise those of row_token().
@@ -184,9 +191,9 @@ __device__ __forceinline__ float body_part(RowSlice &r, float d, const VecSlice 
     return o;
 }
 
-// Steps 4-5 of token t (delta d, k, q) and steps 1-2 of token t+1 (decay en,
-// key kn): this lane's output partial of t goes to o, its key partial of t+1
-// to p.
+// Rank-1 update and read-out of token t (delta d, k, q), then the decay and
+// key product of token t+1 (decay en, key kn): this lane's output partial of
+// t goes to o, its key partial of t+1 to p.
 __device__ __forceinline__ void pass(RowSlice &r, float d, const VecSlice &k, const VecSlice &q,
                                      float en, const VecSlice &kn, float &o, float &p) {
     o = 0.0f;

@@ -273,7 +273,8 @@ __device__ __forceinline__ void scale_row(RowSlice &r, float f) {
     }
 }
 
-// Token tt of a chunk: steps 3-5 of tt and, when `next`, steps 1-2 of tt+1
+// Token tt of a chunk: correction, rank-1 update and read-out of tt and,
+// when `next`, the decay and key product of tt+1
 // (kv holds k of token tt on entry and of tt+1 on exit; p the key partials).
 // kPair: a lane's two rows sit in swapped slots (slot 0 is row A in lanes 0-3
 // of the row group and row B in lanes 4-7), so pair_sum() reduces both rows
@@ -287,7 +288,7 @@ __device__ __forceinline__ void seq_token(TokenLds *buf, int tt, bool next, cons
                                           int c, float fold = 1.0f) {
     static_assert(!kPair || TPW == 2, "pairing needs two tiles per wave");
     TokenLds &tok = buf[tt];
-    float d[TPW];                                              // step 3
+    float d[TPW];                                              // correction
     if constexpr (kScaled) {
         // v w - ((S / c) . k) beta = (v - S . k) beta / c = delta / c
         if constexpr (kPair) {
@@ -340,8 +341,9 @@ __device__ __forceinline__ void seq_token(TokenLds *buf, int tt, bool next, cons
 }
 
 // Tokens [0, nt) of the CH staged tokens at buf, with the per-token decay
-// multiply: steps 1-2 of the first, then seq_token() for each; when nt == CH
-// the loop is unrolled, so every LDS address is an immediate offset.
+// multiply: decay and key product of the first, then seq_token() for each;
+// when nt == CH the loop is unrolled, so every LDS address is an immediate
+// offset.
 template <int CH, bool PAIR, int TPW>
 __device__ __forceinline__ void seq_chunk(TokenLds *buf, int nt, const int (&rows)[TPW],
                                           RowSlice (&r)[TPW], int c) {

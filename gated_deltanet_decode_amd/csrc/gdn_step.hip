@@ -119,15 +119,15 @@ __global__ __launch_bounds__(W * 64) void k_step(StepArgs a, int n_tiles, int ep
         if constexpr (!kLateQ) load_vec(qv, qp, c);
         const float e = expf(gt);
 
-        const float sk = group_sum(head_part(r, kv, e));     // steps 1-2
+        const float sk = group_sum(head_part(r, kv, e));     // decay, key product
         if constexpr (kLateQ) {
             __builtin_amdgcn_sched_barrier(0);                // keep the q loads here
             load_vec(qv, qp, c);
             __builtin_amdgcn_sched_barrier(0);
         }
-        update_part(r, (vj - sk) * bt, kv);                   // steps 3-4
+        update_part(r, (vj - sk) * bt, kv);                   // correction, rank-1
         store_row<true>(Mrow, r, c);
-        const float o = group_sum(dot_part(r, qv)) * kInvSqrtD;   // step 5
+        const float o = group_sum(dot_part(r, qv)) * kInvSqrtD;   // read-out
         if (c == 0) a.out[static_cast<int64_t>(w.head) * D + w.row] = o;
     } while (w.next());
 }

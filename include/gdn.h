@@ -3,15 +3,14 @@
  *
  * Operation (Red Lite dev15c "Gated DeltaNet recurrent-state parity",
  * section "Pinned llama.cpp semantics"): for every sequence b and value head
- * h, with key head kh = h % n_k_heads, e = exp(gate[b][h]) and the transposed
- * state M[j][i] = S[i][j] (j = value dim, i = key dim):
- *   1. M *= e
- *   2. sk[j]    = sum_i M[j][i] * k[kh][i]        (decayed M)
- *   3. delta[j] = (v[h][j] - sk[j]) * beta[b][h]
- *   4. M[j][i] += delta[j] * k[kh][i]
- *   5. out[j]   = sum_i M[j][i] * q[kh][i] / sqrt(d_k)   (updated M)
- * The page's geometry is d_k = d_v = 128, 16 key heads, 32 value heads,
- * a 2 MiB F32 state per sequence and layer.
+ * h, with key head kh = h % n_k_heads, e = exp(gate[b][h]), beta = beta[b][h]
+ * and the state kept transposed, M = S^T (row j = value coordinate, column
+ * i = key coordinate; M[j][i] = S[i][j]), one token does
+ *     M' = e M + beta (v - e M k) k^T,        out = M' q / sqrt(d_k)
+ * with k = k[kh], q = q[kh], v = v[h]: the delta rule applied to the decayed
+ * state, and the read-out taken from the new state.  The page's geometry is
+ * d_k = d_v = 128, 16 key heads, 32 value heads, a 2 MiB F32 state per
+ * sequence and layer.
  *
  * Conventions shared by every call
  *   - All tensors are float32 (IEEE binary32), row-major and contiguous.
@@ -86,7 +85,7 @@ typedef struct gdn_tail_params {
 } gdn_tail_params;
 
 /*
- * gdn_step - one token for B sequences (dev15c, steps 1-5 above).
+ * gdn_step - one token for B sequences (dev15c, the update above).
  *   q, k   [B][n_k_heads][d_k]   (L2-normalised by the caller)
  *   v      [B][n_v_heads][d_v]
  *   beta   [B][n_v_heads]        update strength, used as given

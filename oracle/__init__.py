@@ -63,16 +63,19 @@ class Oracle:
         L.oracle_gdn_step_S.argtypes = L.oracle_gdn_step_M.argtypes
         L.oracle_gdn_step_f64.argtypes = [_i32, *dims5[1:], *vec5, _f64p, _f64p]
         L.oracle_gdn_seq.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, *vec5, _f32p, _f32p]
+        L.oracle_gdn_seq_f64.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, *vec5, _f64p, _f64p]
         L.oracle_gdn_pair.argtypes = [_i32, *dims5[1:], *vec5, _f32p, _f32p, _f32p]
         L.oracle_conv_silu.argtypes = [_i32, _i32, _i32, _f32p, _f32p, _f32p, _f32p]
         L.oracle_l2norm_rows.argtypes = [_i32, _i32, _f32p]
         L.oracle_gated_rmsnorm.argtypes = [_i32, _i32, _i32, ctypes.c_float,
                                            _f32p, _f32p, _f32p, _f32p]
         L.oracle_layer_tail.argtypes = [_i32] * 7 + [ctypes.c_float] + [_f32p] * 11
+        L.oracle_layer_tail_pair.argtypes = [_i32] * 7 + [ctypes.c_float] + [_f32p] * 11
         L.oracle_gate_transform.argtypes = [_i32, _i32] + [_f32p] * 5
         for name in ("oracle_gdn_step_M", "oracle_gdn_step_S", "oracle_gdn_step_f64",
-                     "oracle_gdn_seq", "oracle_gdn_pair", "oracle_conv_silu", "oracle_l2norm_rows",
-                     "oracle_gated_rmsnorm", "oracle_layer_tail", "oracle_gate_transform"):
+                     "oracle_gdn_seq", "oracle_gdn_seq_f64", "oracle_gdn_pair", "oracle_conv_silu",
+                     "oracle_l2norm_rows", "oracle_gated_rmsnorm", "oracle_layer_tail",
+                     "oracle_layer_tail_pair", "oracle_gate_transform"):
             getattr(L, name).restype = None
         self.lib = L
 
@@ -128,6 +131,17 @@ class Oracle:
                                 _p32(beta), _p32(gate), _p32(M), _p32(out))
         return out
 
+    def seq_f64(self, q, k, v, beta, gate, M64):
+        """Binary64 shadow of seq: M64 (float64) updated in place; returns
+        float64 out [B][T][Hv][dv]."""
+        B, T, Hk, dk = q.shape
+        _, _, Hv, dv = v.shape
+        assert M64.shape == (B, Hv, dv, dk)
+        out = np.empty((B, T, Hv, dv), np.float64)
+        self.lib.oracle_gdn_seq_f64(B, T, Hv, Hk, dk, dv, _p32(q), _p32(k), _p32(v),
+                                    _p32(beta), _p32(gate), _p64(M64), _p64(out))
+        return out
+
     def pair(self, q, k, v, beta, gate, M):
         """[linear_core] gdn_pair: q,k [B][2][Hk][dk], v [B][2][Hv][dv],
         beta/gate [B][2][Hv].  M is committed in place (position 1); returns
@@ -181,6 +195,28 @@ class Oracle:
                                    _p32(beta), _p32(gate), _p32(M), _p32(z),
                                    _p32(norm_w), _p32(y), _p32(qkv), _p32(core))
         return y, qkv, core
+
+    def layer_tail_pair(self, x, conv_w, conv_state, beta, gate, M, z, norm_w,
+                        Hk, dk, group=128, eps=1e-6):
+        """[linear_core] gdn_pair over the whole tail.  x [B][2][C],
+        beta/gate [B][2][Hv], z [B][2][Hv*dv].  conv_state and M are
+        committed in place (position 1); returns (y [B][2][Hv*dv],
+        conv_state_next, M_next), the tentative ring and state after
+        position 2."""
+        B, two, C = x.shape
+        assert two == 2
+        K = conv_w.shape[1]
+        _, Hv, dv, _ = M.shape
+        assert C == 2 * Hk * dk + Hv * dv
+        assert conv_state.shape == (B, K - 1, C)
+        y = np.empty((B, 2, Hv * dv), np.float32)
+        csn = np.empty_like(conv_state)
+        Mn = np.empty_like(M)
+        self.lib.oracle_layer_tail_pair(B, Hv, Hk, dk, dv, K, group, eps,
+                                        _p32(x), _p32(conv_w), _p32(conv_state), _p32(csn),
+                                        _p32(beta), _p32(gate), _p32(M), _p32(Mn),
+                                        _p32(z), _p32(norm_w), _p32(y))
+        return y, csn, Mn
 
     # -- the beta/alpha parameter transforms ------------------------------
     def gate_transform(self, ba, a_log, dt_bias):

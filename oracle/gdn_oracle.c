@@ -2,9 +2,9 @@
  * gdn_oracle.c - plain C99 CPU oracle (TEST INFRASTRUCTURE ONLY; see
  * gdn_oracle.h for the sources, the layouts and who may call this).
  *
- * Written to be read against the pages, not to be fast: one loop per printed
- * step, sequential binary32 sums, a separate multiply and add (the build uses
- * -ffp-contract=off), libm expf/sqrtf.
+ * Written to be read against the pages, not to be fast: sequential binary32
+ * sums, a separate multiply and add (the build uses -ffp-contract=off), libm
+ * expf/sqrtf.
  */
 #include "gdn_oracle.h"
 
@@ -13,54 +13,56 @@
 #include <stdlib.h>
 #include <string.h>
 
+/* Sequential binary32 dot product of a[0], a[step], ..., a[(n-1)*step]
+ * with b[0..n-1]: one rounded product and one rounded sum per term, in
+ * index order. */
+static float dot(const float *a, size_t step, const float *b, int32_t n)
+{
+    float s = 0.0f;
+    int32_t i;
+    for (i = 0; i < n; ++i)
+        s = s + a[(size_t)i * step] * b[i];
+    return s;
+}
+
 /*
- * One value head, one token, transposed state M[j][i] = S[i][j]
- * ([dev15c] "Pinned llama.cpp semantics"):
- *   1. M *= exp(gate)
- *   2. sk[j]    = dot(M[j], k)            (uses the decayed M)
- *   3. delta[j] = (v[j] - sk[j]) * beta
- *   4. M[j][i] += delta[j] * k[i]
- *   5. out[j]   = dot(M[j], q) / sqrt(dk) (uses the updated M)
- * The page writes sqrt(128) with 128 the state/key dimension; dk is that
- * dimension, generalised only so tiny heads can be brute-forced.
+ * One value head, one token ([dev15c] "Pinned llama.cpp semantics").
+ *
+ * The head's state is a dk x dv matrix S (key coordinate i, value coordinate
+ * j), stored transposed as M = S^T, so that M[j] (row j, dk contiguous
+ * floats) is everything value coordinate j remembers.  With e = exp(gate),
+ * the token's effect in matrix form is
+ *
+ *     M' = e M + beta (v - e M k) k^T          (delta rule on the decayed state)
+ *     out = M' q / sqrt(dk)                    (read-out from the new state)
+ *
+ * dk is the state/key dimension, 128 on the page; it is a parameter only so
+ * that tiny heads can be brute-forced.  Row j of M' depends on row j of M,
+ * on the shared k, q, beta, e and on v[j] alone, so the update is evaluated
+ * row by row: the decayed row r = e M[j], its correction coefficient
+ * c = beta (v[j] - r.k) (the value the page calls delta), the new row
+ * r + c k, and out[j] = (r + c k).q / sqrt(dk).
  */
-static void head_step_M(int32_t dk, int32_t dv,
-                        const float *q, const float *k, const float *v,
-                        float beta, float gate, float *M, float *out,
-                        float *delta)
+static void head_token_M(int32_t dk, int32_t dv,
+                         const float *q, const float *k, const float *v,
+                         float beta, float gate, float *M, float *out,
+                         float *delta)
 {
     const float e = expf(gate);
-    const float scale = sqrtf((float)dk);
+    const float rs = sqrtf((float)dk);
     int32_t i, j;
 
-    /* step 1: decay */
-    for (j = 0; j < dv; ++j)
-        for (i = 0; i < dk; ++i)
-            M[(size_t)j * dk + i] = M[(size_t)j * dk + i] * e;
-
     for (j = 0; j < dv; ++j) {
-        float *row = M + (size_t)j * dk;
-        float sk = 0.0f;
-        float d;
-        /* step 2: sk[j] = M[j] . k */
+        float *m = M + (size_t)j * dk;
+        float c;
         for (i = 0; i < dk; ++i)
-            sk = sk + row[i] * k[i];
-        /* step 3: delta */
-        d = (v[j] - sk) * beta;
+            m[i] = m[i] * e;
+        c = (v[j] - dot(m, 1, k, dk)) * beta;
         if (delta)
-            delta[j] = d;
-        /* step 4: rank-1 update of row j */
+            delta[j] = c;
         for (i = 0; i < dk; ++i)
-            row[i] = row[i] + d * k[i];
-    }
-
-    /* step 5: output from the updated state */
-    for (j = 0; j < dv; ++j) {
-        const float *row = M + (size_t)j * dk;
-        float s = 0.0f;
-        for (i = 0; i < dk; ++i)
-            s = s + row[i] * q[i];
-        out[j] = s / scale;
+            m[i] = m[i] + c * k[i];
+        out[j] = dot(m, 1, q, dk) / rs;
     }
 }
 
@@ -78,58 +80,48 @@ void oracle_gdn_step_M(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv
         for (h = 0; h < Hv; ++h) {
             const int32_t kh = key_head_of(h, Hk);
             const size_t bh = (size_t)b * Hv + h;
-            head_step_M(dk, dv,
-                        q + ((size_t)b * Hk + kh) * dk,
-                        k + ((size_t)b * Hk + kh) * dk,
-                        v + bh * dv,
-                        beta[bh], gate[bh],
-                        M + bh * dv * dk,
-                        out + bh * dv,
-                        delta ? delta + bh * dv : NULL);
+            head_token_M(dk, dv,
+                         q + ((size_t)b * Hk + kh) * dk,
+                         k + ((size_t)b * Hk + kh) * dk,
+                         v + bh * dv,
+                         beta[bh], gate[bh],
+                         M + bh * dv * dk,
+                         out + bh * dv,
+                         delta ? delta + bh * dv : NULL);
         }
     }
 }
 
 /*
- * The same update on the non-transposed state S[i][j] (i = key dim,
- * j = value dim), which the transposed layout M[j][i] = S[i][j] stores:
- *   S *= e;  sk = S^T k;  delta = (v - sk) beta;  S += k delta^T;
- *   out = S^T q / sqrt(dk).
+ * The same token on the non-transposed state S (dk rows of dv floats), in
+ * whole-matrix order rather than row by row:
+ *     S <- e S;   c = beta (v - S^T k);   S <- S + k c^T;   out = S^T q / sqrt(dk).
+ * The products S^T k and S^T q run down the columns of S.
  */
-static void head_step_S(int32_t dk, int32_t dv,
-                        const float *q, const float *k, const float *v,
-                        float beta, float gate, float *S, float *out,
-                        float *delta)
+static void head_token_S(int32_t dk, int32_t dv,
+                         const float *q, const float *k, const float *v,
+                         float beta, float gate, float *S, float *out,
+                         float *delta)
 {
     const float e = expf(gate);
-    const float scale = sqrtf((float)dk);
-    float *d = (float *)malloc((size_t)dv * sizeof(float));
+    const float rs = sqrtf((float)dk);
+    float *c = (float *)malloc((size_t)dv * sizeof(float));
     int32_t i, j;
 
     for (i = 0; i < dk; ++i)
         for (j = 0; j < dv; ++j)
             S[(size_t)i * dv + j] = S[(size_t)i * dv + j] * e;
-
     for (j = 0; j < dv; ++j) {
-        float sk = 0.0f;
-        for (i = 0; i < dk; ++i)
-            sk = sk + S[(size_t)i * dv + j] * k[i];
-        d[j] = (v[j] - sk) * beta;
+        c[j] = (v[j] - dot(S + j, (size_t)dv, k, dk)) * beta;
         if (delta)
-            delta[j] = d[j];
+            delta[j] = c[j];
     }
-
     for (i = 0; i < dk; ++i)
         for (j = 0; j < dv; ++j)
-            S[(size_t)i * dv + j] = S[(size_t)i * dv + j] + k[i] * d[j];
-
-    for (j = 0; j < dv; ++j) {
-        float s = 0.0f;
-        for (i = 0; i < dk; ++i)
-            s = s + S[(size_t)i * dv + j] * q[i];
-        out[j] = s / scale;
-    }
-    free(d);
+            S[(size_t)i * dv + j] = S[(size_t)i * dv + j] + k[i] * c[j];
+    for (j = 0; j < dv; ++j)
+        out[j] = dot(S + j, (size_t)dv, q, dk) / rs;
+    free(c);
 }
 
 void oracle_gdn_step_S(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv,
@@ -142,47 +134,46 @@ void oracle_gdn_step_S(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv
         for (h = 0; h < Hv; ++h) {
             const int32_t kh = key_head_of(h, Hk);
             const size_t bh = (size_t)b * Hv + h;
-            head_step_S(dk, dv,
-                        q + ((size_t)b * Hk + kh) * dk,
-                        k + ((size_t)b * Hk + kh) * dk,
-                        v + bh * dv,
-                        beta[bh], gate[bh],
-                        S + bh * dk * dv,
-                        out + bh * dv,
-                        delta ? delta + bh * dv : NULL);
+            head_token_S(dk, dv,
+                         q + ((size_t)b * Hk + kh) * dk,
+                         k + ((size_t)b * Hk + kh) * dk,
+                         v + bh * dv,
+                         beta[bh], gate[bh],
+                         S + bh * dk * dv,
+                         out + bh * dv,
+                         delta ? delta + bh * dv : NULL);
         }
     }
 }
 
-/* Binary64 shadow of head_step_M. */
-static void head_step_f64(int32_t dk, int32_t dv,
-                          const float *q, const float *k, const float *v,
-                          float beta, float gate, double *M, double *out)
+/* Binary64 shadow of head_token_M: the same row form with f32 inputs
+ * promoted and the state, sums and output in double. */
+static double dot64(const double *a, const float *b, int32_t n)
+{
+    double s = 0.0;
+    int32_t i;
+    for (i = 0; i < n; ++i)
+        s = s + a[i] * (double)b[i];
+    return s;
+}
+
+static void head_token_f64(int32_t dk, int32_t dv,
+                           const float *q, const float *k, const float *v,
+                           float beta, float gate, double *M, double *out)
 {
     const double e = exp((double)gate);
-    const double scale = sqrt((double)dk);
+    const double rs = sqrt((double)dk);
     int32_t i, j;
 
-    for (j = 0; j < dv; ++j)
-        for (i = 0; i < dk; ++i)
-            M[(size_t)j * dk + i] = M[(size_t)j * dk + i] * e;
-
     for (j = 0; j < dv; ++j) {
-        double *row = M + (size_t)j * dk;
-        double sk = 0.0, d;
+        double *m = M + (size_t)j * dk;
+        double c;
         for (i = 0; i < dk; ++i)
-            sk = sk + row[i] * (double)k[i];
-        d = ((double)v[j] - sk) * (double)beta;
+            m[i] = m[i] * e;
+        c = ((double)v[j] - dot64(m, k, dk)) * (double)beta;
         for (i = 0; i < dk; ++i)
-            row[i] = row[i] + d * (double)k[i];
-    }
-
-    for (j = 0; j < dv; ++j) {
-        const double *row = M + (size_t)j * dk;
-        double s = 0.0;
-        for (i = 0; i < dk; ++i)
-            s = s + row[i] * (double)q[i];
-        out[j] = s / scale;
+            m[i] = m[i] + c * (double)k[i];
+        out[j] = dot64(m, q, dk) / rs;
     }
 }
 
@@ -196,13 +187,38 @@ void oracle_gdn_step_f64(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t 
         for (h = 0; h < Hv; ++h) {
             const int32_t kh = key_head_of(h, Hk);
             const size_t bh = (size_t)b * Hv + h;
-            head_step_f64(dk, dv,
-                          q + ((size_t)b * Hk + kh) * dk,
-                          k + ((size_t)b * Hk + kh) * dk,
-                          v + bh * dv,
-                          beta[bh], gate[bh],
-                          M + bh * dv * dk,
-                          out + bh * dv);
+            head_token_f64(dk, dv,
+                           q + ((size_t)b * Hk + kh) * dk,
+                           k + ((size_t)b * Hk + kh) * dk,
+                           v + bh * dv,
+                           beta[bh], gate[bh],
+                           M + bh * dv * dk,
+                           out + bh * dv);
+        }
+    }
+}
+
+/* [linear_core] the binary64 shadow over T positions in order, state carried
+ * (the yardstick for long sequences). */
+void oracle_gdn_seq_f64(int32_t B, int32_t T, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv,
+                        const float *q, const float *k, const float *v,
+                        const float *beta, const float *gate,
+                        double *M, double *out)
+{
+    int32_t b, t, h;
+    for (b = 0; b < B; ++b) {
+        for (t = 0; t < T; ++t) {
+            const size_t bt = (size_t)b * T + t;
+            for (h = 0; h < Hv; ++h) {
+                const int32_t kh = key_head_of(h, Hk);
+                head_token_f64(dk, dv,
+                               q + (bt * Hk + kh) * dk,
+                               k + (bt * Hk + kh) * dk,
+                               v + (bt * Hv + h) * dv,
+                               beta[bt * Hv + h], gate[bt * Hv + h],
+                               M + ((size_t)b * Hv + h) * dv * dk,
+                               out + (bt * Hv + h) * dv);
+            }
         }
     }
 }
@@ -220,7 +236,7 @@ void oracle_gdn_seq(int32_t B, int32_t T, int32_t Hv, int32_t Hk, int32_t dk, in
             const size_t bt = (size_t)b * T + t;
             for (h = 0; h < Hv; ++h) {
                 const int32_t kh = key_head_of(h, Hk);
-                head_step_M(dk, dv,
+                head_token_M(dk, dv,
                             q + (bt * Hk + kh) * dk,
                             k + (bt * Hk + kh) * dk,
                             v + (bt * Hv + h) * dv,
@@ -250,7 +266,7 @@ void oracle_gdn_pair(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv,
                 const size_t bp = (size_t)b * 2 + p;
                 if (p == 1)
                     memcpy(Nh, Mh, (size_t)dv * dk * sizeof(float));
-                head_step_M(dk, dv,
+                head_token_M(dk, dv,
                             q + (bp * Hk + kh) * dk,
                             k + (bp * Hk + kh) * dk,
                             v + (bp * Hv + h) * dv,
@@ -377,6 +393,47 @@ void oracle_layer_tail(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv
     free(k);
     free(v);
     free(o);
+}
+
+/*
+ * [linear_core] gdn_pair applied to the whole recurrent branch: "lane 1
+ * commits into state, lane 2 is tentative in scratch (ring + S move
+ * together)".  Position 1 is one layer tail on the committed conv ring and
+ * state.  Position 2 is one layer tail that starts from what position 1
+ * committed, run on copies: its ring and state go to the tentative buffers,
+ * so the committed ones stay as position 1 left them.
+ *   x [B][2][C]; beta, gate [B][2][Hv]; z, y [B][2][Hv*dv]
+ *   conv_state [B][K-1][C] in/out (committed), conv_state_next out (tentative)
+ *   M [B][Hv][dv][dk] in/out (committed), M_next out (tentative)
+ */
+void oracle_layer_tail_pair(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv,
+                            int32_t K, int32_t group, float eps,
+                            const float *x, const float *conv_w,
+                            float *conv_state, float *conv_state_next,
+                            const float *beta, const float *gate,
+                            float *M, float *M_next,
+                            const float *z, const float *norm_w, float *y)
+{
+    const int32_t nv = Hv * dv;
+    const int32_t C = 2 * Hk * dk + nv;
+    const size_t ring = (size_t)(K - 1) * C;
+    const size_t st = (size_t)Hv * dv * dk;
+    int32_t b, p;
+    for (b = 0; b < B; ++b) {
+        for (p = 0; p < 2; ++p) {
+            const size_t bp = 2 * (size_t)b + p;
+            float *cs = (p == 0 ? conv_state : conv_state_next) + (size_t)b * ring;
+            float *Mb = (p == 0 ? M : M_next) + (size_t)b * st;
+            if (p == 1) {
+                memcpy(cs, conv_state + (size_t)b * ring, ring * sizeof(float));
+                memcpy(Mb, M + (size_t)b * st, st * sizeof(float));
+            }
+            oracle_layer_tail(1, Hv, Hk, dk, dv, K, group, eps,
+                              x + bp * C, conv_w, cs,
+                              beta + bp * Hv, gate + bp * Hv, Mb,
+                              z + bp * nv, norm_w, y + bp * nv, NULL, NULL);
+        }
+    }
 }
 
 /* ---------------------------------------------------------------------

@@ -10,7 +10,7 @@
  * Sources (the pages this follows; cited by page title and section):
  *   [dev15c]  "Red Lite dev15c - Gated DeltaNet recurrent-state parity",
  *             sections "Scope" (geometry) and "Pinned llama.cpp semantics"
- *             (head broadcast, transposed layout, the five per-token steps,
+ *             (head broadcast, transposed layout, the per-token update,
  *             output from the updated state).
  *   [dev15e]  "Red Lite dev15e - complete recurrent DeltaNet layer
  *             composition", the stage list at the top of the page and
@@ -40,7 +40,8 @@
  *   M      [B][Hv][dv][dk]      transposed state, M[j][i] = S[i][j]
  *   S      [B][Hv][dk][dv]      non-transposed state (oracle_gdn_step_S only)
  *   out    [B][Hv][dv]          (seq: [B][T][Hv][dv])
- *   delta  [B][Hv][dv]          optional debug output of step 3; NULL = skip
+ *   delta  [B][Hv][dv]          optional debug output: the correction
+ *                               coefficient beta (v - e M k); NULL = skip
  */
 #ifndef GDN_ORACLE_H
 #define GDN_ORACLE_H
@@ -51,13 +52,14 @@
 extern "C" {
 #endif
 
-/* [dev15c] five-step update on the transposed state M (the authority). */
+/* [dev15c] one token on the transposed state M (the authority):
+ *   M' = e M + beta (v - e M k) k^T, out = M' q / sqrt(dk), e = exp(gate). */
 void oracle_gdn_step_M(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv,
                        const float *q, const float *k, const float *v,
                        const float *beta, const float *gate,
                        float *M, float *out, float *delta);
 
-/* [dev15c] the same update written on the non-transposed state S[i][j]. */
+/* [dev15c] the same token written on the non-transposed state S[i][j]. */
 void oracle_gdn_step_S(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv,
                        const float *q, const float *k, const float *v,
                        const float *beta, const float *gate,
@@ -69,6 +71,14 @@ void oracle_gdn_step_f64(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t 
                          const float *q, const float *k, const float *v,
                          const float *beta, const float *gate,
                          double *M, double *out);
+
+/* [linear_core] the binary64 shadow over T positions in order (state and
+ * outputs in double; f32 inputs promoted), used as the error yardstick of
+ * long sequences. */
+void oracle_gdn_seq_f64(int32_t B, int32_t T, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv,
+                        const float *q, const float *k, const float *v,
+                        const float *beta, const float *gate,
+                        double *M, double *out);
 
 /* [linear_core] gdn_forward_batch: T positions in order, state carried. */
 void oracle_gdn_seq(int32_t B, int32_t T, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv,
@@ -109,7 +119,7 @@ void oracle_gated_rmsnorm(int32_t rows, int32_t n, int32_t group, float eps,
 
 /* [dev15e] recurrent-branch tail for one token, stages in page order:
  * conv-state shift + conv1d + SiLU, Q/K/V split ([Q | K | V] contiguous),
- * per-head Q/K L2, the five-step state update, gated RMSNorm x SiLU(z).
+ * per-head Q/K L2, the state update, gated RMSNorm x SiLU(z).
  *   x [B][C] with C = 2*Hk*dk + Hv*dv; conv_w [C][K]; conv_state [B][K-1][C]
  *   beta, gate [B][Hv]; M [B][Hv][dv][dk]; z, y [B][Hv*dv]; norm_w [group]
  *   qkv_out  [B][C]        optional: normalized Q | K | V fed to the step
@@ -120,6 +130,20 @@ void oracle_layer_tail(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv
                        const float *beta, const float *gate, float *M,
                        const float *z, const float *norm_w, float *y,
                        float *qkv_out, float *core_out);
+
+/* [linear_core] gdn_pair over the whole tail ("ring + S move together"):
+ * position 1 commits conv ring and state; position 2 runs from the committed
+ * ones and writes its ring and state to the tentative buffers.
+ *   x [B][2][C]; beta, gate [B][2][Hv]; z, y [B][2][Hv*dv]
+ *   conv_state [B][K-1][C] in/out; conv_state_next [B][K-1][C] out
+ *   M [B][Hv][dv][dk] in/out; M_next [B][Hv][dv][dk] out */
+void oracle_layer_tail_pair(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv,
+                            int32_t K, int32_t group, float eps,
+                            const float *x, const float *conv_w,
+                            float *conv_state, float *conv_state_next,
+                            const float *beta, const float *gate,
+                            float *M, float *M_next,
+                            const float *z, const float *norm_w, float *y);
 
 /* [dev15a] beta/alpha parameter transforms (the pages name them; the
  * formula is a reading, see the definition):

@@ -50,7 +50,7 @@ def _rand_step(rng, B, Hv, Hk, d, state_scale=0.1):
 
 # --------------------------------------------------------------------- step
 def pin_exact_dyadic(o):
-    """dev15c steps 1-5 on a 4x4 head whose every intermediate is an exact
+    """The dev15c update on a 4x4 head whose every intermediate is an exact
     binary32 dyadic: gate=0 (decay factor exactly 1), beta=1/2, sqrt(4)=2.
     Expected values come from the matrix closed form
         S' = e (I - beta k k^T) S + beta k v^T,   out = S'^T q / sqrt(d)
@@ -91,7 +91,7 @@ def pin_exact_dyadic(o):
 
 def pin_closed_form_tiny_heads(o):
     """Brute force in long double of the dense closed form derived from the
-    five dev15c steps, on tiny heads (d in 1,2,3,4,8; 2 key heads, 4 value
+    dev15c update, on tiny heads (d in 1,2,3,4,8; 2 key heads, 4 value
     heads, value head h on key head h % 2): f32 oracle within 1e-6 abs,
     f64 shadow within 1e-12."""
     rng = np.random.default_rng(11)
@@ -267,6 +267,50 @@ def pin_seq_is_repeated_step(o):
         ot = o.step_M(qs[t], ks[t], vs[t], bs[t], gs[t], Mr)
         assert np.array_equal(out[:, t], ot), f"seq out differs from step at t={t}"
     assert np.array_equal(Ms, Mr), "seq final state differs from repeated steps"
+
+
+def pin_seq_f64_closed_form(o):
+    """The binary64 sequence: over 6 positions on tiny heads (d in 1, 3, 8;
+    2 key / 4 value heads) it follows the dense closed form
+    S_t = e_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,
+    out_t = S_t^T q_t / sqrt(d), iterated in long double, within 1e-12; and
+    at the page geometry it equals the binary64 step applied to the positions
+    in order (bitwise)."""
+    rng = np.random.default_rng(24)
+    LD = np.longdouble
+    T = 6
+    for d in (1, 3, 8):
+        B, Hv, Hk = 2, 4, 2
+        steps = [_rand_step(rng, B, Hv, Hk, d, state_scale=0.5) for _ in range(T)]
+        M0 = steps[0][5]
+        st = lambda i: np.ascontiguousarray(np.stack([s[i] for s in steps], axis=1))
+        q, k, v, beta, gate = (st(i) for i in range(5))
+        M64 = M0.astype(np.float64)
+        out = o.seq_f64(q, k, v, beta, gate, M64)
+        for b in range(B):
+            for h in range(Hv):
+                kh = h % Hk
+                S = M0[b, h].T.astype(LD)
+                for t in range(T):
+                    kk = k[b, t, kh].astype(LD)
+                    e = np.exp(LD(gate[b, t, h]))
+                    bt = LD(beta[b, t, h])
+                    S = e * (np.eye(d, dtype=LD) - bt * np.outer(kk, kk)) @ S \
+                        + bt * np.outer(kk, v[b, t, h].astype(LD))
+                    on = S.T @ q[b, t, kh].astype(LD) / np.sqrt(LD(d))
+                    assert np.max(np.abs(out[b, t, h] - on)) <= 1e-12, f"f64 seq out d={d} t={t}"
+                assert np.max(np.abs(M64[b, h].T - S)) <= 1e-12, f"f64 seq state d={d}"
+    B, T, Hv, Hk, d = 1, 3, 32, 16, 128
+    si = gi.step_inputs(25, 0, B, T=T)
+    M0 = gi.state(25, 0, B).astype(np.float64)
+    Ms = M0.copy()
+    out = o.seq_f64(si["q"], si["k"], si["v"], si["beta"], si["gate"], Ms)
+    Mr = M0.copy()
+    for t in range(T):
+        ot = o.step_f64(*(np.ascontiguousarray(si[n][:, t]) for n in ("q", "k", "v", "beta", "gate")),
+                        Mr)
+        assert np.array_equal(out[:, t], ot), f"f64 seq out differs from f64 step at t={t}"
+    assert np.array_equal(Ms, Mr), "f64 seq state differs from repeated f64 steps"
 
 
 def pin_pair_is_commit_then_tentative_step(o):
@@ -453,6 +497,49 @@ def pin_tail_composition(o):
     assert np.array_equal(cs, cs1) and np.array_equal(M, M1), "tail caches"
     assert np.array_equal(qkv, np.concatenate([Q.reshape(B, qk), Kk.reshape(B, qk), V.reshape(B, vw)], 1)), "qkv"
     assert np.array_equal(core, out) and np.array_equal(y, y1), "tail outputs"
+
+
+def pin_tail_pair_ring_and_state_move_together(o):
+    """linear_core gdn_pair over the tail ("ring + S move together"):
+      * the committed conv ring holds [cs_1, cs_2, x_1] and the tentative one
+        [cs_2, x_1, x_2] (the last K-1 raw inputs after each position,
+        bitwise, independent of any arithmetic);
+      * the committed ring, state and y_1 are those of one layer tail at
+        position 1, and the tentative ring, state and y_2 those of one layer
+        tail at position 2 started from them (bitwise);
+      * with beta = 0 at both positions the state only decays: committed
+        e_1 M, tentative e_2 e_1 M (f64, within 1e-6 relative)."""
+    Hv, Hk, d = G("value_heads"), G("key_heads"), G("state_key_dim")
+    B = 2
+    t1, t2 = gi.tail_inputs(26, B, slot=0), gi.tail_inputs(26, B, slot=1)
+    cs0 = t1["conv_state"].copy()
+    M0 = gi.state(26, 0, B)
+    pr = lambda n: np.ascontiguousarray(np.stack([t1[n], t2[n]], axis=1))
+    x, beta, gate, z = pr("x"), pr("beta"), pr("gate"), pr("z")
+    cs, M = cs0.copy(), M0.copy()
+    y, csn, Mn = o.layer_tail_pair(x, t1["conv_w"], cs, beta, gate, M, z, t1["norm_w"], Hk, d)
+    assert np.array_equal(cs, np.concatenate([cs0[:, 1:], t1["x"][:, None]], axis=1)), \
+        "committed ring is not [cs_1, cs_2, x_1]"
+    assert np.array_equal(csn, np.concatenate([cs0[:, 2:], t1["x"][:, None], t2["x"][:, None]],
+                                              axis=1)), "tentative ring is not [cs_2, x_1, x_2]"
+    cs1, M1 = cs0.copy(), M0.copy()
+    y1, _, _ = o.layer_tail(t1["x"], t1["conv_w"], cs1, t1["beta"], t1["gate"], M1, t1["z"],
+                            t1["norm_w"], Hk, d)
+    cs2, M2 = cs1.copy(), M1.copy()
+    y2, _, _ = o.layer_tail(t2["x"], t1["conv_w"], cs2, t2["beta"], t2["gate"], M2, t2["z"],
+                            t1["norm_w"], Hk, d)
+    assert np.array_equal(cs, cs1) and np.array_equal(M, M1), "committed lane is not position 1"
+    assert np.array_equal(csn, cs2) and np.array_equal(Mn, M2), "tentative lane is not position 2"
+    assert np.array_equal(y[:, 0], y1) and np.array_equal(y[:, 1], y2), "pair outputs"
+    beta0 = np.zeros_like(beta)
+    M = M0.copy()
+    _, _, Mn = o.layer_tail_pair(x, t1["conv_w"], cs0.copy(), beta0, gate, M, z, t1["norm_w"],
+                                 Hk, d)
+    e = np.exp(gate.astype(np.float64))
+    w1 = e[:, 0, :, None, None] * M0
+    w2 = e[:, 1, :, None, None] * w1
+    rel = lambda a, w: np.max(np.abs(a - w) / np.maximum(np.abs(w), 1e-30))
+    assert rel(M, w1) <= 1e-6 and rel(Mn, w2) <= 1e-6, "decay-only pair"
 
 
 def pin_printed_constants(o):

@@ -15,21 +15,34 @@ import oracle
 
 # (name, original text, planted text): the first occurrence is replaced.
 MUTANTS = [
-    ("delta_sign", "d = (v[j] - sk) * beta;", "d = (sk - v[j]) * beta;"),
-    ("beta_dropped", "d = (v[j] - sk) * beta;", "d = (v[j] - sk);"),
-    ("rank1_update_dropped", "row[i] = row[i] + d * k[i];", "row[i] = row[i] + 0.0f * d * k[i];"),
-    ("decay_dropped", "M[(size_t)j * dk + i] = M[(size_t)j * dk + i] * e;",
-     "M[(size_t)j * dk + i] = M[(size_t)j * dk + i];"),
+    ("delta_sign", "c = (v[j] - dot(m, 1, k, dk)) * beta;", "c = (dot(m, 1, k, dk) - v[j]) * beta;"),
+    ("beta_dropped", "c = (v[j] - dot(m, 1, k, dk)) * beta;", "c = (v[j] - dot(m, 1, k, dk));"),
+    ("rank1_update_dropped", "m[i] = m[i] + c * k[i];", "m[i] = m[i] + 0.0f * c * k[i];"),
+    ("decay_dropped", "m[i] = m[i] * e;", "m[i] = m[i];"),
     ("decay_squared", "const float e = expf(gate);", "const float e = expf(2.0f * gate);"),
-    ("sk_transposed_operand", "sk = sk + row[i] * k[i];", "sk = sk + M[(size_t)i * dk + j] * k[i];"),
-    ("out_uses_k", "s = s + row[i] * q[i];", "s = s + row[i] * k[i];"),
-    ("out_unscaled", "out[j] = s / scale;", "out[j] = s;"),
-    ("out_scale_dv", "const float scale = sqrtf((float)dk);", "const float scale = sqrtf((float)(dk + 1));"),
+    ("sk_transposed_operand", "c = (v[j] - dot(m, 1, k, dk)) * beta;",
+     "c = (v[j] - dot(M + j, (size_t)dk, k, dk)) * beta;"),
+    ("sk_before_decay", "for (i = 0; i < dk; ++i)\n            m[i] = m[i] * e;\n        c = (v[j] - dot(m, 1, k, dk)) * beta;",
+     "c = (v[j] - dot(m, 1, k, dk)) * beta;\n        for (i = 0; i < dk; ++i)\n            m[i] = m[i] * e;"),
+    ("out_uses_k", "out[j] = dot(m, 1, q, dk) / rs;", "out[j] = dot(m, 1, k, dk) / rs;"),
+    ("out_unscaled", "out[j] = dot(m, 1, q, dk) / rs;", "out[j] = dot(m, 1, q, dk);"),
+    ("out_scale_dv", "const float rs = sqrtf((float)dk);", "const float rs = sqrtf((float)(dk + 1));"),
     ("head_map_interleaved", "static int32_t key_head_of(int32_t h, int32_t Hk) { return h % Hk; }",
      "static int32_t key_head_of(int32_t h, int32_t Hk) { return (h / 2) % Hk; }"),
     ("seq_wrong_token_stride", "q + (bt * Hk + kh) * dk,", "q + ((size_t)b * Hk + kh) * dk,"),
+    ("f64_decay_dropped", "m[i] = m[i] * e;\n        c = ((double)v[j]", "m[i] = m[i];\n        c = ((double)v[j]"),
+    ("f64_beta_dropped", "c = ((double)v[j] - dot64(m, k, dk)) * (double)beta;",
+     "c = ((double)v[j] - dot64(m, k, dk));"),
+    ("f64_out_unscaled", "out[j] = dot64(m, q, dk) / rs;", "out[j] = dot64(m, q, dk);"),
+    ("seq_f64_token_stride", "v + (bt * Hv + h) * dv,\n                               beta",
+     "v + ((size_t)b * Hv + h) * dv,\n                               beta"),
     ("pair_tentative_from_old_state", "if (p == 1)", "if (p == 0)"),
     ("pair_positions_swapped", "const size_t bp = (size_t)b * 2 + p;", "const size_t bp = (size_t)b * 2 + (1 - p);"),
+    ("tail_pair_tentative_from_old", "for (p = 0; p < 2; ++p) {\n            const size_t bp = 2 * (size_t)b + p;",
+     "for (p = 1; p >= 0; --p) {\n            const size_t bp = 2 * (size_t)b + p;"),
+    ("tail_pair_positions_swapped", "const size_t bp = 2 * (size_t)b + p;", "const size_t bp = 2 * (size_t)b + (1 - p);"),
+    ("tail_pair_state_not_carried", "memcpy(Mb, M + (size_t)b * st, st * sizeof(float));",
+     "memset(Mb, 0, st * sizeof(float));"),
     ("conv_taps_reversed", "acc = acc + conv_w[(size_t)c * K + t] * win[t];",
      "acc = acc + conv_w[(size_t)c * K + (K - 1 - t)] * win[t];"),
     ("conv_cache_not_shifted", "cs[(size_t)t * C + c] = win[t + 1];", "cs[(size_t)t * C + c] = win[t];"),
