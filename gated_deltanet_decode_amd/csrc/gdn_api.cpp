@@ -359,7 +359,14 @@ int layer_tail(const char *name, const gdn_dims *dims, const gdn_tail_params *pa
     if (dbg_core && !aligned(dbg_core, 16))
         return fail(GDN_ERR_ALIGN, "dbg_core is not 16-byte aligned");
 
-    const size_t need = (dbg_qkv ? 0 : nx) + (dbg_core ? 0 : nz) + (raw ? 2 * nh : 0);
+    // The single launch keeps Q|K|V, the step output and beta/gate on chip;
+    // only the three-launch path stages them in the workspace (or in the
+    // debug buffers when they are given).
+    const bool fused = !params->force_unfused &&
+                       gdn::tail_fused_supported(dims->n_v_heads, dims->n_k_heads, K,
+                                                 params->norm_group);
+    const size_t need =
+        fused ? 0 : (dbg_qkv ? 0 : nx) + (dbg_core ? 0 : nz) + (raw ? 2 * nh : 0);
     if (need > 0) {
         if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
         if (!aligned(workspace, 16)) return fail(GDN_ERR_ALIGN, "workspace is not 16-byte aligned");
@@ -367,12 +374,12 @@ int layer_tail(const char *name, const gdn_dims *dims, const gdn_tail_params *pa
             return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
                         need);
     }
-    float *ws = static_cast<float *>(workspace);
+    float *ws = need > 0 ? static_cast<float *>(workspace) : nullptr;
     float *qkv = dbg_qkv ? dbg_qkv : ws;
-    float *core = dbg_core ? dbg_core : ws + (dbg_qkv ? 0 : nx / f);
-    float *wbeta = raw ? ws + ((dbg_qkv ? 0 : nx) + (dbg_core ? 0 : nz)) / f : nullptr;
-    float *wgate = raw ? wbeta + nh / f : nullptr;
-    if (raw) {
+    float *core = dbg_core ? dbg_core : (ws ? ws + (dbg_qkv ? 0 : nx / f) : nullptr);
+    float *wbeta = (raw && ws) ? ws + ((dbg_qkv ? 0 : nx) + (dbg_core ? 0 : nz)) / f : nullptr;
+    float *wgate = wbeta ? wbeta + nh / f : nullptr;
+    if (raw && !fused) {
         beta = wbeta;
         gate = wgate;
     }
@@ -399,8 +406,7 @@ int layer_tail(const char *name, const gdn_dims *dims, const gdn_tail_params *pa
     (void)hipGetLastError();
     char what[96];
 
-    if (!params->force_unfused &&
-        gdn::tail_fused_supported(dims->n_v_heads, dims->n_k_heads, K, params->norm_group)) {
+    if (fused) {
         gdn::TailFusedArgs fa{};
         fa.x = x;
         fa.conv_w = conv_w;

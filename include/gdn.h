@@ -185,8 +185,9 @@ int gdn_pair(const gdn_dims *dims, int32_t B,
  *   dbg_qkv    [B][C] optional (NULL = skip): normalised Q | K | V fed to the step
  *   dbg_core   [B][n_v_heads][d_v] optional: step output before the gated norm
  *   workspace  device scratch of gdn_layer_tail_workspace_bytes() bytes
- *              (16-byte aligned; may be NULL when both dbg buffers are given;
- *              the single-launch path leaves it untouched)
+ *              (16-byte aligned), used only by the three-launch path: it
+ *              may be NULL (workspace_bytes 0) when the single launch
+ *              applies (see gdn_tail_params) or both dbg buffers are given
  * Size limits (GDN_ERR_SHAPE beyond): B * C <= 1073741823 and
  * B * n_v_heads * d_v / norm_group <= 33554431 (gated-norm groups).
  */
@@ -197,8 +198,8 @@ int gdn_layer_tail(const gdn_dims *dims, const gdn_tail_params *params, int32_t 
                    float *dbg_qkv, float *dbg_core,
                    void *workspace, size_t workspace_bytes, void *stream);
 
-/* Bytes of workspace gdn_layer_tail needs when no dbg buffer is given
- * (0 on invalid arguments). */
+/* Bytes of workspace the three-launch path of gdn_layer_tail needs when no
+ * dbg buffer is given: enough for every path (0 on invalid arguments). */
 size_t gdn_layer_tail_workspace_bytes(const gdn_dims *dims, int32_t B);
 
 /*
@@ -235,10 +236,11 @@ int gdn_gate_transform(const gdn_dims *dims, int32_t B, const gdn_gate_inputs *i
  * gdn_layer_tail_ba - gdn_layer_tail with beta and gate computed from the
  * raw gate inputs as in gdn_gate_transform (the whole recurrent branch of
  * one token from the projection outputs x, ba and z to y).  Arguments as in
- * gdn_layer_tail; the workspace must hold gdn_layer_tail_ba_workspace_bytes()
- * bytes, of which the unfused path uses the last 2*B*n_v_heads floats for
- * beta and gate.  Results are bitwise equal to gdn_gate_transform followed
- * by gdn_layer_tail.
+ * gdn_layer_tail; the three-launch path needs a workspace of
+ * gdn_layer_tail_ba_workspace_bytes() bytes, of which it uses the last
+ * 2*B*n_v_heads floats for beta and gate (the single launch needs none, so
+ * the workspace may then be NULL).  Results are bitwise equal to
+ * gdn_gate_transform followed by gdn_layer_tail.
  */
 int gdn_layer_tail_ba(const gdn_dims *dims, const gdn_tail_params *params, int32_t B,
                       const float *x, const float *conv_w, float *conv_state,
@@ -247,8 +249,8 @@ int gdn_layer_tail_ba(const gdn_dims *dims, const gdn_tail_params *params, int32
                       float *dbg_qkv, float *dbg_core,
                       void *workspace, size_t workspace_bytes, void *stream);
 
-/* Bytes of workspace gdn_layer_tail_ba needs when no dbg buffer is given
- * (0 on invalid arguments). */
+/* Bytes of workspace the three-launch path of gdn_layer_tail_ba needs when
+ * no dbg buffer is given: enough for every path (0 on invalid arguments). */
 size_t gdn_layer_tail_ba_workspace_bytes(const gdn_dims *dims, int32_t B);
 
 /* Message for the last non-zero return on this thread ("" if none). */

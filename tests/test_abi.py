@@ -139,6 +139,7 @@ def test_tail_validation(g):
     d = g.Dims(HV, HK, D, D)
     C = 2 * HK * D + HV * D
     p = g.TailParams(4, 128, 1e-6)
+    pu = g.TailParams(4, 128, 1e-6, 1)      # three launches: the workspace is used
     base = {"x": BASE, "conv_w": BASE + (1 << 24), "cs": BASE + (2 << 24), "beta": BASE + (3 << 24),
             "gate": BASE + (4 << 24), "state": BASE + (5 << 24), "z": BASE + (8 << 24),
             "nw": BASE + (9 << 24), "y": BASE + (10 << 24), "ws": BASE + (11 << 24)}
@@ -164,17 +165,23 @@ def test_tail_validation(g):
     # one-element groups at B = 8193: 8193 * 4096 gated-norm workgroups of 128
     # threads would overflow the 32-bit dispatch grid
     expect(g, f(pp=g.TailParams(4, 1, 1e-6), Bv=8193), -2, "groups too many")
-    expect(g, f(ws_bytes=need - 4), -5, "workspace")
-    expect(g, f(ws=None), -5, "workspace")
+    expect(g, f(pp=pu, ws_bytes=need - 4), -5, "workspace")
+    expect(g, f(pp=pu, ws=None), -5, "workspace")
     expect(g, f(cs=base["cs"] + 4), -3, "conv_state")
-    expect(g, f(ws=base["ws"] + 4), -3, "workspace")
+    expect(g, f(pp=pu, ws=base["ws"] + 4), -3, "workspace")
     expect(g, f(y=base["z"]), -4, "y")
     expect(g, f(y=base["x"] + 64), -4, "y")
-    expect(g, f(ws=base["state"]), -4, "buffer")
+    expect(g, f(pp=pu, ws=base["state"]), -4, "buffer")
+    # the single launch never touches the workspace, so an unused one that
+    # overlaps a buffer is not checked (the GPU tests run it with NULL)
     # both debug buffers given -> no workspace needed, but they must not collide
     dq, dc = BASE + (12 << 24), BASE + (13 << 24)
     expect(g, f(ws=None, ws_bytes=0, dq=dq, dc=dq + 64), -4, "buffer")
+    expect(g, f(pp=pu, ws=None, ws_bytes=0, dq=dq, dc=dq + 64), -4, "buffer")
     expect(g, f(dq=dq + 4), -3, "dbg_qkv")
+    # a three-launch tail at a shape the single launch does not take (conv
+    # kernel 3) needs the workspace too
+    expect(g, f(pp=g.TailParams(3, 128, 1e-6), ws=None), -5, "workspace")
 
 
 def test_gate_transform_validation(g):
@@ -214,11 +221,13 @@ def test_tail_ba_validation(g):
     assert need == B * (C + HV * D) * 4 + 2 * B * HV * 4
     assert need == g.layer_tail_workspace_bytes(B) + 2 * B * HV * 4
 
-    def f(ws_bytes=need, null_gates=False, dq=None, dc=None, **over):
+    pu = g.TailParams(4, 128, 1e-6, 1)      # three launches: the workspace is used
+
+    def f(ws_bytes=need, null_gates=False, dq=None, dc=None, pp=pu, **over):
         a = dict(base, **over)
         gi = g.GateInputs(a["ba"], a["a_log"], a["dt"])
         return g.lib.gdn_layer_tail_ba(
-            ctypes.byref(d), ctypes.byref(p), B, a["x"], a["conv_w"], a["cs"],
+            ctypes.byref(d), ctypes.byref(pp), B, a["x"], a["conv_w"], a["cs"],
             None if null_gates else ctypes.byref(gi), a["state"], a["z"], a["nw"], a["y"],
             dq, dc, a["ws"], ws_bytes, None)
 

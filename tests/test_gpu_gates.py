@@ -98,7 +98,9 @@ def run_tail_ba(g, ti, gin, M, force_unfused=0, use_dbg=False, Hv=HV, Hk=16):
     y = torch.empty((B, Hv * 128), device="cuda")
     dq = torch.empty((B, C), device="cuda") if use_dbg else None
     dc = torch.empty((B, Hv, 128), device="cuda") if use_dbg else None
-    ws = torch.empty(g.layer_tail_ba_workspace_bytes(B, dims), dtype=torch.uint8, device="cuda")
+    # the single launch needs no workspace: it runs with none
+    ws = torch.empty(g.layer_tail_ba_workspace_bytes(B, dims), dtype=torch.uint8, device="cuda") \
+        if force_unfused else None
     params = g.TailParams(4, 128, 1e-6, force_unfused)
     g.layer_tail_ba(t["x"], t["conv_w"], t["conv_state"], gd["ba"], gd["a_log"], gd["dt_bias"],
                     Md, t["z"], t["norm_w"], y, dbg_qkv=dq, dbg_core=dc, workspace=ws,

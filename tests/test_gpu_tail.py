@@ -72,14 +72,19 @@ def test_tail_b32_layer_tail(g, orc):
     check(got, want)
 
 
-@pytest.mark.parametrize("use_dbg", [False, True])
-def test_tail_workspace_and_debug_buffers(g, orc, use_dbg):
+@pytest.mark.parametrize("use_dbg,use_ws,unfused", [(False, True, 0), (True, False, 0),
+                                                    (False, False, 0), (False, True, 1),
+                                                    (True, False, 1)])
+def test_tail_workspace_and_debug_buffers(g, orc, use_dbg, use_ws, unfused):
     """The result does not depend on whether intermediates go to the
-    workspace or to the debug buffers."""
-    print(f"\n  gdn_layer_tail B=3 dbg={use_dbg}", flush=True)
+    workspace or to the debug buffers; the single launch runs without any
+    workspace."""
+    print(f"\n  gdn_layer_tail B=3 dbg={use_dbg} workspace={use_ws} three launches={unfused}",
+          flush=True)
     ti = gi.tail_inputs(4100, 3)
     M = gi.state(4100, 0, 3)
-    got = run_tail(g, ti, M, use_dbg=use_dbg, use_ws=not use_dbg)
+    got = run_tail(g, ti, M, use_dbg=use_dbg, use_ws=use_ws,
+                   params=g.TailParams(4, 128, 1e-6, unfused))
     want = oracle_tail(orc, ti, M)
     check(got, want)
 
