@@ -11,6 +11,8 @@ C entry points:
     layer_tail(x, conv_w, conv_state, beta, gate, state, z, norm_w, y, ...)
                                                  -> gdn_layer_tail
     layer_tail_workspace_bytes(B)                -> gdn_layer_tail_workspace_bytes
+    layer_tail_noalloc(x, conv_w, conv_state, beta, gate, state, z, norm_w, y, ...)
+                                                 -> gdn_layer_tail_noalloc
     gate_transform(ba, a_log, dt_bias, beta, gate) -> gdn_gate_transform
     layer_tail_ba(x, conv_w, conv_state, ba, a_log, dt_bias, state, z, norm_w, y, ...)
                                                  -> gdn_layer_tail_ba
@@ -28,7 +30,8 @@ import os
 from ._build import LIBRARY
 
 __all__ = ["GdnError", "Dims", "TailParams", "GateInputs", "lib", "step", "seq", "pair",
-           "layer_tail", "layer_tail_workspace_bytes", "gate_transform", "layer_tail_ba",
+           "layer_tail", "layer_tail_workspace_bytes", "layer_tail_noalloc", "gate_transform",
+           "layer_tail_ba",
            "layer_tail_ba_workspace_bytes", "last_error", "version", "PAGE_DIMS",
            "PAGE_TAIL", "ERRORS"]
 
@@ -82,6 +85,8 @@ lib.gdn_pair.restype = ctypes.c_int
 lib.gdn_pair.argtypes = [_DP, _i32] + [_vp] * 8 + [_vp]
 lib.gdn_layer_tail.restype = ctypes.c_int
 lib.gdn_layer_tail.argtypes = [_DP, _TP, _i32] + [_vp] * 11 + [_vp, ctypes.c_size_t, _vp]
+lib.gdn_layer_tail_noalloc.restype = ctypes.c_int
+lib.gdn_layer_tail_noalloc.argtypes = [_DP, _TP, _i32] + [_vp] * 11 + [_vp]
 lib.gdn_layer_tail_workspace_bytes.restype = ctypes.c_size_t
 lib.gdn_layer_tail_workspace_bytes.argtypes = [_DP, _i32]
 lib.gdn_gate_transform.restype = ctypes.c_int
@@ -224,6 +229,28 @@ def layer_tail(x, conv_w, conv_state, beta, gate, state, z, norm_w, y,
         _ptr(dbg_qkv, "dbg_qkv", (B, C), optional=True),
         _ptr(dbg_core, "dbg_core", (B, dims.n_v_heads, dims.d_v), optional=True),
         ws_ptr, ws_bytes, _stream(stream)))
+
+
+def layer_tail_noalloc(x, conv_w, conv_state, beta, gate, state, z, norm_w, y,
+                       dbg_qkv=None, dbg_core=None,
+                       dims: Dims = PAGE_DIMS, params: TailParams = PAGE_TAIL,
+                       stream=None) -> None:
+    """gdn_layer_tail_noalloc: layer_tail with the library's static per-GPU
+    scratch in place of a workspace (allocates nothing)."""
+    B, C = x.shape
+    K = params.conv_kernel
+    nv = dims.n_v_heads * dims.d_v
+    _check(lib.gdn_layer_tail_noalloc(
+        ctypes.byref(dims), ctypes.byref(params), B,
+        _ptr(x, "x", (B, C)), _ptr(conv_w, "conv_w", (C, K)),
+        _ptr(conv_state, "conv_state", (B, K - 1, C)),
+        _ptr(beta, "beta", (B, dims.n_v_heads)), _ptr(gate, "gate", (B, dims.n_v_heads)),
+        _ptr(state, "state", (B, dims.n_v_heads, dims.d_v, dims.d_k)),
+        _ptr(z, "z", (B, nv)), _ptr(norm_w, "norm_w", (params.norm_group,)),
+        _ptr(y, "y", (B, nv)),
+        _ptr(dbg_qkv, "dbg_qkv", (B, C), optional=True),
+        _ptr(dbg_core, "dbg_core", (B, dims.n_v_heads, dims.d_v), optional=True),
+        _stream(stream)))
 
 
 def _gate_inputs(ba, a_log, dt_bias, B, Hv):

@@ -309,12 +309,13 @@ int check_gate_inputs(const gdn_dims *dims, int32_t B, const gdn_gate_inputs *in
 
 // The layer tail with beta/gate given (raw == NULL) or computed from the raw
 // gate inputs.  With raw inputs the unfused path writes beta and gate to the
-// end of the workspace first.
+// end of the workspace first.  noalloc: the workspace is the library's static
+// per-GPU scratch instead of a caller's buffer.
 int layer_tail(const char *name, const gdn_dims *dims, const gdn_tail_params *params, int32_t B,
                const float *x, const float *conv_w, float *conv_state, const float *beta,
                const float *gate, const gdn_gate_inputs *raw, float *state, const float *z,
                const float *norm_w, float *y, float *dbg_qkv, float *dbg_core, void *workspace,
-               size_t workspace_bytes, void *stream) {
+               size_t workspace_bytes, void *stream, bool noalloc = false) {
     GDN_TRY(check_dims(dims));
     if (!params) return fail(GDN_ERR_NULL, "params is NULL");
     GDN_TRY(check_batch(dims, B, "B"));
@@ -367,6 +368,14 @@ int layer_tail(const char *name, const gdn_dims *dims, const gdn_tail_params *pa
                                                  params->norm_group);
     const size_t need =
         fused ? 0 : (dbg_qkv ? 0 : nx) + (dbg_core ? 0 : nz) + (raw ? 2 * nh : 0);
+    if (noalloc && need > 0) {
+        if (need > gdn::kNoAllocScratchBytes)
+            return fail(GDN_ERR_WORKSPACE,
+                        "%s needs %zu bytes of scratch; the static scratch holds %zu", name, need,
+                        gdn::kNoAllocScratchBytes);
+        GDN_TRY(hip_status(gdn::noalloc_scratch(&workspace), "static scratch lookup"));
+        workspace_bytes = gdn::kNoAllocScratchBytes;
+    }
     if (need > 0) {
         if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
         if (!aligned(workspace, 16)) return fail(GDN_ERR_ALIGN, "workspace is not 16-byte aligned");
@@ -511,6 +520,17 @@ int gdn_layer_tail_ba(const gdn_dims *dims, const gdn_tail_params *params, int32
     return layer_tail("gdn_layer_tail_ba", dims, params, B, x, conv_w, conv_state, nullptr,
                       nullptr, gates, state, z, norm_w, y, dbg_qkv, dbg_core, workspace,
                       workspace_bytes, stream);
+}
+
+int gdn_layer_tail_noalloc(const gdn_dims *dims, const gdn_tail_params *params, int32_t B,
+                           const float *x, const float *conv_w, float *conv_state,
+                           const float *beta, const float *gate, float *state, const float *z,
+                           const float *norm_w, float *y, float *dbg_qkv, float *dbg_core,
+                           void *stream) {
+    clear_error();
+    return layer_tail("gdn_layer_tail_noalloc", dims, params, B, x, conv_w, conv_state, beta,
+                      gate, nullptr, state, z, norm_w, y, dbg_qkv, dbg_core, nullptr, 0, stream,
+                      true);
 }
 
 size_t gdn_layer_tail_ba_workspace_bytes(const gdn_dims *dims, int32_t B) {

@@ -129,6 +129,13 @@ struct TailFusedArgs {
     float eps;
 };
 
+// Bytes of the per-GPU static scratch array of gdn_layer_tail_noalloc.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+
+// The device address of that array on the current device, looked up with
+// hipGetSymbolAddress on the first call per device and cached.
+hipError_t noalloc_scratch(void **ptr);
+
 // True when launch_tail_fused supports these sizes (value heads per key head
 // 1 or 2, conv kernel 4, gated-norm group equal to the head dimension).
 bool tail_fused_supported(int32_t Hv, int32_t Hk, int32_t K, int32_t group);

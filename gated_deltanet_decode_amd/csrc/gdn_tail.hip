@@ -1,22 +1,37 @@
 // gdn_tail.hip - gdn_layer_tail: conv1d prestate, gated RMSNorm, the
 // beta/alpha parameter transforms and the single-launch fused tail.
 
+#include <atomic>
+#include <mutex>
+
 #include "gdn_device.hpp"
 
 namespace gdn {
 namespace {
 
+// Scratch of gdn_layer_tail_noalloc, for callers that cannot allocate: the
+// three-launch tail stages its normalised Q|K|V and step output here instead
+// of in a caller's workspace.  Each GPU the library runs on holds its own
+// copy until the process ends, and every call on that GPU shares it.  Host
+// code never uses this name as an address: noalloc_scratch() returns the
+// device address that hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
 // --------------------------------------------------------- tail helpers
 // Block-wide sum for a block of NW waves; every thread gets the same bits.
 template <int NW>
-__device__ __forceinline__ float block_sum(float x, float *scratch) {
+__device__ __forceinline__ float block_sum(float x, float *red) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = x;
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
     __syncthreads();
     float s = 0.0f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) s += scratch[w];
+    for (int w = 0; w < NW; ++w) s += red[w];
     return s;
 }
 
@@ -42,7 +57,7 @@ __device__ __forceinline__ void beta_gate(float b, float a, float a_log, float d
 // dim is 128, so a chunk is exactly one head).
 template <int K>
 __global__ __launch_bounds__(D) void k_prestate(PrestateArgs a) {
-    __shared__ float scratch[D / 64];
+    __shared__ float red[D / 64];
     const int n_chunks = a.C / D;
     const int64_t b = blockIdx.x / n_chunks;
     const int chunk = static_cast<int>(blockIdx.x - b * n_chunks);
@@ -63,7 +78,7 @@ __global__ __launch_bounds__(D) void k_prestate(PrestateArgs a) {
 
     float s = silu(acc);
     if (chunk * D < a.n_qk) {        // block-uniform: a Q or K head
-        const float ss = block_sum<D / 64>(s * s, scratch);
+        const float ss = block_sum<D / 64>(s * s, red);
         const float nrm = fmaxf(sqrtf(ss), 1e-6f);
         s = s / nrm;
     }
@@ -73,7 +88,7 @@ __global__ __launch_bounds__(D) void k_prestate(PrestateArgs a) {
 // Gated RMSNorm x SiLU(z) over one group of one row.
 constexpr int kNormThreads = kGatedNormThreads;
 __global__ __launch_bounds__(kNormThreads) void k_gated_norm(GatedNormArgs a) {
-    __shared__ float scratch[kNormThreads / 64];
+    __shared__ float red[kNormThreads / 64];
     const int groups = a.n / a.group;
     const int64_t row = blockIdx.x / groups;
     const int64_t base = row * a.n + static_cast<int64_t>(blockIdx.x - row * groups) * a.group;
@@ -82,7 +97,7 @@ __global__ __launch_bounds__(kNormThreads) void k_gated_norm(GatedNormArgs a) {
         const float o = a.o[base + i];
         ss = fmaf(o, o, ss);
     }
-    ss = block_sum<kNormThreads / 64>(ss, scratch);
+    ss = block_sum<kNormThreads / 64>(ss, red);
     const float rms = sqrtf(ss / static_cast<float>(a.group) + a.eps);
     for (int i = threadIdx.x; i < a.group; i += kNormThreads)
         a.y[base + i] = (a.o[base + i] / rms) * a.w[i] * silu(a.z[base + i]);
@@ -120,7 +135,7 @@ __global__ __launch_bounds__(kTailThreads) void k_tail_fused(TailFusedArgs a) {
     constexpr int kTilesPerWave = kTiles / (kTailThreads / 64);
     __shared__ alignas(16) float act[kCh];          // Q | K | V_0 .. V_{RV-1}
     __shared__ float core[RV * D];
-    __shared__ float scratch[kTailThreads / 64];
+    __shared__ float red[kTailThreads / 64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -187,10 +202,10 @@ __global__ __launch_bounds__(kTailThreads) void k_tail_fused(TailFusedArgs a) {
             float x2 = s * s;
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) x2 += __shfl_xor(x2, off, 64);
-            if (lane == 0) scratch[wave] = x2;
+            if (lane == 0) red[wave] = x2;
             __syncthreads();
             const int h2 = wave >> 1;              // 0: Q, 1: K
-            const float ss = (0.0f + scratch[2 * h2]) + scratch[2 * h2 + 1];
+            const float ss = (0.0f + red[2 * h2]) + red[2 * h2 + 1];
             s = s / fmaxf(sqrtf(ss), 1e-6f);
         }
         act[slot] = s;
@@ -226,10 +241,10 @@ __global__ __launch_bounds__(kTailThreads) void k_tail_fused(TailFusedArgs a) {
         float x2 = fmaf(o, o, 0.0f);
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) x2 += __shfl_xor(x2, off, 64);
-        if (lane == 0) scratch[wave] = x2;
+        if (lane == 0) red[wave] = x2;
         __syncthreads();
         if (live) {
-            const float ss = (0.0f + scratch[2 * i]) + scratch[2 * i + 1];
+            const float ss = (0.0f + red[2 * i]) + red[2 * i + 1];
             const float rms = sqrtf(ss / static_cast<float>(D) + a.eps);
             const int h = kh + i * a.Hk;
             const int64_t yo = static_cast<int64_t>(b) * a.Hv * D + static_cast<int64_t>(h) * D + j;
@@ -240,6 +255,27 @@ __global__ __launch_bounds__(kTailThreads) void k_tail_fused(TailFusedArgs a) {
 }
 
 }  // namespace
+
+hipError_t noalloc_scratch(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            // with device `dev` current: its own copy of the array
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
+}
 
 bool tail_fused_supported(int32_t Hv, int32_t Hk, int32_t K, int32_t group) {
     const int32_t rv = Hv / Hk;

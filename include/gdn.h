@@ -253,6 +253,33 @@ int gdn_layer_tail_ba(const gdn_dims *dims, const gdn_tail_params *params, int32
  * no dbg buffer is given: enough for every path (0 on invalid arguments). */
 size_t gdn_layer_tail_ba_workspace_bytes(const gdn_dims *dims, int32_t B);
 
+/* Size of the static scratch of gdn_layer_tail_noalloc, per GPU. */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * gdn_layer_tail_noalloc - gdn_layer_tail without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Where the
+ * three-launch path needs staging (it runs when the single launch does not
+ * apply or force_unfused is set, and no dbg buffers are given), it uses a
+ * static scratch array of GDN_NOALLOC_SCRATCH_BYTES that each GPU holds from
+ * the first such call until the process ends; the single launch needs none.
+ * The call allocates nothing.  Arguments, results (bitwise) and errors are
+ * those of gdn_layer_tail, plus GDN_ERR_WORKSPACE, before anything is
+ * enqueued, when the staging would exceed the scratch
+ * (gdn_layer_tail_workspace_bytes(dims, B) > GDN_NOALLOC_SCRATCH_BYTES: B >
+ * 341 at the page geometry on the three-launch path), and GDN_ERR_HIP if the
+ * scratch's address cannot be obtained.  Every call on one GPU shares the
+ * scratch, which keeps the last call's contents: calls that overlap on one
+ * GPU (on different streams, or from threads without ordering between them)
+ * race when they take the three-launch path; calls on one stream do not.
+ */
+int gdn_layer_tail_noalloc(const gdn_dims *dims, const gdn_tail_params *params, int32_t B,
+                           const float *x, const float *conv_w, float *conv_state,
+                           const float *beta, const float *gate, float *state,
+                           const float *z, const float *norm_w, float *y,
+                           float *dbg_qkv, float *dbg_core, void *stream);
+
 /* Message for the last non-zero return on this thread ("" if none). */
 const char *gdn_last_error(void);
 

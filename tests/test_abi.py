@@ -184,6 +184,31 @@ def test_tail_validation(g):
     expect(g, f(pp=g.TailParams(3, 128, 1e-6), ws=None), -5, "workspace")
 
 
+def test_tail_noalloc_validation(g):
+    """gdn_layer_tail_noalloc: the checks of gdn_layer_tail, and a three-launch
+    call whose staging exceeds the static scratch is refused before anything
+    else happens (B = 342 at the page geometry needs 16.03 MiB)."""
+    d = g.Dims(HV, HK, D, D)
+    assert g.layer_tail_workspace_bytes(341) <= 16 << 20 < g.layer_tail_workspace_bytes(342)
+    step = 1 << 30                          # room for B = 342 in every buffer
+    base = {"x": BASE, "conv_w": BASE + step, "cs": BASE + 2 * step, "beta": BASE + 3 * step,
+            "gate": BASE + 4 * step, "state": BASE + 5 * step, "z": BASE + 6 * step,
+            "nw": BASE + 7 * step, "y": BASE + 8 * step}
+
+    def f(pp, Bv=B, dq=None, dc=None, **over):
+        a = dict(base, **over)
+        return g.lib.gdn_layer_tail_noalloc(
+            ctypes.byref(d), ctypes.byref(pp), Bv, a["x"], a["conv_w"], a["cs"], a["beta"],
+            a["gate"], a["state"], a["z"], a["nw"], a["y"], dq, dc, None)
+
+    pu = g.TailParams(4, 128, 1e-6, 1)
+    expect(g, f(pu, Bv=342), -5, "static scratch holds 16777216")
+    expect(g, f(g.TailParams(3, 128, 1e-6), Bv=342), -5, "static scratch")
+    expect(g, f(pu, x=None), -1, "x")
+    expect(g, f(g.TailParams(4, 128, 1e-6), y=base["z"]), -4, "y")
+    expect(g, f(pu, Bv=0), -2, "B")
+
+
 def test_gate_transform_validation(g):
     d = g.Dims(HV, HK, D, D)
     base = {"ba": BASE, "a_log": BASE + (1 << 20), "dt": BASE + (2 << 20),
