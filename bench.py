@@ -8,8 +8,9 @@ inputs per layer.  Inputs and states are resident in HBM before timing starts.
 
 Printed: ONE JSON line with the headline metric (state-updates/s, one update =
 one 128x128 head state advanced by one token), the roofline of the gdn_step
-kernel (algorithmic bytes per launch / mean launch time from HIP events on the
-launch stream), the plain C oracle timed on the host on a bounded sample, and
+kernel (algorithmic bytes per launch / mean launch time, i.e. the timed
+region's duration from HIP events on the launch stream divided by its 36 x K
+launches), the plain C oracle timed on the host on a bounded sample, and
 secondary measurements of the other entry points.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -42,6 +43,16 @@ TRAFFIC_FILE = os.path.join(HERE, "profiles", "k_step_b256_traffic.json")
 KERNEL_SOURCES = [os.path.join(HERE, "gated_deltanet_decode_amd", "csrc", f)
                   for f in ("gdn_device.hpp", "gdn_step.hip")]
 METRIC = "GDN state-updates/s (seq·head·token) and achieved HBM GB/s, B=256 decode"
+# Algorithmic bytes of gdn_layer_tail at B = 32: per sequence the 2 MiB
+# state read and written, x (32 KiB), the 3-slot conv ring read and written
+# (2 x 96 KiB), z and y (2 x 16 KiB), beta and gate; shared by all: the conv
+# weight (128 KiB) and the norm weight.
+TAIL_B32_BYTES = 32 * (2 * HV * D * D * 4 + 8192 * 4 + 2 * 3 * 8192 * 4 + 2 * HV * D * 4
+                       + 2 * HV * 4) + 8192 * 4 * 4 + D * 4
+# gdn_layer_tail_pair at B = 32: the state read once and written twice, the
+# ring read once and written twice, x, z, y, beta and gate for two positions.
+TAIL_PAIR_B32_BYTES = 32 * (3 * HV * D * D * 4 + 2 * 8192 * 4 + 3 * 3 * 8192 * 4
+                            + 2 * 2 * HV * D * 4 + 2 * 2 * HV * 4) + 8192 * 4 * 4 + D * 4
 
 
 def log(*a):
@@ -151,18 +162,21 @@ def fma_probe(torch, stream, workgroups, threads, iters=20000, reps=3):
     return 2.0 * n * iters * 16 / (ms / 1e3) / 1e12
 
 
-def copy_probe(torch, stream, nbytes=1 << 30, reps=5):
-    """Bandwidth of a plain device-to-device copy (read + write bytes / s)."""
+def copy_probe(torch, stream, nbytes=1 << 30, reps=5, tuned=True):
+    """Bandwidth of a device-to-device copy (read + write bytes / s): tuned
+    (the step kernel's nontemporal persistent walk, src != dst) or a plain
+    grid-stride copy."""
     import ctypes
     from gated_deltanet_decode_amd._build import PROBE_LIBRARY
     lib = ctypes.CDLL(PROBE_LIBRARY)
-    lib.gdn_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    fn = lib.gdn_probe_copy_nt if tuned else lib.gdn_probe_copy
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     src.fill_(1)
 
     def once():
-        assert lib.gdn_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, stream.cuda_stream) == 0
+        assert fn(src.data_ptr(), dst.data_ptr(), nbytes, stream.cuda_stream) == 0
     once()
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -415,6 +429,10 @@ def extra_measurements(torch, g, stream, only=None):
         ms = timeit(lambda: g.step(si["q"], si["k"], si["v"], si["beta"], si["gate"], M, o,
                                    stream=stream), 1000)
         res["step_b1"] = {"us_per_call": ms * 1e3, "state_updates_per_s": 32 / (ms / 1e3)}
+        # the prepared call (tensors checked once, converted arguments reused)
+        call = g.bind_step(si["q"], si["k"], si["v"], si["beta"], si["gate"], M, o, stream=stream)
+        ms = timeit(call, 1000)
+        res["step_b1"]["prepared_us_per_call"] = ms * 1e3
         # the same call replayed from a captured graph of 100 calls (no host
         # launch path in the loop: device-side time per call)
         side = torch.cuda.Stream()
@@ -440,9 +458,20 @@ def extra_measurements(torch, g, stream, only=None):
                 g.step(t["q"], t["k"], t["v"], t["beta"], t["gate"], M, o, stream=stream)
         ms = timeit(c1run, 3)
         upd = 100 * 64 * HV
+
+        def c1cached():
+            for t in ins:
+                g.step(t["q"], t["k"], t["v"], t["beta"], t["gate"], M, o, stream=stream,
+                       cached=True)
+        ms_c = min(timeit(c1cached, 3) for _ in range(3))
+        ms = min(ms, min(timeit(c1run, 3) for _ in range(2)))
         res["step_b64_x100"] = {"ms": ms, "state_updates_per_s": upd / (ms / 1e3),
-                                        "GBps": upd * STATE_UPDATE_BYTES / (ms / 1e3) / 1e9,
-                                        "note": "128 MiB state fits the 256 MB Infinity Cache"}
+                                "GBps": upd * STATE_UPDATE_BYTES / (ms / 1e3) / 1e9,
+                                "cached_ms": ms_c,
+                                "cached_state_updates_per_s": upd / (ms_c / 1e3),
+                                "cached_GBps": upd * STATE_UPDATE_BYTES / (ms_c / 1e3) / 1e9,
+                                "note": "the 128 MiB state fits the 256 MB Infinity Cache; "
+                                        "cached_*: gdn_step_ex with GDN_STATE_CACHED"}
 
     # gdn_pair: B=256, one layer, two positions (state read once, written twice)
     if only is None:
@@ -479,28 +508,28 @@ def extra_measurements(torch, g, stream, only=None):
             ms = min(ms, timeit(lambda: run(False), 5))
             ms_exact = min(ms_exact, timeit(lambda: run(True), 5))
         upd = 8 * 4096 * HV
-        # 6 flop per state element: the rank-1 update and the two dot
-        # products (three FMA); the decay multiplies a per-group scale
-        # instead of every element (7 with the per-element multiply)
-        flops = upd * D * D * 6
-        tf = flops / (ms / 1e3) / 1e12
-        tf7 = upd * D * D * 7 / (ms / 1e3) / 1e12
+        # The method's work is 7 flop per state element and token: the
+        # decay multiply and three FMA (the rank-1 update and the two dot
+        # products).  gdn_seq executes 6 of them: it carries a qualifying
+        # 16-token group's decay as one scale instead of multiplying every
+        # element.
+        tf = upd * D * D * 7 / (ms / 1e3) / 1e12
+        tf6 = upd * D * D * 6 / (ms / 1e3) / 1e12
         # the VALU ceiling measured at the kernel's own occupancy (one 8-wave
         # workgroup per CU, as this launch) and at 16 waves per CU
         cus = torch.cuda.get_device_properties(0).multi_processor_count
         probe8 = fma_probe(torch, stream, cus, 512)
         probe16 = fma_probe(torch, stream, 4 * cus, 256)
         res["seq_b8_t4096"] = {"ms": ms, "state_updates_per_s": upd / (ms / 1e3),
-                                       "TFLOPs": tf,
-                                       "frac_fp32_vector_nonpacked_78.6": tf / 78.6,
-                                       "frac_fp32_vector_157.3": tf / 157.3,
-                                       "fma_probe_TFLOPs_8_waves_per_cu": probe8,
-                                       "fma_probe_TFLOPs_16_waves_per_cu": probe16,
-                                       "frac_of_fma_probe_same_occupancy": tf / probe8,
-                                       "exact_ms": ms_exact,
-                                       "TFLOPs_at_7_flop_per_element": tf7,
-                                       "exact_TFLOPs_at_7_flop_per_element":
-                                           upd * D * D * 7 / (ms_exact / 1e3) / 1e12}
+                               "TFLOPs": tf, "flop_per_element": 7,
+                               "frac_fp32_vector_nonpacked_78.6": tf / 78.6,
+                               "frac_fp32_vector_157.3": tf / 157.3,
+                               "executed_TFLOPs_6_flop_per_element": tf6,
+                               "fma_probe_TFLOPs_8_waves_per_cu": probe8,
+                               "fma_probe_TFLOPs_16_waves_per_cu": probe16,
+                               "executed_frac_of_fma_probe_same_occupancy": tf6 / probe8,
+                               "exact_ms": ms_exact,
+                               "exact_TFLOPs": upd * D * D * 7 / (ms_exact / 1e3) / 1e12}
 
     # tail_b32: layer tail B=32
     if want("tail_b32"):
@@ -532,8 +561,25 @@ def extra_measurements(torch, g, stream, only=None):
                          ti["norm_w"], y, workspace=ws, stream=stream)
         ms = timeit(rot, 120)
         res["tail_b32"]["rotating_6_states_us_per_call"] = ms * 1e3
-        res["tail_b32"]["rotating_GBps"] = 142.75e6 / (ms / 1e3) / 1e9
-        del sets, css
+        res["tail_b32"]["rotating_GBps"] = TAIL_B32_BYTES / (ms / 1e3) / 1e9
+        res["tail_b32"]["rotating_frac_of_8TBps"] = TAIL_B32_BYTES / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS
+        # gdn_layer_tail_pair over the same rotating states: both positions,
+        # ring and state read once and written twice
+        t2 = {n: torch.from_numpy(x).cuda() for n, x in gi.tail_inputs(c4["seed"], 32, slot=1).items()}
+        pr = {n: torch.stack([ti[n], t2[n]], dim=1).contiguous() for n in ("x", "beta", "gate", "z")}
+        nxt = [torch.empty_like(sets[0]), torch.empty_like(css[0])]
+        y2 = torch.empty((32, 2, HV * D), device="cuda")
+
+        def rot_pair():
+            i = k[0] % 6
+            k[0] += 1
+            g.layer_tail_pair(pr["x"], ti["conv_w"], css[i], nxt[1], pr["beta"], pr["gate"],
+                              sets[i], nxt[0], pr["z"], ti["norm_w"], y2, stream=stream)
+        ms = timeit(rot_pair, 120)
+        res["tail_b32"]["pair_rotating_us_per_call"] = ms * 1e3
+        res["tail_b32"]["pair_bytes_per_call"] = TAIL_PAIR_B32_BYTES
+        res["tail_b32"]["pair_rotating_GBps"] = TAIL_PAIR_B32_BYTES / (ms / 1e3) / 1e9
+        del sets, css, nxt
         # the same tail starting from the raw beta/alpha logits (gdn_layer_tail_ba)
         gin = {n: torch.from_numpy(x).cuda() for n, x in gi.gate_inputs(c4["seed"], 32).items()}
         wsb = torch.empty(g.layer_tail_ba_workspace_bytes(32), dtype=torch.uint8, device="cuda")
@@ -562,7 +608,8 @@ def main():
         print(json.dumps({"workload": args.workload, "extra": res}), flush=True)
         return
     copy_gbps = copy_probe(torch, stream)
-    log(f"[bench] copy probe: {copy_gbps:.0f} GB/s")
+    plain_copy_gbps = copy_probe(torch, stream, tuned=False)
+    log(f"[bench] copy probes: tuned {copy_gbps:.0f} GB/s, plain {plain_copy_gbps:.0f} GB/s")
     w = setup_step_b256_x36(torch, g)
     L, B = w["L"], w["B"]
     inplace_gbps = inplace_probe(torch, stream, w["states"][0])
@@ -573,33 +620,39 @@ def main():
     torch.cuda.synchronize()
 
     log(f"[bench] timing {args.steps} steps x {L} gdn_step launches")
-    # Every launch of every 5th timed step is bracketed by HIP events on the
-    # launch stream (event records between kernels cost a few us each, so the
-    # other steps run bare).
-    timed = [s for s in range(args.steps) if s % 5 == 0]
-    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-            for _ in range(L)] if s in timed else None for s in range(args.steps)]
+    # The timed region holds nothing but the K x 36 launches; its duration
+    # from HIP events on the launch stream, divided by the launches, is the
+    # mean launch duration (gaps between back-to-back launches included).
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for s in range(args.steps):
-        run_step36(g, w, stream, evs[s])
+        run_step36(g, w, stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_end)
-    launch_ms = [evs[s][l][0].elapsed_time(evs[s][l][1]) for s in timed for l in range(L)]
-    avg_launch_ms = float(np.mean(launch_ms))
 
     updates_per_step = L * B * HV
     ms_per_step = ms_total / args.steps
     value = updates_per_step / (ms_per_step / 1e3)
     bytes_per_launch = B * HV * STATE_UPDATE_BYTES
+    avg_launch_ms = ms_per_step / L
     achieved = bytes_per_launch / (avg_launch_ms / 1e3) / 1e9
+    # A separate pass, outside the timed region: each launch of 3 more steps
+    # bracketed by its own pair of events (the event records between kernels
+    # slow those steps slightly; context only).
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in range(L)] for _ in range(3)]
+    for s in range(3):
+        run_step36(g, w, stream, evs[s])
+    torch.cuda.synchronize()
+    launch_ms = [evs[s][l][0].elapsed_time(evs[s][l][1]) for s in range(3) for l in range(L)]
     log(f"[bench] {ms_per_step:.3f} ms/step (wall {wall / args.steps * 1e3:.3f}), "
-        f"launch mean {avg_launch_ms * 1e3:.1f} us min {min(launch_ms) * 1e3:.1f} "
-        f"max {max(launch_ms) * 1e3:.1f}; {achieved:.0f} GB/s")
+        f"{avg_launch_ms * 1e3:.1f} us per launch; {achieved:.0f} GB/s; event-bracketed "
+        f"launches: mean {np.mean(launch_ms) * 1e3:.1f} us min {min(launch_ms) * 1e3:.1f} "
+        f"max {max(launch_ms) * 1e3:.1f}")
 
     line = {
         "metric": METRIC,
@@ -624,12 +677,15 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(),
                      "bytes_per_launch": bytes_per_launch,
+                     "avg_launch_us": avg_launch_ms * 1e3,
+                     "launches_timed": L * args.steps,
                      "copy_probe_GBps": copy_gbps,
                      "frac_of_copy_probe": achieved / copy_gbps,
+                     "plain_copy_probe_GBps": plain_copy_gbps,
                      "inplace_probe_GBps": inplace_gbps,
                      "frac_of_inplace_probe": achieved / inplace_gbps,
-                     "avg_launch_us": avg_launch_ms * 1e3,
-                     "launches_timed": len(launch_ms)},
+                     "event_bracketed_launch_us": float(np.mean(launch_ms)) * 1e3,
+                     "event_bracketed_launches": len(launch_ms)},
     }
     if not args.no_extra:
         log("[bench] graph replay and flattened single launch of the 36 layers")

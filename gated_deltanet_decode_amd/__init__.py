@@ -5,6 +5,8 @@ kernels.  PyTorch provides device memory and streams.  The names mirror the
 C entry points:
 
     step(q, k, v, beta, gate, state, out)        -> gdn_step
+    step(..., cached=True)                       -> gdn_step_ex(GDN_STATE_CACHED)
+    bind_step(q, k, v, beta, gate, state, out)   -> a prepared gdn_step call
     seq(q, k, v, beta, gate, state, out)         -> gdn_seq
     seq(..., exact=True)                         -> gdn_seq_exact
     pair(q, k, v, beta, gate, state, state_next, out) -> gdn_pair
@@ -13,6 +15,8 @@ C entry points:
     layer_tail_workspace_bytes(B)                -> gdn_layer_tail_workspace_bytes
     layer_tail_noalloc(x, conv_w, conv_state, beta, gate, state, z, norm_w, y, ...)
                                                  -> gdn_layer_tail_noalloc
+    layer_tail_pair(x, conv_w, conv_state, conv_state_next, beta, gate, state,
+                    state_next, z, norm_w, y)    -> gdn_layer_tail_pair
     gate_transform(ba, a_log, dt_bias, beta, gate) -> gdn_gate_transform
     layer_tail_ba(x, conv_w, conv_state, ba, a_log, dt_bias, state, z, norm_w, y, ...)
                                                  -> gdn_layer_tail_ba
@@ -29,8 +33,10 @@ import os
 
 from ._build import LIBRARY
 
-__all__ = ["GdnError", "Dims", "TailParams", "GateInputs", "lib", "step", "seq", "pair",
-           "layer_tail", "layer_tail_workspace_bytes", "layer_tail_noalloc", "gate_transform",
+__all__ = ["GdnError", "Dims", "TailParams", "GateInputs", "lib", "step", "bind_step", "seq",
+           "pair",
+           "layer_tail", "layer_tail_workspace_bytes", "layer_tail_noalloc", "layer_tail_pair",
+           "gate_transform",
            "layer_tail_ba",
            "layer_tail_ba_workspace_bytes", "last_error", "version", "PAGE_DIMS",
            "PAGE_TAIL", "ERRORS"]
@@ -77,6 +83,9 @@ lib.gdn_last_error.restype = ctypes.c_char_p
 lib.gdn_last_error.argtypes = []
 lib.gdn_step.restype = ctypes.c_int
 lib.gdn_step.argtypes = [_DP, _i32] + [_vp] * 7 + [_vp]
+lib.gdn_step_ex.restype = ctypes.c_int
+lib.gdn_step_ex.argtypes = [_DP, _i32] + [_vp] * 7 + [ctypes.c_uint32, _vp]
+STATE_CACHED = 1
 lib.gdn_seq.restype = ctypes.c_int
 lib.gdn_seq.argtypes = [_DP, _i32, _i32] + [_vp] * 7 + [_vp]
 lib.gdn_seq_exact.restype = ctypes.c_int
@@ -85,6 +94,8 @@ lib.gdn_pair.restype = ctypes.c_int
 lib.gdn_pair.argtypes = [_DP, _i32] + [_vp] * 8 + [_vp]
 lib.gdn_layer_tail.restype = ctypes.c_int
 lib.gdn_layer_tail.argtypes = [_DP, _TP, _i32] + [_vp] * 11 + [_vp, ctypes.c_size_t, _vp]
+lib.gdn_layer_tail_pair.restype = ctypes.c_int
+lib.gdn_layer_tail_pair.argtypes = [_DP, _TP, _i32] + [_vp] * 11 + [_vp]
 lib.gdn_layer_tail_noalloc.restype = ctypes.c_int
 lib.gdn_layer_tail_noalloc.argtypes = [_DP, _TP, _i32] + [_vp] * 11 + [_vp]
 lib.gdn_layer_tail_workspace_bytes.restype = ctypes.c_size_t
@@ -149,18 +160,55 @@ def _dims_of(q, v):
     return Dims(Hv, Hk, dk, dv)
 
 
-def step(q, k, v, beta, gate, state, out, stream=None) -> None:
+def step(q, k, v, beta, gate, state, out, stream=None, cached=False) -> None:
     """gdn_step: q,k [B][Hk][dk], v [B][Hv][dv], beta/gate [B][Hv],
-    state [B][Hv][dv][dk] (updated in place), out [B][Hv][dv]."""
+    state [B][Hv][dv][dk] (updated in place), out [B][Hv][dv].  cached=True
+    calls gdn_step_ex with GDN_STATE_CACHED (states resident in the Infinity
+    Cache across calls)."""
     B = q.shape[0]
     d = _dims_of(q, v)
-    _check(lib.gdn_step(
-        ctypes.byref(d), B,
-        _ptr(q, "q", (B, d.n_k_heads, d.d_k)), _ptr(k, "k", (B, d.n_k_heads, d.d_k)),
-        _ptr(v, "v", (B, d.n_v_heads, d.d_v)),
-        _ptr(beta, "beta", (B, d.n_v_heads)), _ptr(gate, "gate", (B, d.n_v_heads)),
-        _ptr(state, "state", (B, d.n_v_heads, d.d_v, d.d_k)),
-        _ptr(out, "out", (B, d.n_v_heads, d.d_v)), _stream(stream)))
+    args = (ctypes.byref(d), B,
+            _ptr(q, "q", (B, d.n_k_heads, d.d_k)), _ptr(k, "k", (B, d.n_k_heads, d.d_k)),
+            _ptr(v, "v", (B, d.n_v_heads, d.d_v)),
+            _ptr(beta, "beta", (B, d.n_v_heads)), _ptr(gate, "gate", (B, d.n_v_heads)),
+            _ptr(state, "state", (B, d.n_v_heads, d.d_v, d.d_k)),
+            _ptr(out, "out", (B, d.n_v_heads, d.d_v)))
+    if cached:
+        _check(lib.gdn_step_ex(*args, STATE_CACHED, _stream(stream)))
+    else:
+        _check(lib.gdn_step(*args, _stream(stream)))
+
+
+def bind_step(q, k, v, beta, gate, state, out, stream=None, cached=False):
+    """A prepared gdn_step call for latency-bound decode loops that step the
+    same buffers again and again (new token values written into q, k, v,
+    beta and gate between calls): the tensors are checked once here and the
+    returned function only re-issues the C call with the converted
+    arguments.  The tensors must stay alive and in place while it is used.
+    The library still validates every call."""
+    B = q.shape[0]
+    d = _dims_of(q, v)
+    ptrs = (_ptr(q, "q", (B, d.n_k_heads, d.d_k)), _ptr(k, "k", (B, d.n_k_heads, d.d_k)),
+            _ptr(v, "v", (B, d.n_v_heads, d.d_v)),
+            _ptr(beta, "beta", (B, d.n_v_heads)), _ptr(gate, "gate", (B, d.n_v_heads)),
+            _ptr(state, "state", (B, d.n_v_heads, d.d_v, d.d_k)),
+            _ptr(out, "out", (B, d.n_v_heads, d.d_v)))
+    args = [ctypes.byref(d), ctypes.c_int32(B), *(ctypes.c_void_p(p) for p in ptrs)]
+    if cached:
+        fn = lib.gdn_step_ex
+        args.append(ctypes.c_uint32(STATE_CACHED))
+    else:
+        fn = lib.gdn_step
+    args.append(ctypes.c_void_p(_stream(stream)))
+    args = tuple(args)
+    keep = (d, q, k, v, beta, gate, state, out)
+
+    def call() -> None:
+        rc = fn(*args)
+        if rc != 0:
+            raise GdnError(rc, last_error())
+    call.tensors = keep
+    return call
 
 
 def seq(q, k, v, beta, gate, state, out, stream=None, exact=False) -> None:
@@ -251,6 +299,28 @@ def layer_tail_noalloc(x, conv_w, conv_state, beta, gate, state, z, norm_w, y,
         _ptr(dbg_qkv, "dbg_qkv", (B, C), optional=True),
         _ptr(dbg_core, "dbg_core", (B, dims.n_v_heads, dims.d_v), optional=True),
         _stream(stream)))
+
+
+def layer_tail_pair(x, conv_w, conv_state, conv_state_next, beta, gate, state, state_next,
+                    z, norm_w, y, dims: Dims = PAGE_DIMS, params: TailParams = PAGE_TAIL,
+                    stream=None) -> None:
+    """gdn_layer_tail_pair: x [B][2][C], beta/gate [B][2][Hv], z/y [B][2][Hv*dv].
+    conv_state and state are committed with position 1 in place;
+    conv_state_next and state_next receive the tentative ring and state after
+    position 2."""
+    B, _, C = x.shape
+    K = params.conv_kernel
+    nv = dims.n_v_heads * dims.d_v
+    st = (B, dims.n_v_heads, dims.d_v, dims.d_k)
+    _check(lib.gdn_layer_tail_pair(
+        ctypes.byref(dims), ctypes.byref(params), B,
+        _ptr(x, "x", (B, 2, C)), _ptr(conv_w, "conv_w", (C, K)),
+        _ptr(conv_state, "conv_state", (B, K - 1, C)),
+        _ptr(conv_state_next, "conv_state_next", (B, K - 1, C)),
+        _ptr(beta, "beta", (B, 2, dims.n_v_heads)), _ptr(gate, "gate", (B, 2, dims.n_v_heads)),
+        _ptr(state, "state", st), _ptr(state_next, "state_next", st),
+        _ptr(z, "z", (B, 2, nv)), _ptr(norm_w, "norm_w", (params.norm_group,)),
+        _ptr(y, "y", (B, 2, nv)), _stream(stream)))
 
 
 def _gate_inputs(ba, a_log, dt_bias, B, Hv):

@@ -198,7 +198,15 @@ const char *gdn_last_error(void) { return g_error; }
 
 int gdn_step(const gdn_dims *dims, int32_t B, const float *q, const float *k, const float *v,
              const float *beta, const float *gate, float *state, float *out, void *stream) {
+    return gdn_step_ex(dims, B, q, k, v, beta, gate, state, out, 0u, stream);
+}
+
+int gdn_step_ex(const gdn_dims *dims, int32_t B, const float *q, const float *k, const float *v,
+                const float *beta, const float *gate, float *state, float *out, uint32_t flags,
+                void *stream) {
     clear_error();
+    if (flags & ~static_cast<uint32_t>(GDN_STATE_CACHED))
+        return fail(GDN_ERR_SHAPE, "unknown flags 0x%x", flags & ~GDN_STATE_CACHED);
     GDN_TRY(check_dims(dims));
     GDN_TRY(check_batch(dims, B, "B"));
     const size_t f = sizeof(float);
@@ -229,7 +237,9 @@ int gdn_step(const gdn_dims *dims, int32_t B, const float *q, const float *k, co
     a.Hv = dims->n_v_heads;
     a.Hk = dims->n_k_heads;
     (void)hipGetLastError();  // do not report an earlier, unrelated error
-    return hip_status(gdn::launch_step(a, static_cast<hipStream_t>(stream)), "gdn_step launch");
+    return hip_status(gdn::launch_step(a, static_cast<hipStream_t>(stream),
+                                       (flags & GDN_STATE_CACHED) != 0),
+                      "gdn_step launch");
 }
 
 int gdn_seq(const gdn_dims *dims, int32_t B, int32_t T, const float *q, const float *k,
@@ -520,6 +530,75 @@ int gdn_layer_tail_ba(const gdn_dims *dims, const gdn_tail_params *params, int32
     return layer_tail("gdn_layer_tail_ba", dims, params, B, x, conv_w, conv_state, nullptr,
                       nullptr, gates, state, z, norm_w, y, dbg_qkv, dbg_core, workspace,
                       workspace_bytes, stream);
+}
+
+int gdn_layer_tail_pair(const gdn_dims *dims, const gdn_tail_params *params, int32_t B,
+                        const float *x, const float *conv_w, float *conv_state,
+                        float *conv_state_next, const float *beta, const float *gate,
+                        float *state, float *state_next, const float *z, const float *norm_w,
+                        float *y, void *stream) {
+    clear_error();
+    GDN_TRY(check_dims(dims));
+    if (!params) return fail(GDN_ERR_NULL, "params is NULL");
+    GDN_TRY(check_batch(dims, B, "B"));
+    const int K = params->conv_kernel;
+    if (!gdn::tail_fused_supported(dims->n_v_heads, dims->n_k_heads, K, params->norm_group))
+        return fail(GDN_ERR_SHAPE,
+                    "gdn_layer_tail_pair supports conv_kernel 4, norm_group = d_v and n_v_heads "
+                    "= n_k_heads or 2 * n_k_heads (got %d, %d, %d, %d)",
+                    K, params->norm_group, dims->n_v_heads, dims->n_k_heads);
+    if (!(params->norm_eps >= 0.0f) || params->norm_eps > 3.0e38f)
+        return fail(GDN_ERR_SHAPE, "norm_eps must be finite and >= 0");
+    const int64_t nvw = static_cast<int64_t>(dims->n_v_heads) * dims->d_v;
+    const int64_t C = 2 * static_cast<int64_t>(dims->n_k_heads) * dims->d_k + nvw;
+    if (2 * C * B > INT32_MAX / 2)
+        return fail(GDN_ERR_SHAPE, "B * 2 * channels = %lld too large", (long long)(2 * C * B));
+
+    const size_t f = sizeof(float);
+    const size_t nx = static_cast<size_t>(B) * 2 * C * f;
+    const size_t nw = static_cast<size_t>(C) * K * f;
+    const size_t ncs = static_cast<size_t>(B) * (K - 1) * C * f;
+    const size_t nh = static_cast<size_t>(B) * 2 * dims->n_v_heads * f;
+    const size_t ns = static_cast<size_t>(B) * dims->n_v_heads * dims->d_v * dims->d_k * f;
+    const size_t nz = static_cast<size_t>(B) * 2 * nvw * f;
+    const size_t nnw = static_cast<size_t>(params->norm_group) * f;
+    const Buf vec[] = {{"x", x, nx},
+                       {"conv_state", conv_state, ncs},
+                       {"conv_state_next", conv_state_next, ncs},
+                       {"state", state, ns},
+                       {"state_next", state_next, ns},
+                       {"z", z, nz},
+                       {"y", y, nz}};
+    const Buf sc[] = {{"conv_w", conv_w, nw}, {"norm_w", norm_w, nnw}, {"beta", beta, nh},
+                      {"gate", gate, nh}};
+    GDN_TRY(check_ptrs(vec, 7, 16));
+    GDN_TRY(check_ptrs(sc, 4, 4));
+    const Buf all[] = {vec[0], vec[1], vec[2], vec[3], vec[4], vec[5], vec[6],
+                       sc[0],  sc[1],  sc[2],  sc[3]};
+    const Buf outs[] = {vec[1], vec[2], vec[3], vec[4], vec[6]};
+    GDN_TRY(check_alias(outs, 5, all, 11));
+
+    gdn::TailFusedArgs fa{};
+    fa.x = x;
+    fa.conv_w = conv_w;
+    fa.conv_state = conv_state;
+    fa.conv_state_next = conv_state_next;
+    fa.beta = beta;
+    fa.gate = gate;
+    fa.state = state;
+    fa.state_next = state_next;
+    fa.z = z;
+    fa.norm_w = norm_w;
+    fa.y = y;
+    fa.B = B;
+    fa.Hv = dims->n_v_heads;
+    fa.Hk = dims->n_k_heads;
+    fa.C = static_cast<int32_t>(C);
+    fa.K = K;
+    fa.eps = params->norm_eps;
+    (void)hipGetLastError();
+    return hip_status(gdn::launch_tail_pair(fa, static_cast<hipStream_t>(stream)),
+                      "gdn_layer_tail_pair launch");
 }
 
 int gdn_layer_tail_noalloc(const gdn_dims *dims, const gdn_tail_params *params, int32_t B,

@@ -105,17 +105,22 @@ struct GateArgs {
 
 // The whole tail in one launch (one workgroup per sequence and key head).
 // beta/gate are used as given, or, when ba is set, computed in the kernel
-// from ba, a_log and dt_bias as in GateArgs.
+// from ba, a_log and dt_bias as in GateArgs.  The pair (launch_tail_pair)
+// takes two positions per sequence: x [B][2][C], beta/gate [B][2][Hv],
+// z/y [B][2][Hv*D]; position 1 commits conv_state and state, position 2
+// writes conv_state_next and state_next.
 struct TailFusedArgs {
     const float *x;
     const float *conv_w;
     float *conv_state;
+    float *conv_state_next;   // pair only
     const float *beta;
     const float *gate;
     const float *ba;       // optional raw gate inputs (then beta/gate are unused)
     const float *a_log;
     const float *dt_bias;
     float *state;
+    float *state_next;        // pair only
     const float *z;
     const float *norm_w;
     float *y;
@@ -144,8 +149,11 @@ bool tail_fused_supported(int32_t Hv, int32_t Hk, int32_t K, int32_t group);
 // (256 on MI355X; 256 too if the query fails).
 int device_cus();
 
-hipError_t launch_step(const StepArgs &a, hipStream_t s);
+// cached: state loads and stores with the default cache policy instead of
+// nontemporal ones (same arithmetic, same bits).
+hipError_t launch_step(const StepArgs &a, hipStream_t s, bool cached = false);
 hipError_t launch_tail_fused(const TailFusedArgs &a, hipStream_t s);
+hipError_t launch_tail_pair(const TailFusedArgs &a, hipStream_t s);
 // exact: every token multiplies the decay into the state (no scaled groups).
 hipError_t launch_seq(const SeqArgs &a, hipStream_t s, bool exact);
 hipError_t launch_pair(const PairArgs &a, hipStream_t s);

@@ -94,7 +94,10 @@ struct TileWalk {
 // B) fetches q early, since there the extra L2 round trip is pure latency.
 // W: waves per workgroup (kStepWaves for the persistent walk; 1 for small
 // launches, where one wave per tile spreads the few tiles over every CU).
-template <bool kLateQ, int W>
+// NT: state rows streamed with nontemporal loads and stores (the default);
+// false keeps them in the caches, for callers whose states fit in the
+// Infinity Cache across calls.
+template <bool kLateQ, int W, bool NT>
 __global__ __launch_bounds__(W * 64) void k_step(StepArgs a, int n_tiles, int epoch_wgs,
                                                  int epoch_iters) {
     const int lane = threadIdx.x & 63;
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(W * 64) void k_step(StepArgs a, int n_tiles, int ep
         const float bt = a.beta[w.head];
         const float vj = a.v[w.b * a.v_bstride + w.h * D + w.row];
         RowSlice r;
-        load_row<true>(r, Mrow, c);
+        load_row<NT>(r, Mrow, c);
         VecSlice kv, qv;
         load_vec(kv, kp, c);
         if constexpr (!kLateQ) load_vec(qv, qp, c);
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(W * 64) void k_step(StepArgs a, int n_tiles, int ep
             __builtin_amdgcn_sched_barrier(0);
         }
         update_part(r, (vj - sk) * bt, kv);                   // correction, rank-1
-        store_row<true>(Mrow, r, c);
+        store_row<NT>(Mrow, r, c);
         const float o = group_sum(dot_part(r, qv)) * kInvSqrtD;   // read-out
         if (c == 0) a.out[static_cast<int64_t>(w.head) * D + w.row] = o;
     } while (w.next());
@@ -219,11 +222,12 @@ constexpr int kEpochIters = 4;
 constexpr size_t kEpochLdsBytes = 96 * 1024;
 constexpr int64_t kMaxEpochWgs = int64_t(1) << 22;
 
-hipError_t launch_step(const StepArgs &a, hipStream_t s) {
+template <bool NT>
+hipError_t launch_step_policy(const StepArgs &a, hipStream_t s) {
     const int64_t tiles = static_cast<int64_t>(a.B) * a.Hv * kTilesPerHead;
     const int nt = static_cast<int>(tiles);
     if (tiles <= kOneShotTiles) {
-        k_step<false, 1><<<dim3(static_cast<unsigned>(tiles)), dim3(64), 0, s>>>(a, nt, nt, 1);
+        k_step<false, 1, NT><<<dim3(static_cast<unsigned>(tiles)), dim3(64), 0, s>>>(a, nt, nt, 1);
         return hipGetLastError();
     }
     int64_t full = device_cus() * static_cast<int64_t>(GDN_STEP_WGS_PER_CU);
@@ -235,16 +239,21 @@ hipError_t launch_step(const StepArgs &a, hipStream_t s) {
     const int64_t span = static_cast<int64_t>(grid) * kStepWaves * kEpochIters;
     const int64_t epochs = (tiles + span - 1) / span;
     if (passes > kPersistentIters && grid * epochs <= kMaxEpochWgs) {
-        k_step<true, kStepWaves><<<dim3(static_cast<unsigned>(grid * epochs)),
-                                   dim3(kStepWaves * 64), kEpochLdsBytes, s>>>(a, nt, grid,
-                                                                               kEpochIters);
+        k_step<true, kStepWaves, NT><<<dim3(static_cast<unsigned>(grid * epochs)),
+                                       dim3(kStepWaves * 64), kEpochLdsBytes, s>>>(
+            a, nt, grid, kEpochIters);
     } else if (passes > 1) {
-        k_step<true, kStepWaves><<<dim3(grid), dim3(kStepWaves * 64), 0, s>>>(
+        k_step<true, kStepWaves, NT><<<dim3(grid), dim3(kStepWaves * 64), 0, s>>>(
             a, nt, grid, static_cast<int>(passes));
     } else {
-        k_step<false, kStepWaves><<<dim3(grid), dim3(kStepWaves * 64), 0, s>>>(a, nt, grid, 1);
+        k_step<false, kStepWaves, NT><<<dim3(grid), dim3(kStepWaves * 64), 0, s>>>(a, nt, grid,
+                                                                                    1);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_step(const StepArgs &a, hipStream_t s, bool cached) {
+    return cached ? launch_step_policy<false>(a, s) : launch_step_policy<true>(a, s);
 }
 
 // The pair kernel runs its persistent walk in epochs of kEpochIters passes

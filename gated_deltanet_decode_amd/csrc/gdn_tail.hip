@@ -116,26 +116,57 @@ __global__ __launch_bounds__(kGateThreads) void k_gate_transform(GateArgs a) {
 
 
 // ------------------------------------------------------ fused layer tail
-// The whole recurrent-branch tail for one token in one launch.  One
-// workgroup per (sequence b, key head kh) owns every channel that key head's
-// value heads need: Q head kh, K head kh and the V channels of the RV value
-// heads h = kh + i*Hk.  Owning them outright makes the conv-cache shift
-// race-free, and lets the step read Q, K and V from LDS.  The workgroup issues
-// the nontemporal loads of its RV x 64 KiB of state first and computes the
-// prestate while they are in flight.  Every reduction keeps the order of the
-// three-launch path (k_prestate, k_step, k_gated_norm), so both paths give
-// the same bits.  With kRaw the lanes also make their heads' beta and gate
-// from the raw gate inputs with beta_gate(), as k_gate_transform does.
+// The whole recurrent-branch tail for NP consecutive positions in one launch
+// (NP = 1: one token; NP = 2: the speculative pair, docs.rs "Module
+// linear_core", gdn_pair: position 1 commits ring and state, position 2
+// moves them together into the tentative buffers).  One workgroup per
+// (sequence b, key head kh) owns every channel that key head's value heads
+// need: Q head kh, K head kh and the V channels of the RV value heads
+// h = kh + i*Hk.  Owning them outright makes the conv-ring update race-free
+// and lets the step read Q, K and V from LDS.
+//
+// Order of work, chosen by measurement on MI355X (B = 32, states streamed
+// from HBM): each wave issues the nontemporal loads of its state tiles, then
+// every conv input of the workgroup's channels at once (the K-1 ring slots,
+// the NP new inputs and the K taps of both channel passes), so conv, SiLU
+// and L2 run as soon as the wave's loads are back and no further memory
+// round trip sits between the state loads and the step.  Fetching the V
+// channels' inputs after the Q/K barrier measured 6 % slower, fetching the
+// conv inputs ahead of the state 5 % slower, and 8 waves of 4 tiles 4 %
+// slower.
+//
+// Every reduction keeps the order of the three-launch path (k_prestate,
+// k_step, k_gated_norm), so both paths give the same bits, and position 2
+// of a pair gives the bits of a one-position call on the ring and state
+// that position 1 committed.  With kRaw the lanes also make their heads'
+// beta and gate from the raw gate inputs with beta_gate(), as
+// k_gate_transform does.
 constexpr int kTailThreads = 256;
 
-template <int RV, int K, bool kRaw>
-__global__ __launch_bounds__(kTailThreads) void k_tail_fused(TailFusedArgs a) {
+// Channel of owned slot `slot` of key head kh: Q head kh, K head kh, then
+// the V channels of value heads kh, kh + Hk, ...  Slots beyond the owned
+// ones (a partial last pass) map to a Q channel, so their loads stay in
+// bounds; nothing computed from them is stored.
+template <int RV>
+__device__ __forceinline__ int owned_channel(int slot, int kh, int Hk) {
+    const int nq = Hk * D;
+    if (slot < D) return kh * D + slot;
+    if (slot < 2 * D) return nq + kh * D + (slot - D);
+    if (slot < (2 + RV) * D) return 2 * nq + (kh + ((slot - 2 * D) / D) * Hk) * D + (slot % D);
+    return kh * D + (slot % D);
+}
+
+template <int RV, int K, bool kRaw, int NP>
+__global__ __launch_bounds__(kTailThreads) void k_tail(TailFusedArgs a) {
+    constexpr int kW = kTailThreads / 64;
     constexpr int kCh = (2 + RV) * D;               // owned channels
+    constexpr int kPasses = (kCh + kTailThreads - 1) / kTailThreads;
     constexpr int kTiles = RV * kTilesPerHead;      // state tiles of the workgroup
-    constexpr int kTilesPerWave = kTiles / (kTailThreads / 64);
-    __shared__ alignas(16) float act[kCh];          // Q | K | V_0 .. V_{RV-1}
-    __shared__ float core[RV * D];
-    __shared__ float red[kTailThreads / 64];
+    constexpr int kTPW = kTiles / kW;
+    constexpr int kWin = K - 1 + NP;                // ring slots, then the NP inputs
+    __shared__ alignas(16) float act[NP][kCh];      // Q | K | V_0 .. V_{RV-1} per position
+    __shared__ float core[NP][RV * D];
+    __shared__ float red[NP][kW];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -144,23 +175,24 @@ __global__ __launch_bounds__(kTailThreads) void k_tail_fused(TailFusedArgs a) {
     const int c = lane & 7;
     const int b = blockIdx.x / a.Hk;
     const int kh = blockIdx.x - b * a.Hk;
-    const int nq = a.Hk * D;
 
-    // 1. state loads in flight, with the wave's beta and gate (or, with kRaw,
-    //    the raw logits and per-head parameters they are made from).  All
-    //    tiles of a wave lie in one value head.
-    static_assert(kTilesPerHead % kTilesPerWave == 0, "a wave's tiles must share a head");
-    const int hw = kh + (wave * kTilesPerWave / kTilesPerHead) * a.Hk;
-    RowSlice r[kTilesPerWave];
-    int64_t roff[kTilesPerWave];
+    // 1. state loads in flight, with each position's beta and gate (or, with
+    //    kRaw, the raw logits and per-head parameters they are made from).
+    //    All tiles of a wave lie in one value head.
+    static_assert(kTilesPerHead % kTPW == 0, "a wave's tiles must share a head");
+    static_assert(NP == 1 || !kRaw, "the pair takes beta and gate as given");
+    const int hw = kh + (wave * kTPW / kTilesPerHead) * a.Hk;
+    RowSlice r[kTPW];
+    int64_t roff[kTPW];
 #pragma unroll
-    for (int j = 0; j < kTilesPerWave; ++j) {
-        const int t = wave * kTilesPerWave + j;
+    for (int j = 0; j < kTPW; ++j) {
+        const int t = wave * kTPW + j;
         const int row = (t % kTilesPerHead) * kRowsPerTile + grp;
         roff[j] = (static_cast<int64_t>(b) * a.Hv + hw) * (D * D) + row * D;
         load_row<true>(r[j], a.state + roff[j], c);
     }
-    float bt = 0.0f, gt = 0.0f, raw_b = 0.0f, raw_a = 0.0f, raw_l = 0.0f, raw_d = 0.0f;
+    float bt[NP], gt[NP];
+    float raw_b = 0.0f, raw_a = 0.0f, raw_l = 0.0f, raw_d = 0.0f;
     if constexpr (kRaw) {
         const float *ba = a.ba + static_cast<int64_t>(b) * 2 * a.Hv;
         raw_b = ba[hw];
@@ -168,88 +200,153 @@ __global__ __launch_bounds__(kTailThreads) void k_tail_fused(TailFusedArgs a) {
         raw_l = a.a_log[hw];
         raw_d = a.dt_bias[hw];
     } else {
-        bt = a.beta[static_cast<int64_t>(b) * a.Hv + hw];
-        gt = a.gate[static_cast<int64_t>(b) * a.Hv + hw];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int64_t bp = static_cast<int64_t>(b) * NP + p;
+            bt[p] = a.beta[bp * a.Hv + hw];
+            gt[p] = a.gate[bp * a.Hv + hw];
+        }
     }
 
-    // 2. conv-state shift + conv1d + SiLU on the owned channels; the first
-    //    pass holds Q (threads 0..127) and K (threads 128..255), which are
-    //    L2-normalised per head with the reduction order of k_prestate.
+    // 2. every conv input of the owned channels
     float *cs = a.conv_state + static_cast<int64_t>(b) * (K - 1) * a.C;
+    float win[kPasses][kWin], wt[kPasses][K];
+    int chs[kPasses];
 #pragma unroll
-    for (int pass = 0; pass < (kCh + kTailThreads - 1) / kTailThreads; ++pass) {
-        const int slot = tid + pass * kTailThreads;
-        if (pass > 0 && slot >= kCh) continue;     // only in a partial last pass
-        int ch;
-        if (slot < D)
-            ch = kh * D + slot;
-        else if (slot < 2 * D)
-            ch = nq + kh * D + (slot - D);
-        else
-            ch = 2 * nq + (kh + ((slot - 2 * D) / D) * a.Hk) * D + (slot % D);
-        float win[K];
+    for (int pass = 0; pass < kPasses; ++pass) {
+        const int ch = owned_channel<RV>(tid + pass * kTailThreads, kh, a.Hk);
+        chs[pass] = ch;
 #pragma unroll
-        for (int t = 0; t < K - 1; ++t) win[t] = cs[static_cast<int64_t>(t) * a.C + ch];
-        win[K - 1] = a.x[static_cast<int64_t>(b) * a.C + ch];
+        for (int t = 0; t < K - 1; ++t) win[pass][t] = cs[static_cast<int64_t>(t) * a.C + ch];
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+            win[pass][K - 1 + p] = a.x[(static_cast<int64_t>(b) * NP + p) * a.C + ch];
         const float *w = a.conv_w + static_cast<int64_t>(ch) * K;
-        float acc = 0.0f;
 #pragma unroll
-        for (int t = 0; t < K; ++t) acc = fmaf(w[t], win[t], acc);
+        for (int t = 0; t < K; ++t) wt[pass][t] = w[t];
+    }
+
+    // 3. conv1d over each position's window (oldest first) + SiLU; the ring
+    //    after position 1 goes to conv_state and, for a pair, the ring after
+    //    position 2 to conv_state_next.  The first pass holds Q (threads
+    //    0..127) and K (threads 128..255), which are L2-normalised per head
+    //    with the reduction order of k_prestate.
+    float *csn = NP == 2 ? a.conv_state_next + static_cast<int64_t>(b) * (K - 1) * a.C : nullptr;
 #pragma unroll
-        for (int t = 0; t < K - 1; ++t) cs[static_cast<int64_t>(t) * a.C + ch] = win[t + 1];
-        float s = silu(acc);
+    for (int pass = 0; pass < kPasses; ++pass) {
+        const int slot = tid + pass * kTailThreads;
+        const bool live = slot < kCh;
+        const int ch = chs[pass];
+        float sv[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int t = 0; t < K; ++t) acc = fmaf(wt[pass][t], win[pass][p + t], acc);
+            sv[p] = silu(acc);
+        }
+        if (live) {
+#pragma unroll
+            for (int t = 0; t < K - 1; ++t)
+                cs[static_cast<int64_t>(t) * a.C + ch] = win[pass][t + 1];
+            if constexpr (NP == 2) {
+#pragma unroll
+                for (int t = 0; t < K - 1; ++t)
+                    csn[static_cast<int64_t>(t) * a.C + ch] = win[pass][t + 2];
+            }
+        }
         if (pass == 0) {
-            float x2 = s * s;
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) x2 += __shfl_xor(x2, off, 64);
-            if (lane == 0) red[wave] = x2;
+            for (int p = 0; p < NP; ++p) {
+                float x2 = sv[p] * sv[p];
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) x2 += __shfl_xor(x2, off, 64);
+                if (lane == 0) red[p][wave] = x2;
+            }
             __syncthreads();
             const int h2 = wave >> 1;              // 0: Q, 1: K
-            const float ss = (0.0f + red[2 * h2]) + red[2 * h2 + 1];
-            s = s / fmaxf(sqrtf(ss), 1e-6f);
-        }
-        act[slot] = s;
-        if (a.dbg_qkv) a.dbg_qkv[static_cast<int64_t>(b) * a.C + ch] = s;
-    }
-    if constexpr (kRaw) beta_gate(raw_b, raw_a, raw_l, raw_d, bt, gt);
-    const float e = expf(gt);
-    __syncthreads();
-
-    // 3. the state step on the preloaded rows; k and q come from LDS
-    VecSlice kv, qv;
-    load_vec(kv, act + D, c);
-    load_vec(qv, act, c);
 #pragma unroll
-    for (int j = 0; j < kTilesPerWave; ++j) {
-        const int t = wave * kTilesPerWave + j;
-        const int i = t / kTilesPerHead;
-        const int row = (t % kTilesPerHead) * kRowsPerTile + grp;
-        const float o = row_token(r[j], kv, qv, e, bt, act[(2 + i) * D + row]);
-        store_row<true>(a.state + roff[j], r[j], c);
-        if (c == 0) core[i * D + row] = o;
+            for (int p = 0; p < NP; ++p) {
+                const float ss = (0.0f + red[p][2 * h2]) + red[p][2 * h2 + 1];
+                sv[p] = sv[p] / fmaxf(sqrtf(ss), 1e-6f);
+            }
+        }
+        if (live) {
+#pragma unroll
+            for (int p = 0; p < NP; ++p) act[p][slot] = sv[p];
+            if (NP == 1 && a.dbg_qkv) a.dbg_qkv[static_cast<int64_t>(b) * a.C + ch] = sv[0];
+        }
+    }
+    if constexpr (kRaw) beta_gate(raw_b, raw_a, raw_l, raw_d, bt[0], gt[0]);
+    float e[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) e[p] = expf(gt[p]);
+    __syncthreads();
+
+    // 4. the state step on the preloaded rows, one position after the other;
+    //    k and q come from LDS.  Position 1's rows go back to `state`, a
+    //    pair's position 2 rows to `state_next`.
+    if constexpr (NP == 1) {
+        VecSlice kv, qv;
+        load_vec(kv, act[0] + D, c);
+        load_vec(qv, act[0], c);
+#pragma unroll
+        for (int j = 0; j < kTPW; ++j) {
+            const int t = wave * kTPW + j;
+            const int i = t / kTilesPerHead;
+            const int row = (t % kTilesPerHead) * kRowsPerTile + grp;
+            const float o = row_token(r[j], kv, qv, e[0], bt[0], act[0][(2 + i) * D + row]);
+            store_row<true>(a.state + roff[j], r[j], c);
+            if (c == 0) core[0][i * D + row] = o;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kTPW; ++j) {
+            const int t = wave * kTPW + j;
+            const int i = t / kTilesPerHead;
+            const int row = (t % kTilesPerHead) * kRowsPerTile + grp;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                VecSlice kv, qv;
+                load_vec(kv, act[p] + D, c);
+                load_vec(qv, act[p], c);
+                const float o = row_token(r[j], kv, qv, e[p], bt[p], act[p][(2 + i) * D + row]);
+                store_row<true>((p == 0 ? a.state : a.state_next) + roff[j], r[j], c);
+                if (c == 0) core[p][i * D + row] = o;
+            }
+        }
     }
     __syncthreads();
 
-    // 4. gated RMSNorm x SiLU(z), one 128-element group per value head, with
-    //    the reduction order of k_gated_norm (128 threads per group); with
-    //    RV = 1 the upper 128 threads carry zeros through the barriers.
+    // 5. gated RMSNorm x SiLU(z), one 128-element group per value head and
+    //    position, with the reduction order of k_gated_norm (128 threads per
+    //    group); with RV = 1 the upper 128 threads carry zeros through the
+    //    barrier.
     {
         const int i = tid / D;                     // value head slot
         const int j = tid - i * D;
         const bool live = tid < RV * D;
-        const float o = live ? core[tid] : 0.0f;
-        float x2 = fmaf(o, o, 0.0f);
+        float o[NP];
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) x2 += __shfl_xor(x2, off, 64);
-        if (lane == 0) red[wave] = x2;
+        for (int p = 0; p < NP; ++p) {
+            o[p] = live ? core[p][tid] : 0.0f;
+            float x2 = fmaf(o[p], o[p], 0.0f);
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) x2 += __shfl_xor(x2, off, 64);
+            if (lane == 0) red[p][wave] = x2;
+        }
         __syncthreads();
         if (live) {
-            const float ss = (0.0f + red[2 * i]) + red[2 * i + 1];
-            const float rms = sqrtf(ss / static_cast<float>(D) + a.eps);
             const int h = kh + i * a.Hk;
-            const int64_t yo = static_cast<int64_t>(b) * a.Hv * D + static_cast<int64_t>(h) * D + j;
-            a.y[yo] = (o / rms) * a.norm_w[j] * silu(a.z[yo]);
-            if (a.dbg_core) a.dbg_core[yo] = o;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const float ss = (0.0f + red[p][2 * i]) + red[p][2 * i + 1];
+                const float rms = sqrtf(ss / static_cast<float>(D) + a.eps);
+                const int64_t yo = (static_cast<int64_t>(b) * NP + p) * a.Hv * D +
+                                   static_cast<int64_t>(h) * D + j;
+                a.y[yo] = (o[p] / rms) * a.norm_w[j] * silu(a.z[yo]);
+                if (NP == 1 && a.dbg_core) a.dbg_core[yo] = o[p];
+            }
         }
     }
 }
@@ -287,17 +384,29 @@ hipError_t launch_tail_fused(const TailFusedArgs &a, hipStream_t s) {
     const bool raw = a.ba != nullptr;
     if (a.Hv == a.Hk && a.K == 4) {
         if (raw)
-            k_tail_fused<1, 4, true><<<grid, dim3(kTailThreads), 0, s>>>(a);
+            k_tail<1, 4, true, 1><<<grid, dim3(kTailThreads), 0, s>>>(a);
         else
-            k_tail_fused<1, 4, false><<<grid, dim3(kTailThreads), 0, s>>>(a);
+            k_tail<1, 4, false, 1><<<grid, dim3(kTailThreads), 0, s>>>(a);
     } else if (a.Hv == 2 * a.Hk && a.K == 4) {
         if (raw)
-            k_tail_fused<2, 4, true><<<grid, dim3(kTailThreads), 0, s>>>(a);
+            k_tail<2, 4, true, 1><<<grid, dim3(kTailThreads), 0, s>>>(a);
         else
-            k_tail_fused<2, 4, false><<<grid, dim3(kTailThreads), 0, s>>>(a);
+            k_tail<2, 4, false, 1><<<grid, dim3(kTailThreads), 0, s>>>(a);
     } else {
         return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_tail_pair(const TailFusedArgs &a, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hk));
+    if (a.ba != nullptr || !a.state_next || !a.conv_state_next) return hipErrorInvalidValue;
+    if (a.Hv == a.Hk && a.K == 4)
+        k_tail<1, 4, false, 2><<<grid, dim3(kTailThreads), 0, s>>>(a);
+    else if (a.Hv == 2 * a.Hk && a.K == 4)
+        k_tail<2, 4, false, 2><<<grid, dim3(kTailThreads), 0, s>>>(a);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

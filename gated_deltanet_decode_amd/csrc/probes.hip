@@ -6,6 +6,8 @@
 //  - an in-place read-modify-write with the state step's memory pattern and
 //    none of its arithmetic: the rate the step's access pattern alone
 //    reaches, the practical ceiling for the step kernel;
+//  - the same walk copying between two buffers: a copy tuned as the step
+//    kernel is (nontemporal 16-byte accesses, persistent XCD-aware walk);
 //  - a stream of independent non-packed FP32 FMAs with no memory traffic:
 //    the issue rate the VALU sustains at a given number of waves per CU, the
 //    practical ceiling for the multi-token kernel.
@@ -33,7 +35,9 @@ __global__ __launch_bounds__(256) void k_copy_probe(const f4 *__restrict__ src,
 typedef unsigned int u4 __attribute__((ext_vector_type(4)));
 constexpr int kProbeWaves = 8;
 
-__global__ __launch_bounds__(kProbeWaves * 64) void k_inplace_probe(f4 *buf, int64_t n_tiles,
+// src == dst: the in-place probe; otherwise a copy with the same walk.
+__global__ __launch_bounds__(kProbeWaves * 64) void k_inplace_probe(const f4 *src, f4 *dst,
+                                                                    int64_t n_tiles,
                                                                     unsigned key) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -44,14 +48,14 @@ __global__ __launch_bounds__(kProbeWaves * 64) void k_inplace_probe(f4 *buf, int
     const int lg = (G % 8 == 0) ? (g % 8) * (G / 8) + g / 8 : g;
     const int64_t stride = static_cast<int64_t>(G) * kProbeWaves;
     for (int64_t u = static_cast<int64_t>(lg) * kProbeWaves + wave; u < n_tiles; u += stride) {
-        f4 *row = buf + u * 256 + grp * 32;        // a tile is 256 float4, a row 32
+        const int64_t row = u * 256 + grp * 32;    // a tile is 256 float4, a row 32
         f4 v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = __builtin_nontemporal_load(row + 8 * i + c);
+        for (int i = 0; i < 4; ++i) v[i] = __builtin_nontemporal_load(src + row + 8 * i + c);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const u4 b = __builtin_bit_cast(u4, v[i]) ^ key;
-            __builtin_nontemporal_store(__builtin_bit_cast(f4, b), row + 8 * i + c);
+            __builtin_nontemporal_store(__builtin_bit_cast(f4, b), dst + row + 8 * i + c);
         }
     }
 }
@@ -115,7 +119,24 @@ int gdn_probe_inplace(void *buf, size_t bytes, unsigned key, void *stream) {
     const int grid = static_cast<int>(need < cus ? need : cus);
     (void)hipGetLastError();
     k_inplace_probe<<<dim3(grid), dim3(kProbeWaves * 64), 0, static_cast<hipStream_t>(stream)>>>(
-        static_cast<f4 *>(buf), tiles, key);
+        static_cast<const f4 *>(buf), static_cast<f4 *>(buf), tiles, key);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// Copies `bytes` (a multiple of 4096; both pointers 16-byte aligned device
+// memory, not overlapping) from src to dst with the in-place probe's walk.
+// Returns 0, -1 on bad arguments, -6 when the launch fails.
+int gdn_probe_copy_nt(const void *src, void *dst, size_t bytes, void *stream) {
+    if (!src || !dst || bytes == 0 || bytes % 4096 != 0 ||
+        reinterpret_cast<size_t>(src) % 16 != 0 || reinterpret_cast<size_t>(dst) % 16 != 0)
+        return -1;
+    const int64_t tiles = static_cast<int64_t>(bytes / 4096);
+    const int64_t need = (tiles + kProbeWaves - 1) / kProbeWaves;
+    const int cus = device_cus();
+    const int grid = static_cast<int>(need < cus ? need : cus);
+    (void)hipGetLastError();
+    k_inplace_probe<<<dim3(grid), dim3(kProbeWaves * 64), 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<const f4 *>(src), static_cast<f4 *>(dst), tiles, 0u);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

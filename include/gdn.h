@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 10200 /* 1.2.0 */
+#define GDN_VERSION 10300 /* 1.3.0 */
 
 #define GDN_OK 0
 #define GDN_ERR_NULL (-1)      /* a required pointer is NULL                  */
@@ -98,6 +98,27 @@ int gdn_step(const gdn_dims *dims, int32_t B,
              const float *q, const float *k, const float *v,
              const float *beta, const float *gate,
              float *state, float *out, void *stream);
+
+/* gdn_step_ex flags */
+#define GDN_STATE_CACHED 1u /* state through the caches instead of streamed */
+
+/*
+ * gdn_step_ex - gdn_step with a cache-policy hint for the state.
+ *   flags  0: as gdn_step (the state is streamed with nontemporal loads and
+ *             stores, which keeps it from displacing other data: right when
+ *             the states a decode loop cycles through exceed the GPU's
+ *             256 MB Infinity Cache, e.g. many layers of a large batch);
+ *          GDN_STATE_CACHED: state loads and stores use the default cache
+ *             policy, for callers whose whole working set of states stays
+ *             resident in the Infinity Cache from call to call (e.g. one
+ *             128 MiB state stepped repeatedly).
+ * Results are bitwise equal for both policies.  Unknown flag bits:
+ * GDN_ERR_SHAPE.  Other arguments, layouts and errors as gdn_step.
+ */
+int gdn_step_ex(const gdn_dims *dims, int32_t B,
+                const float *q, const float *k, const float *v,
+                const float *beta, const float *gate,
+                float *state, float *out, uint32_t flags, void *stream);
 
 /*
  * gdn_seq - T tokens for B sequences, run in order with the state carried
@@ -197,6 +218,39 @@ int gdn_layer_tail(const gdn_dims *dims, const gdn_tail_params *params, int32_t 
                    const float *z, const float *norm_w, float *y,
                    float *dbg_qkv, float *dbg_core,
                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_layer_tail_pair - gdn_layer_tail for two consecutive positions fused
+ * for speculative verification (docs.rs "Module linear_core", gdn_pair: lane
+ * 1 commits into the state, lane 2 is tentative in scratch, the conv ring
+ * and the recurrent state moving together).  Position 1 advances
+ * `conv_state` and `state` in place (committed); position 2 starts from the
+ * committed ring and state and writes its ring to `conv_state_next` and its
+ * state to `state_next` (tentative: the caller adopts both on acceptance,
+ * e.g. by swapping the buffers, or drops them on rejection).
+ *   x            [B][2][C]              raw pre-conv channels, position 1 then 2
+ *   conv_w       [C][conv_kernel]
+ *   conv_state   [B][conv_kernel-1][C]  in: before position 1, out: after it
+ *   conv_state_next [B][conv_kernel-1][C]  out: after position 2
+ *   beta, gate   [B][2][n_v_heads]
+ *   state        [B][n_v_heads][d_v][d_k]  in: before position 1, out: after it
+ *   state_next   [B][n_v_heads][d_v][d_k]  out: after position 2
+ *   z            [B][2][n_v_heads*d_v]
+ *   norm_w       [norm_group]
+ *   y            [B][2][n_v_heads*d_v]  output of both positions
+ * One launch; supports the single-launch geometry only (conv_kernel 4,
+ * norm_group = d_v, n_v_heads = n_k_heads or 2*n_k_heads; GDN_ERR_SHAPE
+ * otherwise; force_unfused is ignored) and needs no workspace.  The state is
+ * read once and written twice, and so is the conv ring.  Results are bitwise
+ * equal to gdn_layer_tail on position 1 followed by gdn_layer_tail on
+ * position 2 (on copies of the committed ring and state).
+ * Size limit (GDN_ERR_SHAPE beyond): B * 2 * C <= 1073741823.
+ */
+int gdn_layer_tail_pair(const gdn_dims *dims, const gdn_tail_params *params, int32_t B,
+                        const float *x, const float *conv_w, float *conv_state,
+                        float *conv_state_next, const float *beta, const float *gate,
+                        float *state, float *state_next, const float *z,
+                        const float *norm_w, float *y, void *stream);
 
 /* Bytes of workspace the three-launch path of gdn_layer_tail needs when no
  * dbg buffer is given: enough for every path (0 on invalid arguments). */

@@ -34,6 +34,31 @@ def pytest_configure(config):
             oracle.build()
 
 
+def pytest_sessionfinish(session, exitstatus):
+    """After a GPU session, write the parity records (one JSON object per
+    compared quantity) to gpurun_out/parity_records.jsonl."""
+    import json
+    ref = sys.modules.get("ref")
+    if ref is None or not ref.RECORDS:
+        return
+    out = os.path.join(ROOT, "gpurun_out")
+    os.makedirs(out, exist_ok=True)
+    with open(os.path.join(out, "parity_records.jsonl"), "w") as f:
+        for r in ref.RECORDS:
+            f.write(json.dumps(r) + "\n")
+
+
+@pytest.fixture
+def workload():
+    """Names the workload a test checks, for its parity records."""
+    import ref
+
+    def name(n):
+        ref.WORKLOAD["name"] = n
+    yield name
+    ref.WORKLOAD["name"] = None
+
+
 @pytest.fixture(scope="session")
 def orc():
     import oracle

@@ -135,6 +135,23 @@ def test_pair_validation(g):
     expect(g, f(dict(a, out=a["k"])), -4, "out")
 
 
+def test_step_ex_flags(g):
+    """gdn_step_ex refuses unknown flag bits before anything else happens;
+    with a known flag it validates like gdn_step."""
+    a, sz = addrs()
+    d = g.Dims(HV, HK, D, D)
+
+    def f(flags, **over):
+        x = dict(a, **over)
+        return g.lib.gdn_step_ex(ctypes.byref(d), B, x["q"], x["k"], x["v"], x["beta"], x["gate"],
+                                 x["state"], x["out"], flags, None)
+
+    expect(g, f(2), -2, "unknown flags 0x2")
+    expect(g, f(0x80000001), -2, "unknown flags 0x80000000")
+    expect(g, f(1, q=None), -1, "q")
+    expect(g, f(1, out=a["state"]), -4, "out")
+
+
 def test_tail_validation(g):
     d = g.Dims(HV, HK, D, D)
     C = 2 * HK * D + HV * D
@@ -207,6 +224,35 @@ def test_tail_noalloc_validation(g):
     expect(g, f(pu, x=None), -1, "x")
     expect(g, f(g.TailParams(4, 128, 1e-6), y=base["z"]), -4, "y")
     expect(g, f(pu, Bv=0), -2, "B")
+
+
+def test_tail_pair_validation(g):
+    d = g.Dims(HV, HK, D, D)
+    p = g.TailParams(4, 128, 1e-6)
+    step = 1 << 26
+    names = ("x", "conv_w", "cs", "csn", "beta", "gate", "state", "sn", "z", "nw", "y")
+    base = {n: BASE + i * step for i, n in enumerate(names)}
+
+    def f(pp=p, dd=d, Bv=B, **over):
+        a = dict(base, **over)
+        return g.lib.gdn_layer_tail_pair(
+            ctypes.byref(dd), ctypes.byref(pp) if pp is not None else None, Bv,
+            *(a[n] for n in names), None)
+
+    expect(g, f(pp=None), -1, "params")
+    expect(g, f(csn=None), -1, "conv_state_next")
+    expect(g, f(sn=None), -1, "state_next")
+    expect(g, f(pp=g.TailParams(3, 128, 1e-6)), -2, "conv_kernel 4")
+    expect(g, f(pp=g.TailParams(4, 64, 1e-6)), -2, "norm_group")
+    expect(g, f(dd=g.Dims(64, 16, D, D)), -2, "n_v_heads")
+    expect(g, f(pp=g.TailParams(4, 128, float("inf"))), -2, "norm_eps")
+    expect(g, f(Bv=0), -2, "B")
+    expect(g, f(x=base["x"] + 4), -3, "x")
+    expect(g, f(beta=base["beta"] + 2), -3, "beta")
+    expect(g, f(csn=base["cs"]), -4, "conv_state")
+    expect(g, f(sn=base["state"] + 64), -4, "state")
+    expect(g, f(y=base["z"]), -4, "y")
+    expect(g, f(csn=base["x"]), -4, "conv_state_next")
 
 
 def test_gate_transform_validation(g):

@@ -58,12 +58,16 @@ def test_seq_matches_oracle(g, orc, B, T, Hv, Hk):
     si = gi.step_inputs(3000 + T, 0, B, Hv, Hk, T=T)
     M = gi.state(3000 + T, 0, B, Hv)
     Mg, og = run_seq(g, si, M)
+    M64 = M.astype(np.float64)
     want = ref.seq_mt(orc, si, M)
+    out64 = ref.seq_f64_mt(orc, si, M64)
     # The recurrence contracts (0 < exp(gate) < 1, 0 < beta < 1, unit k), so
     # rounding differences do not build up over short runs: the per-step
     # tolerances apply.
     ref.assert_close("state", Mg, M, 1e-6)
     ref.assert_close("out", og, want, 1e-5)
+    ref.assert_vs_f64("state", Mg, M, M64)
+    ref.assert_vs_f64("out", og, want, out64)
 
 
 def strong_decay(si):

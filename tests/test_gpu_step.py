@@ -62,8 +62,9 @@ def test_step_epoch_launch_matches_oracle(g, orc):
     ref.assert_close("out", og, want, OUT_TOL)
 
 
-def test_step_b1_single_sequence(g, orc):
+def test_step_b1_single_sequence(g, orc, workload):
     """One sequence, one token, the page geometry."""
+    workload("step_b1")
     c = gi.WORKLOADS["step_b1"]
     print("\n  gdn_step B=1 (step_b1)", flush=True)
     si = gi.step_inputs(c["seed"], 0, 1)
@@ -74,10 +75,9 @@ def test_step_b1_single_sequence(g, orc):
     out64 = orc.step_f64(si["q"], si["k"], si["v"], si["beta"], si["gate"], M64)
     ref.assert_close("state", Mg, M, STATE_TOL)
     ref.assert_close("out", og, want, OUT_TOL)
-    # diagnostic: GPU and f32-oracle errors against the binary64 shadow
-    print("    vs f64: gpu state %.3e out %.3e | oracle state %.3e out %.3e" % (
-        ref.max_err(Mg, M64)[0], ref.max_err(og, out64)[0],
-        ref.max_err(M, M64)[0], ref.max_err(want, out64)[0]), flush=True)
+    # the binary64 yardstick: GPU error within a small factor of the f32 oracle's
+    ref.assert_vs_f64("state", Mg, M, M64)
+    ref.assert_vs_f64("out", og, want, out64)
 
 
 def test_broadcast_and_delta_rule_on_gpu(g):
@@ -195,3 +195,32 @@ def test_nan_stays_in_its_row(g):
     mask = np.ones(Mg.shape[:3], bool)
     mask[1, 5, 7] = False
     assert np.array_equal(Mg[mask], clean_M[mask]) and np.array_equal(og[mask], clean_o[mask])
+
+
+# B = 1: one wave per tile; 64: the persistent walk (the Infinity-Cache
+# resident decode); 300 x 33 heads: 4-pass epochs
+@pytest.mark.parametrize("B,Hv,Hk", [(1, 32, 16), (64, 32, 16), (300, 33, 11)])
+def test_step_cached_policy_is_bitwise(g, orc, B, Hv, Hk):
+    """gdn_step_ex with GDN_STATE_CACHED (state through the caches) gives the
+    bits of gdn_step (nontemporal state), over two chained calls, and matches
+    the oracle."""
+    import torch
+    print(f"\n  gdn_step_ex cached B={B} Hv={Hv} Hk={Hk}", flush=True)
+    M = gi.state(2700 + B, 0, B, Hv)
+    Mn, Mc = dev(M), dev(M)
+    outs = []
+    for call in range(2):
+        si = gi.step_inputs(2700 + B, call + 1, B, Hv, Hk)
+        t = {n: dev(x) for n, x in si.items()}
+        on = torch.empty((B, Hv, 128), device="cuda")
+        oc = torch.empty_like(on)
+        g.step(t["q"], t["k"], t["v"], t["beta"], t["gate"], Mn, on)
+        g.step(t["q"], t["k"], t["v"], t["beta"], t["gate"], Mc, oc, cached=True)
+        want = ref.step_mt(orc, si, M)
+        outs.append((on, oc, want))
+    torch.cuda.synchronize()
+    assert np.array_equal(Mn.cpu().numpy(), Mc.cpu().numpy()), "state differs between policies"
+    for on, oc, want in outs:
+        assert np.array_equal(on.cpu().numpy(), oc.cpu().numpy()), "out differs between policies"
+        ref.assert_close("out", oc.cpu().numpy(), want, OUT_TOL)
+    ref.assert_close("state", Mc.cpu().numpy(), M, STATE_TOL)

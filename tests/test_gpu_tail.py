@@ -61,8 +61,9 @@ def check(got, want, state_tol=1e-6):
     assert np.array_equal(got["conv_state"], want["conv_state"]), "conv cache not bitwise"
 
 
-def test_tail_b32_layer_tail(g, orc):
+def test_tail_b32_layer_tail(g, orc, workload):
     """B=32, 8192 channels, kernel 4, group 128, eps 1e-6."""
+    workload("tail_b32")
     c = gi.WORKLOADS["tail_b32"]
     print("\n  gdn_layer_tail B=32 (tail_b32)", flush=True)
     ti = gi.tail_inputs(c["seed"], c["B"])

@@ -31,8 +31,9 @@ def dev(a):
 
 
 @pytest.mark.timeout(600)
-def test_step_b64_x100(g, orc):
+def test_step_b64_x100(g, orc, workload):
     import torch
+    workload("step_b64_x100")
     c = gi.WORKLOADS["step_b64_x100"]
     B, calls = c["B"], c["calls"]
     print(f"\n  step_b64_x100: gdn_step B={B} x {calls} calls", flush=True)
@@ -50,19 +51,27 @@ def test_step_b64_x100(g, orc):
     torch.cuda.synchronize()
     Mg, og = Md.cpu().numpy(), outs.cpu().numpy()
     worst = 0.0
+    M64 = M.astype(np.float64)
+    e_gpu = e_orc = 0.0
     for i in range(calls):
         want = ref.step_mt(orc, inputs[i], M)
+        out64 = ref.step_f64_mt(orc, inputs[i], M64)
         if i == 0:
             ref.assert_close("state@1", M1, M, 1e-6)
         worst = max(worst, ref.max_err(og[i], want)[0])
+        e_gpu = max(e_gpu, ref.max_abs_err64(og[i], out64))
+        e_orc = max(e_orc, ref.max_abs_err64(want, out64))
         assert worst <= 1e-5, f"call {i}: out error {worst:.3e}"
-    print(f"    all {calls} outputs: max abs {worst:.3e}", flush=True)
+    ref.assert_abs_bound(f"all {calls} outs", worst, 1e-5)
     ref.assert_close("state@100", Mg, M, 1e-6)
+    ref.assert_f64_ratio(f"all {calls} outs", e_gpu, e_orc)
+    ref.assert_vs_f64("state@100", Mg, M, M64)
 
 
 @pytest.mark.timeout(900)
-def test_step_b256_x36_layers(g, orc):
+def test_step_b256_x36_layers(g, orc, workload):
     import torch
+    workload("step_b256_x36")
     c = gi.WORKLOADS["step_b256_x36"]
     B, L, seed = c["B"], c["layers"], c["seed"]
     print(f"\n  step_b256_x36: gdn_step B={B} x {L} layers (18 GiB state)", flush=True)
@@ -87,15 +96,28 @@ def test_step_b256_x36_layers(g, orc):
     # host, advance it with the oracle, compare the whole 512 MiB layer
     worst_s = worst_o = 0.0
     og = outs.cpu().numpy()
+    f64 = {"gs": 0.0, "os": 0.0, "go": 0.0, "oo": 0.0}
     for l in range(L):
         gi.state_into(sn, seed, l)
         M = sn.copy()
+        if l in (0, L - 1):     # the binary64 yardstick on the first and last layer
+            M64 = sn.astype(np.float64)
+            out64 = ref.step_f64_mt(orc, ins[l], M64)
         want = ref.step_mt(orc, ins[l], M)
-        worst_s = max(worst_s, ref.max_abs_err(states[l].cpu().numpy(), M))
+        Ml = states[l].cpu().numpy()
+        worst_s = max(worst_s, ref.max_abs_err(Ml, M))
         worst_o = max(worst_o, ref.max_abs_err(og[l], want))
+        if l in (0, L - 1):
+            f64["gs"] = max(f64["gs"], ref.max_abs_err64(Ml, M64))
+            f64["os"] = max(f64["os"], ref.max_abs_err64(M, M64))
+            f64["go"] = max(f64["go"], ref.max_abs_err64(og[l], out64))
+            f64["oo"] = max(f64["oo"], ref.max_abs_err64(want, out64))
         if l % 6 == 5:
             print(f"    layers 0..{l} checked: state {worst_s:.3e} out {worst_o:.3e}", flush=True)
-    assert worst_s <= 1e-6 and worst_o <= 1e-5, (worst_s, worst_o)
+    ref.assert_abs_bound("state, 36 layers", worst_s, 1e-6)
+    ref.assert_abs_bound("out, 36 layers", worst_o, 1e-5)
+    ref.assert_f64_ratio("state, layers 0 and 35", f64["gs"], f64["os"])
+    ref.assert_f64_ratio("out, layers 0 and 35", f64["go"], f64["oo"])
 
     # The same memory as one flattened B=9216 call (one more token), checked
     # in full the same way.
@@ -118,23 +140,46 @@ def test_step_b256_x36_layers(g, orc):
         if l % 6 == 5:
             print(f"    flattened, layers 0..{l} checked: state {worst_s:.3e} out {worst_o:.3e}",
                   flush=True)
-    assert worst_s <= 1e-6 and worst_o <= 1e-5, (worst_s, worst_o)
+    ref.assert_abs_bound("flattened B=9216 state", worst_s, 1e-6)
+    ref.assert_abs_bound("flattened B=9216 out", worst_o, 1e-5)
 
 
-@pytest.mark.timeout(600)
-def test_seq_b8_t4096(g, orc):
+@pytest.mark.timeout(900)
+def test_seq_b8_t4096(g, orc, workload):
+    """gdn_seq (scaled decay) and gdn_seq_exact at full size against the
+    oracle (1e-4), both against the binary64 shadow (within the yardstick
+    factor of the f32 oracle's own error), and the gap between the two forms
+    (within twice that)."""
     import torch
+    workload("seq_b8_t4096")
     c = gi.WORKLOADS["seq_b8_t4096"]
     B, T = c["B"], c["T"]
-    print(f"\n  seq_b8_t4096: gdn_seq B={B} T={T} from zero state", flush=True)
+    print(f"\n  seq_b8_t4096: gdn_seq and gdn_seq_exact B={B} T={T} from zero state", flush=True)
     si = gi.step_inputs(c["seed"], 0, B, T=T)
     M = np.zeros((B, 32, 128, 128), np.float32)
     t = {n: dev(x) for n, x in si.items()}
-    Md = dev(M)
-    out = torch.empty((B, T, 32, 128), device="cuda")
-    g.seq(t["q"], t["k"], t["v"], t["beta"], t["gate"], Md, out)
-    torch.cuda.synchronize()
-    print("    GPU done; oracle running", flush=True)
+    res = {}
+    for exact in (False, True):
+        Md = dev(M)
+        out = torch.empty((B, T, 32, 128), device="cuda")
+        g.seq(t["q"], t["k"], t["v"], t["beta"], t["gate"], Md, out, exact=exact)
+        torch.cuda.synchronize()
+        res[exact] = (Md.cpu().numpy(), out.cpu().numpy())
+        del Md, out
+    print("    GPU done; oracle (f32 and f64) running", flush=True)
+    M64 = M.astype(np.float64)
     want = ref.seq_mt(orc, si, M)
-    ref.assert_close("state", Md.cpu().numpy(), M, 1e-4)
-    ref.assert_close("out", out.cpu().numpy(), want, 1e-4)
+    out64 = ref.seq_f64_mt(orc, si, M64)
+    for exact, tag in ((False, "seq"), (True, "seq_exact")):
+        Mg, og = res[exact]
+        ref.assert_close(f"{tag} state", Mg, M, 1e-4)
+        ref.assert_close(f"{tag} out", og, want, 1e-4)
+        ref.assert_vs_f64(f"{tag} state", Mg, M, M64)
+        ref.assert_vs_f64(f"{tag} out", og, want, out64)
+    for i, what, o32, o64 in ((0, "state", M, M64), (1, "out", want, out64)):
+        gap = ref.max_abs_err(res[False][i], res[True][i])
+        e_orc = ref.max_abs_err64(o32, o64)
+        bound = 2 * ref.F64_FACTOR * e_orc + 1e-12
+        ref.record(name=f"seq vs seq_exact {what}", max_abs=gap, bound=bound, passed=gap <= bound)
+        print(f"    seq vs seq_exact {what}: {gap:.3e} (bound {bound:.3e})", flush=True)
+        assert gap <= bound, f"gdn_seq and gdn_seq_exact differ by {gap:.3e} in {what}"
