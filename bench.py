@@ -69,7 +69,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--workload", default="step_b256_x36",
                    choices=["step_b1", "step_b64_x100", "step_b256_x36", "seq_b8_t4096",
-                            "tail_b32"],
+                            "seq_b256_t64", "tail_b32"],
                    help="step_b256_x36 (default): the headline run; the others run only that "
                         "workload's secondary measurement (for profiling)")
     return p.parse_args()
@@ -530,6 +530,34 @@ def extra_measurements(torch, g, stream, only=None):
                                "executed_frac_of_fma_probe_same_occupancy": tf6 / probe8,
                                "exact_ms": ms_exact,
                                "exact_TFLOPs": upd * D * D * 7 / (ms_exact / 1e3) / 1e12}
+
+    # seq_b256_t64: gdn_seq with many heads and a short sequence (B=256 x
+    # T=64 from a seeded state, 4 states in rotation): the half-head route
+    # with 16-token chunks, 3 workgroups per CU
+    if want("seq_b256_t64"):
+        c5 = gi.WORKLOADS["seq_b256_t64"]
+        B, T = c5["B"], c5["T"]
+        si = {n: torch.from_numpy(x).cuda() for n, x in gi.step_inputs(c5["seed"], 0, B, T=T).items()}
+        sts = [torch.from_numpy(gi.state(c5["seed"], s_, B)).cuda() for s_ in range(4)]
+        o = torch.empty((B, T, HV, D), device="cuda")
+        k = [0]
+
+        def rot(exact):
+            i = k[0] % 4
+            k[0] += 1
+            g.seq(si["q"], si["k"], si["v"], si["beta"], si["gate"], sts[i], o, stream=stream,
+                  exact=exact)
+        ms = min(timeit(lambda: rot(False), 8) for _ in range(3))
+        ms_x = min(timeit(lambda: rot(True), 8) for _ in range(3))
+        upd = B * T * HV
+        tf = upd * D * D * 7 / (ms / 1e3) / 1e12
+        res["seq_b256_t64"] = {"ms": ms, "state_updates_per_s": upd / (ms / 1e3),
+                               "TFLOPs": tf, "flop_per_element": 7,
+                               "frac_fp32_vector_nonpacked_78.6": tf / 78.6,
+                               "state_GBps": B * HV * 2 * D * D * 4 / (ms / 1e3) / 1e9,
+                               "exact_ms": ms_x,
+                               "exact_TFLOPs": upd * D * D * 7 / (ms_x / 1e3) / 1e12}
+        del sts
 
     # tail_b32: layer tail B=32
     if want("tail_b32"):

@@ -135,6 +135,55 @@ __global__ __launch_bounds__(W * 64) void k_step(StepArgs a, int n_tiles, int ep
     } while (w.next());
 }
 
+// --------------------------------------------------- gdn_step, cached state
+// gdn_step_ex with GDN_STATE_CACHED: the caller's states stay resident in
+// the Infinity Cache across calls, so the state goes through the caches and
+// the launch is laid out for latency rather than for a streaming window.
+// Each wave takes TPW consecutive tiles of one head (every head's 16 tiles
+// split over 16 / TPW waves), issues all their state loads at once, reads
+// the head's k, q, beta and gate once, and then updates and stores its tiles
+// one after the other.  Same per-row arithmetic as k_step, so the same bits.
+// Measured on MI355X, 100 calls with fresh inputs per call: B = 64 (a
+// 128 MiB state) 4.15 ms against 4.48 ms for the nontemporal walk and
+// 4.95 ms for the walk with cached state access; B = 32 2.04 against
+// 2.37 ms.  With 4 tiles per wave 0.5-2 % slower.  Beyond the Infinity
+// Cache (one 512 MiB state) it is 20 % slower than the default.
+template <int TPW, int W>
+__global__ __launch_bounds__(W * 64) void k_step_cached(StepArgs a, int n_tiles) {
+    static_assert(kTilesPerHead % TPW == 0, "a wave's tiles must share a head");
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = lane >> 3;
+    const int c = lane & 7;
+    const int t0 = (static_cast<int>(blockIdx.x) * W + wave) * TPW;
+    if (t0 >= n_tiles) return;
+    const int head = t0 / kTilesPerHead;
+    const int b = head / a.Hv;
+    const int h = head - b * a.Hv;
+    const int kh = h % a.Hk;                                   // key-head broadcast
+    float *Mh = a.state + static_cast<int64_t>(head) * (D * D);
+    const int row0 = (t0 % kTilesPerHead) * kRowsPerTile + grp;
+    RowSlice r[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) load_row<false>(r[j], Mh + (row0 + j * kRowsPerTile) * D, c);
+    VecSlice kv, qv;
+    load_vec(kv, a.k + b * a.qk_bstride + kh * D, c);
+    load_vec(qv, a.q + b * a.qk_bstride + kh * D, c);
+    const float bt = a.beta[head];
+    const float e = expf(a.gate[head]);
+    float vj[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) vj[j] = a.v[b * a.v_bstride + h * D + row0 + j * kRowsPerTile];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        const float sk = group_sum(head_part(r[j], kv, e));   // decay, key product
+        update_part(r[j], (vj[j] - sk) * bt, kv);              // correction, rank-1
+        store_row<false>(Mh + (row0 + j * kRowsPerTile) * D, r[j], c);
+        const float o = group_sum(dot_part(r[j], qv)) * kInvSqrtD;   // read-out
+        if (c == 0) a.out[static_cast<int64_t>(head) * D + row0 + j * kRowsPerTile] = o;
+    }
+}
+
 // ------------------------------------------------------------- gdn_pair
 // Speculative two-position step (docs.rs "Module linear_core", gdn_pair):
 // the same persistent tile walk as k_step; each row is read once, advanced
@@ -222,12 +271,24 @@ constexpr int kEpochIters = 4;
 constexpr size_t kEpochLdsBytes = 96 * 1024;
 constexpr int64_t kMaxEpochWgs = int64_t(1) << 22;
 
+constexpr int kCachedTilesPerWave = 8;
+constexpr int kCachedWaves = 4;
+
 template <bool NT>
 hipError_t launch_step_policy(const StepArgs &a, hipStream_t s) {
     const int64_t tiles = static_cast<int64_t>(a.B) * a.Hv * kTilesPerHead;
     const int nt = static_cast<int>(tiles);
     if (tiles <= kOneShotTiles) {
         k_step<false, 1, NT><<<dim3(static_cast<unsigned>(tiles)), dim3(64), 0, s>>>(a, nt, nt, 1);
+        return hipGetLastError();
+    }
+    // (a launch past 2^32 work-items, a state far beyond any GPU's memory,
+    // falls back to the walk)
+    constexpr int64_t per_wg = kCachedTilesPerWave * kCachedWaves;
+    if (!NT && (tiles + per_wg - 1) / per_wg * kCachedWaves * 64 <= INT64_C(0xffffffff)) {
+        k_step_cached<kCachedTilesPerWave, kCachedWaves>
+            <<<dim3(static_cast<unsigned>((tiles + per_wg - 1) / per_wg)), dim3(kCachedWaves * 64),
+               0, s>>>(a, nt);
         return hipGetLastError();
     }
     int64_t full = device_cus() * static_cast<int64_t>(GDN_STEP_WGS_PER_CU);

@@ -283,37 +283,24 @@ __global__ __launch_bounds__(kTailThreads) void k_tail(TailFusedArgs a) {
     for (int p = 0; p < NP; ++p) e[p] = expf(gt[p]);
     __syncthreads();
 
-    // 4. the state step on the preloaded rows, one position after the other;
-    //    k and q come from LDS.  Position 1's rows go back to `state`, a
-    //    pair's position 2 rows to `state_next`.
-    if constexpr (NP == 1) {
+    // 4. the state step on the preloaded rows; k and q come from LDS.  All of
+    //    the wave's rows take position 1 and go back to `state`; a pair's
+    //    rows then take position 2 and go to `state_next` (2 % faster at
+    //    B = 32 than both positions tile by tile; same bits).
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
         VecSlice kv, qv;
-        load_vec(kv, act[0] + D, c);
-        load_vec(qv, act[0], c);
+        load_vec(kv, act[p] + D, c);
+        load_vec(qv, act[p], c);
+        float *dst = p == 0 ? a.state : a.state_next;
 #pragma unroll
         for (int j = 0; j < kTPW; ++j) {
             const int t = wave * kTPW + j;
             const int i = t / kTilesPerHead;
             const int row = (t % kTilesPerHead) * kRowsPerTile + grp;
-            const float o = row_token(r[j], kv, qv, e[0], bt[0], act[0][(2 + i) * D + row]);
-            store_row<true>(a.state + roff[j], r[j], c);
-            if (c == 0) core[0][i * D + row] = o;
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < kTPW; ++j) {
-            const int t = wave * kTPW + j;
-            const int i = t / kTilesPerHead;
-            const int row = (t % kTilesPerHead) * kRowsPerTile + grp;
-#pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                VecSlice kv, qv;
-                load_vec(kv, act[p] + D, c);
-                load_vec(qv, act[p], c);
-                const float o = row_token(r[j], kv, qv, e[p], bt[p], act[p][(2 + i) * D + row]);
-                store_row<true>((p == 0 ? a.state : a.state_next) + roff[j], r[j], c);
-                if (c == 0) core[p][i * D + row] = o;
-            }
+            const float o = row_token(r[j], kv, qv, e[p], bt[p], act[p][(2 + i) * D + row]);
+            store_row<true>(dst + roff[j], r[j], c);
+            if (c == 0) core[p][i * D + row] = o;
         }
     }
     __syncthreads();

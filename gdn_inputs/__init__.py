@@ -68,6 +68,9 @@ WORKLOADS = {
     "seq_b8_t4096": dict(B=8, T=4096, seed=1003),
     # gdn_layer_tail, 32 sequences, 8192 channels
     "tail_b32": dict(B=32, seed=1004),
+    # gdn_seq with many heads and a short sequence: 256 sequences x 64 tokens
+    # from seeded states (a secondary line, not one of the five configs)
+    "seq_b256_t64": dict(B=256, T=64, seed=1005),
 }
 
 

@@ -197,9 +197,11 @@ def test_nan_stays_in_its_row(g):
     assert np.array_equal(Mg[mask], clean_M[mask]) and np.array_equal(og[mask], clean_o[mask])
 
 
-# B = 1: one wave per tile; 64: the persistent walk (the Infinity-Cache
-# resident decode); 300 x 33 heads: 4-pass epochs
-@pytest.mark.parametrize("B,Hv,Hk", [(1, 32, 16), (64, 32, 16), (300, 33, 11)])
+# B = 1: one wave per tile (both policies); 64: the Infinity-Cache resident
+# decode (cached: 8 tiles per wave, 4 waves per workgroup; default: the
+# persistent walk); 17 x 33 heads: the last cached workgroup half empty;
+# 300 x 33 heads: the default launch runs as 4-pass epochs
+@pytest.mark.parametrize("B,Hv,Hk", [(1, 32, 16), (64, 32, 16), (17, 33, 11), (300, 33, 11)])
 def test_step_cached_policy_is_bitwise(g, orc, B, Hv, Hk):
     """gdn_step_ex with GDN_STATE_CACHED (state through the caches) gives the
     bits of gdn_step (nontemporal state), over two chained calls, and matches
