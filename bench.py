@@ -433,6 +433,10 @@ def extra_measurements(torch, g, stream, only=None):
         call = g.bind_step(si["q"], si["k"], si["v"], si["beta"], si["gate"], M, o, stream=stream)
         ms = timeit(call, 1000)
         res["step_b1"]["prepared_us_per_call"] = ms * 1e3
+        call = g.bind_step(si["q"], si["k"], si["v"], si["beta"], si["gate"], M, o, stream=stream,
+                           cached=True)
+        ms = timeit(call, 1000)
+        res["step_b1"]["prepared_cached_us_per_call"] = ms * 1e3
         # the same call replayed from a captured graph of 100 calls (no host
         # launch path in the loop: device-side time per call)
         side = torch.cuda.Stream()
@@ -444,6 +448,13 @@ def extra_measurements(torch, g, stream, only=None):
         torch.cuda.synchronize()
         ms = timeit(gr.replay, 10) / 100
         res["step_b1"]["graph_us_per_call"] = ms * 1e3
+        gr2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr2, stream=side):
+            for _ in range(100):
+                g.step(si["q"], si["k"], si["v"], si["beta"], si["gate"], M, o, cached=True)
+        torch.cuda.synchronize()
+        ms = timeit(gr2.replay, 10) / 100
+        res["step_b1"]["graph_cached_us_per_call"] = ms * 1e3
 
     # step_b64_x100: B=64 decode, 100 calls with fresh inputs
     if want("step_b64_x100"):

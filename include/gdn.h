@@ -327,6 +327,9 @@ size_t gdn_layer_tail_ba_workspace_bytes(const gdn_dims *dims, int32_t B);
  * scratch, which keeps the last call's contents: calls that overlap on one
  * GPU (on different streams, or from threads without ordering between them)
  * race when they take the three-launch path; calls on one stream do not.
+ * The first call on a device looks the scratch's address up
+ * (hipGetSymbolAddress): a caller that captures the call into a HIP graph
+ * makes one call before capturing.
  */
 int gdn_layer_tail_noalloc(const gdn_dims *dims, const gdn_tail_params *params, int32_t B,
                            const float *x, const float *conv_w, float *conv_state,

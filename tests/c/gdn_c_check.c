@@ -11,6 +11,8 @@
  *   6. gdn_gate_transform: sigmoid(0) = 1/2 exactly, sigmoid(ln 3) = 3/4,
  *      gate = -ln 2 at a zero softplus argument, exp(gate) = 1 - beta when
  *      a_log = dt_bias = 0 and the alpha logit equals the beta logit
+ *   7. gdn_step_ex with GDN_STATE_CACHED == gdn_step, bit for bit, and an
+ *      unknown flag bit is refused
  * Exits 0 on success; prints the first failure otherwise.
  */
 #include <hip/hip_runtime_api.h>
@@ -230,6 +232,33 @@ int main(void) {
         if (gdn_gate_transform(&dims, B, &gin, db, dba, NULL) != GDN_ERR_ALIAS)
             return fail("gate aliasing ba not rejected", 0);
         hipFree(dba); hipFree(dal); hipFree(ddt); hipFree(db); hipFree(dg);
+    }
+
+    /* 7. the cached-state policy gives the bits of the default */
+    {
+        float *M1, *M2d, *o1, *o2;
+        HIP_OK(hipMalloc((void **)&M1, NS * 4));
+        HIP_OK(hipMalloc((void **)&M2d, NS * 4));
+        HIP_OK(hipMalloc((void **)&o1, (size_t)B * HV * D * 4));
+        HIP_OK(hipMalloc((void **)&o2, (size_t)B * HV * D * 4));
+        HIP_OK(hipMemcpy(M1, d.M, NS * 4, hipMemcpyDeviceToDevice));
+        HIP_OK(hipMemcpy(M2d, d.M, NS * 4, hipMemcpyDeviceToDevice));
+        if (gdn_step(&dims, B, d.q, d.k, d.v, d.beta, d.gate, M1, o1, NULL) != GDN_OK ||
+            gdn_step_ex(&dims, B, d.q, d.k, d.v, d.beta, d.gate, M2d, o2, GDN_STATE_CACHED,
+                        NULL) != GDN_OK)
+            return fail(gdn_last_error(), 0);
+        if (gdn_step_ex(&dims, B, d.q, d.k, d.v, d.beta, d.gate, M2d, o2, 2u, NULL) !=
+            GDN_ERR_SHAPE)
+            return fail("unknown gdn_step_ex flag not rejected", 0);
+        float *h1 = (float *)malloc(NS * 4), *h2 = (float *)malloc(NS * 4);
+        HIP_OK(hipMemcpy(h1, M1, NS * 4, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(h2, M2d, NS * 4, hipMemcpyDeviceToHost));
+        if (memcmp(h1, h2, NS * 4) != 0) return fail("cached-policy state != gdn_step", 0);
+        HIP_OK(hipMemcpy(h1, o1, (size_t)B * HV * D * 4, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(h2, o2, (size_t)B * HV * D * 4, hipMemcpyDeviceToHost));
+        if (memcmp(h1, h2, (size_t)B * HV * D * 4) != 0) return fail("cached-policy out != gdn_step", 0);
+        free(h1); free(h2);
+        hipFree(M1); hipFree(M2d); hipFree(o1); hipFree(o2);
     }
 
     HIP_OK(hipDeviceSynchronize());

@@ -126,6 +126,46 @@ def test_graph_capture_gate_transform_and_tail_ba(g):
             {"M": M, "cs": ti["conv_state"]}, {"y": torch.empty((B, 4096), device="cuda")})
 
 
+def test_graph_capture_cached_step_tail_pair_noalloc(g):
+    """gdn_step_ex with GDN_STATE_CACHED (one wave per tile at B = 1, the
+    one-shot cached layout at B = 64), gdn_layer_tail_pair, and
+    gdn_layer_tail_noalloc on both launch paths (after one call outside the
+    capture, which looks up the static scratch's address)."""
+    import torch
+    print("\n  graph capture: cached step, tail pair, no-alloc tail", flush=True)
+    for B in (1, 64):
+        si = {n: dev(x) for n, x in gi.step_inputs(6010 + B, 0, B).items()}
+        M = dev(gi.state(6010 + B, 0, B))
+        _replay_matches_eager(
+            lambda st, o: g.step(si["q"], si["k"], si["v"], si["beta"], si["gate"], st["M"],
+                                 o["out"], cached=True),
+            {"M": M}, {"out": torch.empty((B, 32, 128), device="cuda")})
+        del M
+    B = 4
+    t1 = {n: dev(x) for n, x in gi.tail_inputs(6020, B, slot=0).items()}
+    t2 = {n: dev(x) for n, x in gi.tail_inputs(6020, B, slot=1).items()}
+    pr = {n: torch.stack([t1[n], t2[n]], dim=1).contiguous() for n in ("x", "beta", "gate", "z")}
+    M = dev(gi.state(6020, 0, B))
+    _replay_matches_eager(
+        lambda st, o: g.layer_tail_pair(pr["x"], t1["conv_w"], st["cs"], o["csn"], pr["beta"],
+                                        pr["gate"], st["M"], o["Mn"], pr["z"], t1["norm_w"],
+                                        o["y"]),
+        {"M": M, "cs": t1["conv_state"]},
+        {"y": torch.empty((B, 2, 4096), device="cuda"), "Mn": torch.empty_like(M),
+         "csn": torch.empty_like(t1["conv_state"])})
+    for fu in (0, 1):
+        p = g.TailParams(4, 128, 1e-6, fu)
+        warm = (M.clone(), t1["conv_state"].clone(), torch.empty((B, 4096), device="cuda"))
+        g.layer_tail_noalloc(t1["x"], t1["conv_w"], warm[1], t1["beta"], t1["gate"], warm[0],
+                             t1["z"], t1["norm_w"], warm[2], params=p)
+        torch.cuda.synchronize()
+        _replay_matches_eager(
+            lambda st, o: g.layer_tail_noalloc(t1["x"], t1["conv_w"], st["cs"], t1["beta"],
+                                               t1["gate"], st["M"], t1["z"], t1["norm_w"],
+                                               o["y"], params=p),
+            {"M": M, "cs": t1["conv_state"]}, {"y": torch.empty((B, 4096), device="cuda")})
+
+
 def test_concurrent_host_threads(g):
     """Four host threads, each on its own stream and buffers, call gdn_step
     and gdn_seq repeatedly at the same time."""
