@@ -144,6 +144,40 @@ def test_tail_three_tokens_fill_the_cache(g, orc):
     ref.assert_close("state", Md.cpu().numpy(), M, 1e-6)
 
 
+@pytest.mark.parametrize("Hv,Hk", [(22, 11), (11, 11)])
+def test_tail_other_head_counts(g, orc, Hv, Hk):
+    """Key-head counts other than the page's (5632 / 4224 channels), single
+    launch and three launches, against the oracle."""
+    print(f"\n  gdn_layer_tail Hv={Hv} Hk={Hk}", flush=True)
+    dims = g.Dims(Hv, Hk, 128, 128)
+    ti = gi.tail_inputs(4600 + Hv, 3, Hv, Hk)
+    M = gi.state(4600 + Hv, 0, 3, Hv)
+    for fu in (0, 1):
+        got = run_tail(g, ti, M, dims=dims, params=g.TailParams(4, 128, 1e-6, fu))
+        want = oracle_tail(orc, ti, M.copy(), Hk=Hk)
+        check(got, want)
+
+
+def test_tail_degenerate_inputs(g, orc):
+    """Degenerate cases of the branch: one sequence's channels all zero (its
+    Q and K heads hit the L2 floor and stay zero, so the step sees a zero key
+    and only decays), another's gates at -80 (the decay underflows towards a
+    full forget), and a zero state, against the oracle on both launch paths."""
+    print("\n  gdn_layer_tail degenerate inputs", flush=True)
+    B = 4
+    ti = gi.tail_inputs(4700, B)
+    ti["x"][1] = 0.0
+    ti["conv_state"][1] = 0.0
+    ti["gate"][2] = -80.0
+    M = gi.state(4700, 0, B)
+    M[3] = 0.0
+    for fu in (0, 1):
+        got = run_tail(g, ti, M, params=g.TailParams(4, 128, 1e-6, fu))
+        want = oracle_tail(orc, ti, M.copy())
+        check(got, want)
+        assert np.all(got["qkv"][1] == 0.0), "zero channels must stay zero through L2"
+
+
 def test_tail_b128(g, orc):
     """A larger batch (B=128: 2048 workgroups of the single-launch tail)."""
     print("\n  gdn_layer_tail B=128", flush=True)

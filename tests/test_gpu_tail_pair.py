@@ -52,7 +52,8 @@ def run_pair(g, pi, M, dims):
 
 # B = 32: the page's tail batch; B = 1, 5: small and odd; Hv = Hk: one value
 # head per key head (the other single-launch shape)
-@pytest.mark.parametrize("B,Hv,Hk", [(32, 32, 16), (1, 32, 16), (5, 32, 16), (3, 16, 16)])
+@pytest.mark.parametrize("B,Hv,Hk", [(32, 32, 16), (1, 32, 16), (5, 32, 16), (3, 16, 16),
+                                     (7, 22, 11)])
 def test_tail_pair_matches_oracle(g, orc, B, Hv, Hk):
     print(f"\n  gdn_layer_tail_pair B={B} Hv={Hv} Hk={Hk}", flush=True)
     dims = g.Dims(Hv, Hk, 128, 128)
