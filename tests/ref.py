@@ -2,7 +2,7 @@
 threads (ctypes releases the GIL during the C call), error reporting, and the
 parity records every check appends to (written out as JSON lines at the end
 of a GPU session, one record per compared quantity: max abs, max rel, the
-tolerance and the verdict, with the workload named where the test is one)."""
+tolerance and whether it passed, with the workload named where the test is one)."""
 from __future__ import annotations
 
 import os
