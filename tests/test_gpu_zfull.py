@@ -3,10 +3,13 @@ times, checked against the oracle element by element (every sequence of every
 layer for step_b256_x36, whose pre-states are regenerated on the host layer
 by layer).
 
-  step_b64_x100: B=64 decode, 100 gdn_step calls with fresh inputs
+  step_b64_x100: B=64 decode, 100 gdn_step calls with fresh inputs (both
+                 cache policies the benchmark times)
   step_b256_x36: B=256 x 36 layers (18 GiB of state), one gdn_step per
                  layer, plus the same 36 layers flattened into one B=9216 call
   seq_b8_t4096:  gdn_seq B=8 x T=4096 from a zero state
+  seq_b256_t64:  gdn_seq B=256 x T=64 from seeded states (the benchmark's
+                 many-heads short-sequence line)
 """
 import numpy as np
 import pytest
@@ -48,8 +51,17 @@ def test_step_b64_x100(g, orc, workload):
         g.step(t["q"], t["k"], t["v"], t["beta"], t["gate"], Md, outs[i])
         if i == 0:
             M1 = Md.cpu().numpy()
+    # the same 100 calls with GDN_STATE_CACHED (the benchmark's cached line):
+    # bitwise the default policy's results
+    Mc = dev(M)
+    outs_c = torch.empty_like(outs)
+    for i in range(calls):
+        t = dins[i]
+        g.step(t["q"], t["k"], t["v"], t["beta"], t["gate"], Mc, outs_c[i], cached=True)
     torch.cuda.synchronize()
     Mg, og = Md.cpu().numpy(), outs.cpu().numpy()
+    assert np.array_equal(Mc.cpu().numpy(), Mg) and np.array_equal(outs_c.cpu().numpy(), og), \
+        "cached policy differs from the default over 100 calls"
     worst = 0.0
     M64 = M.astype(np.float64)
     e_gpu = e_orc = 0.0
@@ -183,3 +195,39 @@ def test_seq_b8_t4096(g, orc, workload):
         ref.record(name=f"seq vs seq_exact {what}", max_abs=gap, bound=bound, passed=gap <= bound)
         print(f"    seq vs seq_exact {what}: {gap:.3e} (bound {bound:.3e})", flush=True)
         assert gap <= bound, f"gdn_seq and gdn_seq_exact differ by {gap:.3e} in {what}"
+
+
+@pytest.mark.timeout(600)
+def test_seq_b256_t64(g, orc, workload):
+    """gdn_seq at the benchmark's B=256 x T=64 (8192 heads: half heads, three
+    workgroups per CU) against the oracle, every element, and the binary64
+    yardstick on 8 of the sequences; gdn_seq_exact likewise."""
+    import torch
+    workload("seq_b256_t64")
+    c = gi.WORKLOADS["seq_b256_t64"]
+    B, T = c["B"], c["T"]
+    print(f"\n  seq_b256_t64: gdn_seq and gdn_seq_exact B={B} T={T}", flush=True)
+    si = gi.step_inputs(c["seed"], 0, B, T=T)
+    M = gi.state(c["seed"], 0, B)
+    t = {n: dev(x) for n, x in si.items()}
+    res = {}
+    for exact in (False, True):
+        Md = dev(M)
+        out = torch.empty((B, T, 32, 128), device="cuda")
+        g.seq(t["q"], t["k"], t["v"], t["beta"], t["gate"], Md, out, exact=exact)
+        torch.cuda.synchronize()
+        res[exact] = (Md.cpu().numpy(), out.cpu().numpy())
+        del Md, out
+    Mo = M.copy()
+    want = ref.seq_mt(orc, si, Mo)
+    s8 = {n: np.ascontiguousarray(x[:8]) for n, x in si.items()}
+    M64 = M[:8].astype(np.float64)
+    Mo8 = M[:8].copy()
+    want8 = ref.seq_mt(orc, s8, Mo8)
+    out64 = ref.seq_f64_mt(orc, s8, M64)
+    for exact, tag in ((False, "seq"), (True, "seq_exact")):
+        Mg, og = res[exact]
+        ref.assert_close(f"{tag} state", Mg, Mo, 1e-6)
+        ref.assert_close(f"{tag} out", og, want, 1e-5)
+        ref.assert_vs_f64(f"{tag} state[:8]", Mg[:8], Mo8, M64)
+        ref.assert_vs_f64(f"{tag} out[:8]", og[:8], want8, out64)
