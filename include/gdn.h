@@ -123,7 +123,8 @@ int gdn_step_ex(const gdn_dims *dims, int32_t B,
 /*
  * gdn_seq - T tokens for B sequences, run in order with the state carried
  * (docs.rs "Module linear_core", gdn_forward_batch: the recurrence runs
- * sequentially over positions, elementwise identical to single steps).
+ * over the positions one after another, with the same elementwise results
+ * as single steps).
  *   q, k   [B][T][n_k_heads][d_k]
  *   v      [B][T][n_v_heads][d_v]
  *   beta, gate [B][T][n_v_heads]
@@ -165,8 +166,9 @@ int gdn_seq_exact(const gdn_dims *dims, int32_t B, int32_t T,
 
 /*
  * gdn_pair - two consecutive positions for B sequences, fused for speculative
- * verification (docs.rs "Module linear_core", gdn_pair: lane 1 commits into
- * the state, lane 2 is tentative in scratch).  Position 1 advances `state`
+ * verification (docs.rs "Module linear_core", gdn_pair: the first position's
+ * update is kept, the second's is held aside until the draft is accepted or
+ * rejected).  Position 1 advances `state`
  * in place (committed); position 2 advances the committed state into
  * `state_next` (tentative: the caller adopts it on acceptance, e.g. by
  * swapping the buffers, or drops it on rejection).
@@ -221,9 +223,9 @@ int gdn_layer_tail(const gdn_dims *dims, const gdn_tail_params *params, int32_t 
 
 /*
  * gdn_layer_tail_pair - gdn_layer_tail for two consecutive positions fused
- * for speculative verification (docs.rs "Module linear_core", gdn_pair: lane
- * 1 commits into the state, lane 2 is tentative in scratch, the conv ring
- * and the recurrent state moving together).  Position 1 advances
+ * for speculative verification (docs.rs "Module linear_core", gdn_pair: the
+ * first position's update is kept, the second's is held aside, and the
+ * conv ring is held aside with the recurrent state).  Position 1 advances
  * `conv_state` and `state` in place (committed); position 2 starts from the
  * committed ring and state and writes its ring to `conv_state_next` and its
  * state to `state_next` (tentative: the caller adopts both on acceptance,

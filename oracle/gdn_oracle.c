@@ -223,8 +223,8 @@ void oracle_gdn_seq_f64(int32_t B, int32_t T, int32_t Hv, int32_t Hk, int32_t dk
     }
 }
 
-/* [linear_core] the batch path walks the positions in order; each position
- * is one single-token step on the carried state. */
+/* [linear_core] the batch path takes the positions one after another; each
+ * position is one single-token step on the carried state. */
 void oracle_gdn_seq(int32_t B, int32_t T, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv,
                     const float *q, const float *k, const float *v,
                     const float *beta, const float *gate,
@@ -396,12 +396,13 @@ void oracle_layer_tail(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv
 }
 
 /*
- * [linear_core] gdn_pair applied to the whole recurrent branch: "lane 1
- * commits into state, lane 2 is tentative in scratch (ring + S move
- * together)".  Position 1 is one layer tail on the committed conv ring and
- * state.  Position 2 is one layer tail that starts from what position 1
- * committed, run on copies: its ring and state go to the tentative buffers,
- * so the committed ones stay as position 1 left them.
+ * [linear_core] gdn_pair applied to the whole recurrent branch: the first
+ * position's update is kept, the second's is held aside, and the conv ring
+ * is held aside together with the state.  Position 1 is one layer tail on
+ * the committed conv ring and state.  Position 2 is one layer tail that
+ * starts from what position 1 committed, run on copies: its ring and state
+ * go to the tentative buffers, so the committed ones stay as position 1 left
+ * them.
  *   x [B][2][C]; beta, gate [B][2][Hv]; z, y [B][2][Hv*dv]
  *   conv_state [B][K-1][C] in/out (committed), conv_state_next out (tentative)
  *   M [B][Hv][dv][dk] in/out (committed), M_next out (tentative)

@@ -19,9 +19,10 @@
  *             "Validation boundary" (order of the prestate stages) and
  *             "DeltaNet projection parity - real layer 0" (RMS epsilon).
  *   [linear_core] docs.rs "Module linear_core" (cortiq_engine), functions
- *             gdn_forward / gdn_forward_batch (one position advances the
- *             state; the batch form runs the recurrence over positions in
- *             order and is elementwise identical to the single-step path).
+ *             gdn_forward / gdn_forward_batch (a call moves the state on by
+ *             one position; the batch form takes the positions one after
+ *             another and gives the single-position results element for
+ *             element), gdn_pair.
  *
  * Precision: the pages fix F32 for the state, the vectors and the conv path,
  * so the authority functions compute in binary32 with sequential sums and no
@@ -96,7 +97,8 @@ void oracle_gdn_pair(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv,
                      const float *beta, const float *gate,
                      float *M, float *M_next, float *out);
 
-/* [dev15a] "conv-state shift, real F32 ssm_conv1d, SiLU" for one token.
+/* [dev15a] the conv stage of the prestate for one token: shift of the conv
+ * cache, causal conv1d with the F32 weights, then SiLU.
  *   x          [B][C]        raw pre-conv channels of this token
  *   conv_w     [C][K]        tap 0 is applied to the oldest input
  *   conv_state [B][K-1][C]   slot 0 = oldest; in/out (shifted by one)
@@ -109,7 +111,8 @@ void oracle_conv_silu(int32_t B, int32_t C, int32_t K,
  * is divided by its Euclidean norm (floored at 1e-6).  In place. */
 void oracle_l2norm_rows(int32_t n, int32_t d, float *u);
 
-/* [dev15e] "gated RMSNorm with ssm_norm.weight and SiLU(z)".
+/* [dev15e] the tail's normalisation: RMSNorm per group, scaled by the norm
+ * weight and gated by SiLU(z).
  *   o, z, y [rows][n]; the norm runs over consecutive groups of `group`
  *   elements; w [group] is indexed by the position inside the group.
  *   y = o / sqrt(mean(o^2) + eps) * w * SiLU(z). */
@@ -131,7 +134,7 @@ void oracle_layer_tail(int32_t B, int32_t Hv, int32_t Hk, int32_t dk, int32_t dv
                        const float *z, const float *norm_w, float *y,
                        float *qkv_out, float *core_out);
 
-/* [linear_core] gdn_pair over the whole tail ("ring + S move together"):
+/* [linear_core] gdn_pair over the whole tail, conv ring and state together:
  * position 1 commits conv ring and state; position 2 runs from the committed
  * ones and writes its ring and state to the tentative buffers.
  *   x [B][2][C]; beta, gate [B][2][Hv]; z, y [B][2][Hv*dv]

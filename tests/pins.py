@@ -500,7 +500,7 @@ def pin_tail_composition(o):
 
 
 def pin_tail_pair_ring_and_state_move_together(o):
-    """linear_core gdn_pair over the tail ("ring + S move together"):
+    """linear_core gdn_pair over the tail, conv ring and state held aside together:
       * the committed conv ring holds [cs_1, cs_2, x_1] and the tentative one
         [cs_2, x_1, x_2] (the last K-1 raw inputs after each position,
         bitwise, independent of any arithmetic);

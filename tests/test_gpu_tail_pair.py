@@ -1,6 +1,6 @@
 """GPU: gdn_layer_tail_pair, the speculative pair over the whole recurrent
-branch (docs.rs "Module linear_core", gdn_pair: lane 1 commits, lane 2 is
-tentative, conv ring and state moving together), against the oracle
+branch (docs.rs "Module linear_core", gdn_pair: the first position is kept,
+the second held aside with its conv ring and state), against the oracle
 (oracle_layer_tail_pair), and its bitwise contract with two gdn_layer_tail
 calls."""
 import numpy as np
