@@ -141,9 +141,13 @@ constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
 // hipGetSymbolAddress on the first call per device and cached.
 hipError_t noalloc_scratch(void **ptr);
 
-// True when launch_tail_fused supports these sizes (value heads per key head
-// 1 or 2, conv kernel 4, gated-norm group equal to the head dimension).
-bool tail_fused_supported(int32_t Hv, int32_t Hk, int32_t K, int32_t group);
+// True when launch_tail_fused and launch_tail_pair have a kernel for these
+// sizes: value heads per key head 1 or 2 (Hv a multiple of Hk, Hk >= 1, as
+// the ABI checks first), conv kernel 4, gated-norm group equal to the head
+// dimension.
+inline bool tail_fused_supported(int32_t Hv, int32_t Hk, int32_t K, int32_t group) {
+    return (Hv == Hk || Hv == 2 * Hk) && K == 4 && group == kHeadDim;
+}
 
 // Compute units of the current device, read once per device and cached
 // (256 on MI355X; 256 too if the query fails).

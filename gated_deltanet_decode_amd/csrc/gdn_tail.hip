@@ -361,11 +361,6 @@ hipError_t noalloc_scratch(void **ptr) {
     return hipSuccess;
 }
 
-bool tail_fused_supported(int32_t Hv, int32_t Hk, int32_t K, int32_t group) {
-    const int32_t rv = Hv / Hk;
-    return (rv == 1 || rv == 2) && K == 4 && group == D;
-}
-
 hipError_t launch_tail_fused(const TailFusedArgs &a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hk));
     const bool raw = a.ba != nullptr;

@@ -1,6 +1,6 @@
-"""CPU: sanitizer run of the oracle, thread-local error messages of the C
-ABI, the input generator's determinism and slice regeneration, and the
-package failing loudly without its library."""
+"""CPU: sanitizer runs of the oracle and of the C-ABI layer, thread-local
+error messages of the C ABI, the input generator's determinism and slice
+regeneration, and the package failing loudly without its library."""
 import ctypes
 import os
 import shutil
@@ -25,6 +25,32 @@ def test_oracle_under_asan_ubsan(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "ok" in r.stdout
+
+
+def test_abi_layer_under_asan_ubsan(tmp_path):
+    """gdn_api.cpp built for the host with g++ under ASan/UBSan, its kernel
+    launchers replaced by recording stubs (tests/c/gdn_api_stubs.cpp), and
+    driven through every entry point's checks and launch arguments by
+    tests/c/gdn_api_check.c."""
+    csrc = os.path.join(ROOT, "gated_deltanet_decode_amd", "csrc")
+    cdir = os.path.join(ROOT, "tests", "c")
+    san = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all"]
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", csrc, "-I", cdir]
+    hip = ["-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include"]
+    objs = []
+    for src, cmd in ((os.path.join(csrc, "gdn_api.cpp"), ["g++", "-std=c++17"] + hip),
+                     (os.path.join(cdir, "gdn_api_stubs.cpp"), ["g++", "-std=c++17"] + hip),
+                     (os.path.join(cdir, "gdn_api_check.c"), ["gcc", "-std=c99", "-Wall",
+                                                               "-Werror"])):
+        obj = str(tmp_path / (os.path.basename(src) + ".o"))
+        subprocess.run(cmd + san + inc + ["-c", src, "-o", obj], check=True)
+        objs.append(obj)
+    exe = str(tmp_path / "gdn_api_check")
+    subprocess.run(["g++"] + san + objs + ["-o", exe, "-lm"], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "C ABI host check ok" in r.stdout
 
 
 def test_last_error_is_thread_local():
