@@ -135,6 +135,34 @@ def inplace_probe(torch, stream, buf, reps=5):
     return 2 * nbytes / (ms / 1e3) / 1e9
 
 
+def small_launch_floors(torch, side, timeit, workgroups, nbytes):
+    """Per-launch device time, from a graph of 100 launches, of an empty
+    kernel of `workgroups` one-wave workgroups and of the in-place probe over
+    `nbytes` with one one-wave workgroup per 4 KiB tile."""
+    import ctypes
+    from gated_deltanet_decode_amd._build import PROBE_LIBRARY
+    lib = ctypes.CDLL(PROBE_LIBRARY)
+    lib.gdn_probe_empty.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.gdn_probe_inplace_small.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint,
+                                            ctypes.c_void_p]
+    buf = torch.zeros(nbytes // 4, device="cuda")
+    torch.cuda.synchronize()
+    calls = {
+        "graph_empty_launch_us": lambda: lib.gdn_probe_empty(workgroups, 64, side.cuda_stream),
+        "graph_inplace_probe_us": lambda: lib.gdn_probe_inplace_small(
+            buf.data_ptr(), nbytes, 0, side.cuda_stream),
+    }
+    out = {}
+    for name, fn in calls.items():
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=side):
+            for _ in range(100):
+                assert fn() == 0
+        torch.cuda.synchronize()
+        out[name] = timeit(gr.replay, 10) / 100 * 1e3
+    return out
+
+
 def fma_probe(torch, stream, workgroups, threads, iters=20000, reps=3):
     """Non-packed FP32 FMA rate (TFLOP/s) of independent fmaf chains with no
     memory traffic, at `workgroups` x `threads` threads: the VALU ceiling at
@@ -455,6 +483,10 @@ def extra_measurements(torch, g, stream, only=None):
         torch.cuda.synchronize()
         ms = timeit(gr2.replay, 10) / 100
         res["step_b1"]["graph_cached_us_per_call"] = ms * 1e3
+        # floors of this launch, replayed the same way: an empty kernel of the
+        # step's shape at B = 1 (512 one-wave workgroups) and the in-place
+        # probe over 2 MiB with that shape (the state's bytes, no arithmetic)
+        res["step_b1"].update(small_launch_floors(torch, side, timeit, 512, 2 << 20))
 
     # step_b64_x100: B=64 decode, 100 calls with fresh inputs
     if want("step_b64_x100"):

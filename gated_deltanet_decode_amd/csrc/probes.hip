@@ -10,7 +10,9 @@
 //    kernel is (nontemporal 16-byte accesses, persistent XCD-aware walk);
 //  - a stream of independent non-packed FP32 FMAs with no memory traffic:
 //    the issue rate the VALU sustains at a given number of waves per CU, the
-//    practical ceiling for the multi-token kernel.
+//    practical ceiling for the multi-token kernel;
+//  - an empty kernel and the in-place probe with one wave per tile: the
+//    floors of a small, latency-bound launch.
 
 #include <hip/hip_runtime.h>
 
@@ -35,10 +37,12 @@ __global__ __launch_bounds__(256) void k_copy_probe(const f4 *__restrict__ src,
 typedef unsigned int u4 __attribute__((ext_vector_type(4)));
 constexpr int kProbeWaves = 8;
 
-// src == dst: the in-place probe; otherwise a copy with the same walk.
-__global__ __launch_bounds__(kProbeWaves * 64) void k_inplace_probe(const f4 *src, f4 *dst,
-                                                                    int64_t n_tiles,
-                                                                    unsigned key) {
+// src == dst: the in-place probe; otherwise a copy with the same walk.  W:
+// waves per workgroup (kProbeWaves for the persistent walk; 1 with one
+// workgroup per tile, the step kernel's shape for small launches).
+template <int W>
+__global__ __launch_bounds__(W * 64) void k_inplace_probe(const f4 *src, f4 *dst,
+                                                          int64_t n_tiles, unsigned key) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int grp = lane >> 3;
@@ -46,8 +50,8 @@ __global__ __launch_bounds__(kProbeWaves * 64) void k_inplace_probe(const f4 *sr
     const int G = gridDim.x;
     const int g = blockIdx.x;
     const int lg = (G % 8 == 0) ? (g % 8) * (G / 8) + g / 8 : g;
-    const int64_t stride = static_cast<int64_t>(G) * kProbeWaves;
-    for (int64_t u = static_cast<int64_t>(lg) * kProbeWaves + wave; u < n_tiles; u += stride) {
+    const int64_t stride = static_cast<int64_t>(G) * W;
+    for (int64_t u = static_cast<int64_t>(lg) * W + wave; u < n_tiles; u += stride) {
         const int64_t row = u * 256 + grp * 32;    // a tile is 256 float4, a row 32
         f4 v[4];
 #pragma unroll
@@ -60,6 +64,8 @@ __global__ __launch_bounds__(kProbeWaves * 64) void k_inplace_probe(const f4 *sr
     }
 }
 
+// Does nothing: the cost of a launch of a given shape.
+__global__ void k_empty_probe() {}
 
 // kFmaChains independent fmaf chains per lane, iterated `iters` times; one
 // float per thread is stored at the end so nothing is optimised away.  Built,
@@ -118,8 +124,9 @@ int gdn_probe_inplace(void *buf, size_t bytes, unsigned key, void *stream) {
     const int cus = device_cus();
     const int grid = static_cast<int>(need < cus ? need : cus);
     (void)hipGetLastError();
-    k_inplace_probe<<<dim3(grid), dim3(kProbeWaves * 64), 0, static_cast<hipStream_t>(stream)>>>(
-        static_cast<const f4 *>(buf), static_cast<f4 *>(buf), tiles, key);
+    k_inplace_probe<kProbeWaves>
+        <<<dim3(grid), dim3(kProbeWaves * 64), 0, static_cast<hipStream_t>(stream)>>>(
+            static_cast<const f4 *>(buf), static_cast<f4 *>(buf), tiles, key);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
@@ -135,8 +142,35 @@ int gdn_probe_copy_nt(const void *src, void *dst, size_t bytes, void *stream) {
     const int cus = device_cus();
     const int grid = static_cast<int>(need < cus ? need : cus);
     (void)hipGetLastError();
-    k_inplace_probe<<<dim3(grid), dim3(kProbeWaves * 64), 0, static_cast<hipStream_t>(stream)>>>(
-        static_cast<const f4 *>(src), static_cast<f4 *>(dst), tiles, 0u);
+    k_inplace_probe<kProbeWaves>
+        <<<dim3(grid), dim3(kProbeWaves * 64), 0, static_cast<hipStream_t>(stream)>>>(
+            static_cast<const f4 *>(src), static_cast<f4 *>(dst), tiles, 0u);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// The in-place probe with one one-wave workgroup per 4 KiB tile, the shape
+// the step kernel takes for small launches: `bytes` a multiple of 4096, at
+// most 2^36 (2^24 tiles).  Returns 0, -1 on bad arguments, -6 when the
+// launch fails.
+int gdn_probe_inplace_small(void *buf, size_t bytes, unsigned key, void *stream) {
+    if (!buf || bytes == 0 || bytes % 4096 != 0 || bytes > (size_t(1) << 36) ||
+        reinterpret_cast<size_t>(buf) % 16 != 0)
+        return -1;
+    const int64_t tiles = static_cast<int64_t>(bytes / 4096);
+    (void)hipGetLastError();
+    k_inplace_probe<1><<<dim3(static_cast<unsigned>(tiles)), dim3(64), 0,
+                         static_cast<hipStream_t>(stream)>>>(
+        static_cast<const f4 *>(buf), static_cast<f4 *>(buf), tiles, key);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// Launches an empty kernel of `workgroups` x `threads` threads (threads a
+// multiple of 64, at most 1024).  Returns 0, -1 on bad arguments, -6 when
+// the launch fails.
+int gdn_probe_empty(int workgroups, int threads, void *stream) {
+    if (workgroups < 1 || threads < 64 || threads > 1024 || threads % 64 != 0) return -1;
+    (void)hipGetLastError();
+    k_empty_probe<<<dim3(workgroups), dim3(threads), 0, static_cast<hipStream_t>(stream)>>>();
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
