@@ -42,8 +42,10 @@
  * call may have run.
  *
  * Thread safety: every call may be made concurrently from several host
- * threads.  The library's only mutable global state is the thread-local
- * error text and a per-device cache of the compute-unit count.
+ * threads.  The library's mutable global state is the thread-local error
+ * text, a per-device cache of the compute-unit count and, for
+ * gdn_layer_tail_noalloc only, a static per-GPU scratch array with a
+ * per-device cache of its address (see there for the calls that share it).
  */
 #ifndef GDN_H
 #define GDN_H
