@@ -135,6 +135,40 @@ def inplace_probe(torch, stream, buf, reps=5):
     return 2 * nbytes / (ms / 1e3) / 1e9
 
 
+def one_direction_probes(torch, stream, buf, reps=5):
+    """Rates (bytes / s) of reading `buf` only and of writing a buffer of the
+    same size only, with the in-place probe's walk and accesses: what each
+    direction reaches alone, against the in-place probe's mix of both."""
+    import ctypes
+    from gated_deltanet_decode_amd._build import PROBE_LIBRARY
+    lib = ctypes.CDLL(PROBE_LIBRARY)
+    lib.gdn_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                   ctypes.c_size_t, ctypes.c_void_p]
+    lib.gdn_probe_write.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint,
+                                    ctypes.c_void_p]
+    nbytes = buf.numel() * buf.element_size()
+    sink = torch.empty(1 << 20, dtype=torch.int32, device="cuda")
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    calls = {
+        "read": lambda: lib.gdn_probe_read(buf.data_ptr(), nbytes, sink.data_ptr(), 4 << 20,
+                                           stream.cuda_stream),
+        "write": lambda: lib.gdn_probe_write(dst.data_ptr(), nbytes, 0, stream.cuda_stream),
+    }
+    out = {}
+    for name, fn in calls.items():
+        assert fn() == 0
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for _ in range(reps):
+            assert fn() == 0
+        e.record(stream)
+        torch.cuda.synchronize()
+        out[name] = nbytes / (s.elapsed_time(e) / reps / 1e3) / 1e9
+    del dst
+    return out["read"], out["write"]
+
+
 def small_launch_floors(torch, side, timeit, workgroups, nbytes):
     """Per-launch device time, from a graph of 100 launches, of an empty
     kernel of `workgroups` one-wave workgroups and of the in-place probe over
@@ -685,6 +719,9 @@ def main():
     L, B = w["L"], w["B"]
     inplace_gbps = inplace_probe(torch, stream, w["states"][0])
     log(f"[bench] in-place probe (the step's access pattern, no arithmetic): {inplace_gbps:.0f} GB/s")
+    read_gbps, write_gbps = one_direction_probes(torch, stream, w["states"][0])
+    log(f"[bench] the same walk one way: read only {read_gbps:.0f} GB/s, write only "
+        f"{write_gbps:.0f} GB/s")
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
         run_step36(g, w, stream)
@@ -755,6 +792,8 @@ def main():
                      "plain_copy_probe_GBps": plain_copy_gbps,
                      "inplace_probe_GBps": inplace_gbps,
                      "frac_of_inplace_probe": achieved / inplace_gbps,
+                     "read_only_probe_GBps": read_gbps,
+                     "write_only_probe_GBps": write_gbps,
                      "event_bracketed_launch_us": float(np.mean(launch_ms)) * 1e3,
                      "event_bracketed_launches": len(launch_ms)},
     }

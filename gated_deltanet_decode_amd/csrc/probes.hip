@@ -8,6 +8,7 @@
 //    reaches, the practical ceiling for the step kernel;
 //  - the same walk copying between two buffers: a copy tuned as the step
 //    kernel is (nontemporal 16-byte accesses, persistent XCD-aware walk);
+//  - the same walk reading only or writing only;
 //  - a stream of independent non-packed FP32 FMAs with no memory traffic:
 //    the issue rate the VALU sustains at a given number of waves per CU, the
 //    practical ceiling for the multi-token kernel;
@@ -61,6 +62,52 @@ __global__ __launch_bounds__(W * 64) void k_inplace_probe(const f4 *src, f4 *dst
             const u4 b = __builtin_bit_cast(u4, v[i]) ^ key;
             __builtin_nontemporal_store(__builtin_bit_cast(f4, b), dst + row + 8 * i + c);
         }
+    }
+}
+
+// One direction only, with the same walk, lanes and nontemporal accesses:
+// reads every tile and folds its bits into one word per thread, written to
+// sink[thread] at the end (so the loads are kept); or writes every tile with
+// `key`.  Together with the in-place probe they show what mixing reads and
+// writes in one stream costs.
+__global__ __launch_bounds__(kProbeWaves * 64) void k_read_probe(const f4 *src, unsigned *sink,
+                                                                 int64_t n_tiles) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = lane >> 3;
+    const int c = lane & 7;
+    const int G = gridDim.x;
+    const int g = blockIdx.x;
+    const int lg = (G % 8 == 0) ? (g % 8) * (G / 8) + g / 8 : g;
+    const int64_t stride = static_cast<int64_t>(G) * kProbeWaves;
+    unsigned acc = 0;
+    for (int64_t u = static_cast<int64_t>(lg) * kProbeWaves + wave; u < n_tiles; u += stride) {
+        const int64_t row = u * 256 + grp * 32;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u4 b = __builtin_bit_cast(u4, __builtin_nontemporal_load(src + row + 8 * i + c));
+            acc ^= b.x ^ b.y ^ b.z ^ b.w;
+        }
+    }
+    sink[static_cast<int64_t>(g) * blockDim.x + threadIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(kProbeWaves * 64) void k_write_probe(f4 *dst, int64_t n_tiles,
+                                                                  unsigned key) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = lane >> 3;
+    const int c = lane & 7;
+    const int G = gridDim.x;
+    const int g = blockIdx.x;
+    const int lg = (G % 8 == 0) ? (g % 8) * (G / 8) + g / 8 : g;
+    const int64_t stride = static_cast<int64_t>(G) * kProbeWaves;
+    const u4 b = {key, key, key, key};
+    for (int64_t u = static_cast<int64_t>(lg) * kProbeWaves + wave; u < n_tiles; u += stride) {
+        const int64_t row = u * 256 + grp * 32;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_nontemporal_store(__builtin_bit_cast(f4, b), dst + row + 8 * i + c);
     }
 }
 
@@ -145,6 +192,42 @@ int gdn_probe_copy_nt(const void *src, void *dst, size_t bytes, void *stream) {
     k_inplace_probe<kProbeWaves>
         <<<dim3(grid), dim3(kProbeWaves * 64), 0, static_cast<hipStream_t>(stream)>>>(
             static_cast<const f4 *>(src), static_cast<f4 *>(dst), tiles, 0u);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// Reads `bytes` (a multiple of 4096, 16-byte aligned device memory) with
+// the in-place probe's walk; each thread writes one 32-bit word to `sink`,
+// which must hold sink_bytes >= 4 x (one 512-thread workgroup per compute
+// unit, at most one per 8 tiles) bytes.  Returns 0, -1 on bad arguments, -6
+// when the launch fails.
+int gdn_probe_read(const void *buf, size_t bytes, void *sink, size_t sink_bytes, void *stream) {
+    if (!buf || !sink || bytes == 0 || bytes % 4096 != 0 ||
+        reinterpret_cast<size_t>(buf) % 16 != 0 || reinterpret_cast<size_t>(sink) % 4 != 0)
+        return -1;
+    const int64_t tiles = static_cast<int64_t>(bytes / 4096);
+    const int64_t need = (tiles + kProbeWaves - 1) / kProbeWaves;
+    const int cus = device_cus();
+    const int grid = static_cast<int>(need < cus ? need : cus);
+    if (sink_bytes < static_cast<size_t>(grid) * kProbeWaves * 64 * sizeof(unsigned)) return -1;
+    (void)hipGetLastError();
+    k_read_probe<<<dim3(grid), dim3(kProbeWaves * 64), 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<const f4 *>(buf), static_cast<unsigned *>(sink), tiles);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// Writes `bytes` (a multiple of 4096, 16-byte aligned device memory) with
+// the in-place probe's walk, every 32-bit word set to `key`.  Returns 0, -1
+// on bad arguments, -6 when the launch fails.
+int gdn_probe_write(void *buf, size_t bytes, unsigned key, void *stream) {
+    if (!buf || bytes == 0 || bytes % 4096 != 0 || reinterpret_cast<size_t>(buf) % 16 != 0)
+        return -1;
+    const int64_t tiles = static_cast<int64_t>(bytes / 4096);
+    const int64_t need = (tiles + kProbeWaves - 1) / kProbeWaves;
+    const int cus = device_cus();
+    const int grid = static_cast<int>(need < cus ? need : cus);
+    (void)hipGetLastError();
+    k_write_probe<<<dim3(grid), dim3(kProbeWaves * 64), 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<f4 *>(buf), tiles, key);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
