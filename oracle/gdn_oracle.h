@@ -107,8 +107,9 @@ void oracle_conv_silu(int32_t B, int32_t C, int32_t K,
                       const float *x, const float *conv_w, float *conv_state,
                       float *act);
 
-/* [dev15a] "per-head Q/K L2 normalization": each of the n rows of length d
- * is divided by its Euclidean norm (floored at 1e-6).  In place. */
+/* [dev15a, Validation boundary] the L2 norm stage of the Q and K heads: each
+ * of the n rows of length d is divided by its Euclidean norm (floored at
+ * 1e-6).  In place. */
 void oracle_l2norm_rows(int32_t n, int32_t d, float *u);
 
 /* [dev15e] the tail's normalisation: RMSNorm per group, scaled by the norm
@@ -121,8 +122,9 @@ void oracle_gated_rmsnorm(int32_t rows, int32_t n, int32_t group, float eps,
                           float *y);
 
 /* [dev15e] recurrent-branch tail for one token, stages in page order:
- * conv-state shift + conv1d + SiLU, Q/K/V split ([Q | K | V] contiguous),
- * per-head Q/K L2, the state update, gated RMSNorm x SiLU(z).
+ * conv-state shift + conv1d + SiLU; the channels cut into contiguous
+ * [Q | K | V]; each Q and K head scaled to unit L2 norm; the state update;
+ * gated RMSNorm x SiLU(z).
  *   x [B][C] with C = 2*Hk*dk + Hv*dv; conv_w [C][K]; conv_state [B][K-1][C]
  *   beta, gate [B][Hv]; M [B][Hv][dv][dk]; z, y [B][Hv*dv]; norm_w [group]
  *   qkv_out  [B][C]        optional: normalized Q | K | V fed to the step

@@ -420,7 +420,7 @@ def pin_conv_special_cases(o):
 
 
 def pin_l2_norm(o):
-    """dev15a per-head Q/K L2 normalization: every row gets unit Euclidean
+    """dev15a, the L2 norm of each Q and K head: every row gets unit Euclidean
     norm (within 1e-6) and keeps its direction (numpy.linalg.norm in f64);
     an all-zero row stays zero instead of turning into NaN."""
     rng = np.random.default_rng(17)
