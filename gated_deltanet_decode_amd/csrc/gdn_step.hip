@@ -135,6 +135,84 @@ __global__ __launch_bounds__(W * 64) void k_step(StepArgs a, int n_tiles, int ep
     } while (w.next());
 }
 
+
+// Large launches: staged tiles.  A workgroup of 8 waves takes two
+// consecutive tiles of one head per pass.  Every thread streams one float4
+// of the pair into LDS with a nontemporal load, so each load instruction of
+// a wave covers 1 KiB of contiguous state (four waves per tile); after a
+// barrier, waves 0 and 4 read their tile back from LDS in the row layout,
+// run k_step's arithmetic on it and store the rows straight from registers.
+// Same per-row arithmetic, so the same bits.  Measured on MI355X against
+// the persistent walk (the same pattern with each wave loading its own tile
+// row by row): 5.90-5.92 against 6.19-6.21 ms for the B = 256 x 36-layer
+// step, 5.84-5.89 against 6.12 ms for those layers as one B = 9216 call,
+// 3-4 % faster from B = 32 to 512.  An in-place probe shows why: one
+// float4 per thread in 1 KiB-contiguous instructions reads and writes
+// 6.56-6.66 TB/s where the walk's pattern reaches 6.29-6.37.  Measured and
+// not taken: one tile per 256-thread workgroup (1.5 % slower on the 36
+// layers), 4 or 8 tiles per workgroup, one or two waves per tile (slower),
+// every wave computing a share of the rows (up to 50 % slower), the stores
+// also staged through LDS behind a second barrier (6.6-6.7 ms), workgroups
+// remapped so that one XCD takes a contiguous share of the tiles (2 %
+// slower), and a grid-stride loop over tile pairs inside the kernel (its
+// live values took 68 VGPRs instead of 56: three workgroups per CU instead
+// of four, 25 % slower).  A launch with more tile pairs than one dispatch
+// holds (states beyond 64 GiB) is split into several launches.
+constexpr int kStagedThreads = 512;
+constexpr int kStagedTiles = 2;
+constexpr int kF4PerTile = kRowsPerTile * D / 4;   // 256
+static_assert(kStagedThreads == kStagedTiles * kF4PerTile, "one float4 per thread");
+
+template <bool NT>
+__global__ __launch_bounds__(kStagedThreads) void k_step_staged(StepArgs a, int pair0) {
+    constexpr int kWavesPerTile = kF4PerTile / 64;   // 4
+    __shared__ f4 tile[kStagedTiles][kF4PerTile];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = lane >> 3;
+    const int c = lane & 7;
+    const int mine = wave / kWavesPerTile;           // the tile of the pair this wave streams
+    const int p = (wave % kWavesPerTile) * 64 + lane;   // this lane's float4 in it
+    const bool computes = wave % kWavesPerTile == 0;    // waves 0 and 4 compute tile `mine`
+    const int t = (pair0 + static_cast<int>(blockIdx.x)) * kStagedTiles + mine;
+    const int head = t / kTilesPerHead;
+    const int row0 = (t % kTilesPerHead) * kRowsPerTile;
+    float *Mt = a.state + static_cast<int64_t>(head) * (D * D) + row0 * D;
+    const f4 *src = reinterpret_cast<const f4 *>(Mt) + p;
+    if constexpr (NT)
+        tile[mine][p] = __builtin_nontemporal_load(src);
+    else
+        tile[mine][p] = *src;
+    // The computing waves fetch their vectors only now: the barrier below
+    // then waits for the tile alone, the six other waves leave as soon as it
+    // is in LDS, and the vector loads complete while the next workgroup
+    // starts (fetching them before the LDS write measured 4 % slower).
+    VecSlice kv, qv;
+    float gt = 0.0f, bt = 0.0f, vj = 0.0f;
+    if (computes) {
+        const int b = head / a.Hv;
+        const int h = head - b * a.Hv;
+        int kh = h;
+        while (kh >= a.Hk) kh -= a.Hk;                      // key-head broadcast
+        load_vec(kv, a.k + b * a.qk_bstride + kh * D, c);
+        load_vec(qv, a.q + b * a.qk_bstride + kh * D, c);
+        gt = a.gate[head];
+        bt = a.beta[head];
+        vj = a.v[b * a.v_bstride + h * D + row0 + grp];
+    }
+    __syncthreads();                 // every wave: its share of the tiles is in LDS
+    if (!computes) return;
+    RowSlice r;
+#pragma unroll
+    for (int i = 0; i < kF4PerLane; ++i) r.m[i] = tile[mine][grp * (D / 4) + kLanesPerRow * i + c];
+    const float e = expf(gt);
+    const float sk = group_sum(head_part(r, kv, e));         // decay, key product
+    update_part(r, (vj - sk) * bt, kv);                       // correction, rank-1
+    store_row<NT>(Mt + grp * D, r, c);
+    const float o = group_sum(dot_part(r, qv)) * kInvSqrtD;   // read-out
+    if (c == 0) a.out[static_cast<int64_t>(head) * D + row0 + grp] = o;
+}
+
 // --------------------------------------------------- gdn_step, cached state
 // gdn_step_ex with GDN_STATE_CACHED: the caller's states stay resident in
 // the Infinity Cache across calls, so the state goes through the caches and
@@ -273,6 +351,7 @@ constexpr int64_t kMaxEpochWgs = int64_t(1) << 22;
 
 constexpr int kCachedTilesPerWave = 8;
 constexpr int kCachedWaves = 4;
+constexpr int64_t kMaxStagedWgs = int64_t(1) << 22;
 
 template <bool NT>
 hipError_t launch_step_policy(const StepArgs &a, hipStream_t s) {
@@ -283,7 +362,7 @@ hipError_t launch_step_policy(const StepArgs &a, hipStream_t s) {
         return hipGetLastError();
     }
     // (a launch past 2^32 work-items, a state far beyond any GPU's memory,
-    // falls back to the walk)
+    // falls back to the staged kernel with cached access)
     constexpr int64_t per_wg = kCachedTilesPerWave * kCachedWaves;
     if (!NT && (tiles + per_wg - 1) / per_wg * kCachedWaves * 64 <= INT64_C(0xffffffff)) {
         k_step_cached<kCachedTilesPerWave, kCachedWaves>
@@ -291,26 +370,16 @@ hipError_t launch_step_policy(const StepArgs &a, hipStream_t s) {
                0, s>>>(a, nt);
         return hipGetLastError();
     }
-    int64_t full = device_cus() * static_cast<int64_t>(GDN_STEP_WGS_PER_CU);
-    if (full > kMaxGrid) full = kMaxGrid;
-    const int64_t need = (tiles + kStepWaves - 1) / kStepWaves;
-    const int grid = static_cast<int>(need < full ? need : full);
-    const int64_t passes = (tiles + static_cast<int64_t>(grid) * kStepWaves - 1) /
-                           (static_cast<int64_t>(grid) * kStepWaves);
-    const int64_t span = static_cast<int64_t>(grid) * kStepWaves * kEpochIters;
-    const int64_t epochs = (tiles + span - 1) / span;
-    if (passes > kPersistentIters && grid * epochs <= kMaxEpochWgs) {
-        k_step<true, kStepWaves, NT><<<dim3(static_cast<unsigned>(grid * epochs)),
-                                       dim3(kStepWaves * 64), kEpochLdsBytes, s>>>(
-            a, nt, grid, kEpochIters);
-    } else if (passes > 1) {
-        k_step<true, kStepWaves, NT><<<dim3(grid), dim3(kStepWaves * 64), 0, s>>>(
-            a, nt, grid, static_cast<int>(passes));
-    } else {
-        k_step<false, kStepWaves, NT><<<dim3(grid), dim3(kStepWaves * 64), 0, s>>>(a, nt, grid,
-                                                                                    1);
+    // tiles = B * Hv * 16 is even; each launch stays under 2^31 work-items
+    const int64_t pairs = tiles / kStagedTiles;
+    for (int64_t p0 = 0; p0 < pairs; p0 += kMaxStagedWgs) {
+        const int64_t wgs = pairs - p0 < kMaxStagedWgs ? pairs - p0 : kMaxStagedWgs;
+        k_step_staged<NT><<<dim3(static_cast<unsigned>(wgs)), dim3(kStagedThreads), 0, s>>>(
+            a, static_cast<int>(p0));
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 hipError_t launch_step(const StepArgs &a, hipStream_t s, bool cached) {
