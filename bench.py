@@ -110,19 +110,19 @@ def measured_traffic():
     return t.get("traffic_bytes_per_launch")
 
 
-def inplace_probe(torch, stream, buf, reps=5):
-    """Rate of an in-place read-modify-write of `buf` with the step kernel's
-    memory pattern and no arithmetic (read + write bytes / s); the data is
-    left unchanged."""
+def inplace_probe(torch, stream, buf, reps=5, staged=True):
+    """Rate of an in-place read-modify-write of `buf` with no arithmetic
+    (read + write bytes / s; the data is left unchanged): with the staged
+    step kernel's memory pattern, or with the tile walk's (staged=False)."""
     import ctypes
     from gated_deltanet_decode_amd._build import PROBE_LIBRARY
     lib = ctypes.CDLL(PROBE_LIBRARY)
-    lib.gdn_probe_inplace.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint,
-                                      ctypes.c_void_p]
+    fn = lib.gdn_probe_inplace_staged if staged else lib.gdn_probe_inplace
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint, ctypes.c_void_p]
     nbytes = buf.numel() * buf.element_size()
 
     def once():
-        assert lib.gdn_probe_inplace(buf.data_ptr(), nbytes, 0, stream.cuda_stream) == 0
+        assert fn(buf.data_ptr(), nbytes, 0, stream.cuda_stream) == 0
     once()
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -137,8 +137,8 @@ def inplace_probe(torch, stream, buf, reps=5):
 
 def one_direction_probes(torch, stream, buf, reps=5):
     """Rates (bytes / s) of reading `buf` only and of writing a buffer of the
-    same size only, with the in-place probe's walk and accesses: what each
-    direction reaches alone, against the in-place probe's mix of both."""
+    same size only, with the tile walk's accesses: what each direction
+    reaches alone, against the walk's in-place mix of both."""
     import ctypes
     from gated_deltanet_decode_amd._build import PROBE_LIBRARY
     lib = ctypes.CDLL(PROBE_LIBRARY)
@@ -226,7 +226,7 @@ def fma_probe(torch, stream, workgroups, threads, iters=20000, reps=3):
 
 def copy_probe(torch, stream, nbytes=1 << 30, reps=5, tuned=True):
     """Bandwidth of a device-to-device copy (read + write bytes / s): tuned
-    (the step kernel's nontemporal persistent walk, src != dst) or a plain
+    (the tile walk with nontemporal 16-byte accesses, src != dst) or a plain
     grid-stride copy."""
     import ctypes
     from gated_deltanet_decode_amd._build import PROBE_LIBRARY
@@ -718,7 +718,9 @@ def main():
     w = setup_step_b256_x36(torch, g)
     L, B = w["L"], w["B"]
     inplace_gbps = inplace_probe(torch, stream, w["states"][0])
-    log(f"[bench] in-place probe (the step's access pattern, no arithmetic): {inplace_gbps:.0f} GB/s")
+    walk_gbps = inplace_probe(torch, stream, w["states"][0], staged=False)
+    log(f"[bench] in-place probes (no arithmetic): the step's staged pattern {inplace_gbps:.0f} "
+        f"GB/s, the tile walk {walk_gbps:.0f} GB/s")
     read_gbps, write_gbps = one_direction_probes(torch, stream, w["states"][0])
     log(f"[bench] the same walk one way: read only {read_gbps:.0f} GB/s, write only "
         f"{write_gbps:.0f} GB/s")
@@ -781,7 +783,7 @@ def main():
                    "global_batch": B, "layers": L, "launches_per_step": L,
                    "seed": gi.WORKLOADS["step_b256_x36"]["seed"]},
         "achieved_GBps_step": updates_per_step * STATE_UPDATE_BYTES / (ms_per_step / 1e3) / 1e9,
-        "roofline": {"bound": "hbm", "kernel": "k_step (gdn_step)", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": "k_step_staged (gdn_step)", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(),
                      "bytes_per_launch": bytes_per_launch,
@@ -792,6 +794,7 @@ def main():
                      "plain_copy_probe_GBps": plain_copy_gbps,
                      "inplace_probe_GBps": inplace_gbps,
                      "frac_of_inplace_probe": achieved / inplace_gbps,
+                     "walk_inplace_probe_GBps": walk_gbps,
                      "read_only_probe_GBps": read_gbps,
                      "write_only_probe_GBps": write_gbps,
                      "event_bracketed_launch_us": float(np.mean(launch_ms)) * 1e3,

@@ -3,12 +3,13 @@
 //    report the copy bandwidth this GPU sustains, and hardware-counter runs
 //    use its known byte count to calibrate the FETCH_SIZE / WRITE_SIZE
 //    counters;
-//  - an in-place read-modify-write with the state step's memory pattern and
-//    none of its arithmetic: the rate the step's access pattern alone
-//    reaches, the practical ceiling for the step kernel;
-//  - the same walk copying between two buffers: a copy tuned as the step
-//    kernel is (nontemporal 16-byte accesses, persistent XCD-aware walk);
-//  - the same walk reading only or writing only;
+//  - an in-place read-modify-write with the staged step kernel's memory
+//    pattern and none of its arithmetic: the rate the step's access pattern
+//    alone reaches, the practical ceiling for the step kernel;
+//  - an in-place read-modify-write with a persistent XCD-aware tile walk
+//    (each wave loading and storing its own tile row by row, nontemporal
+//    16-byte accesses), the pattern of the pair kernel; the same walk
+//    copying between two buffers, reading only, or writing only;
 //  - a stream of independent non-packed FP32 FMAs with no memory traffic:
 //    the issue rate the VALU sustains at a given number of waves per CU, the
 //    practical ceiling for the multi-token kernel;
@@ -30,11 +31,11 @@ __global__ __launch_bounds__(256) void k_copy_probe(const f4 *__restrict__ src,
         dst[i] = src[i];
 }
 
-// The gdn_step kernel's memory pattern without its arithmetic: a persistent
-// grid of one 8-wave workgroup per CU walks 4 KiB tiles (8 rows of 512 B) in
-// grid-stride order; in a tile, lane c of row group g reads the float4 chunks
-// 8*i + c (i = 0..3) of row g with nontemporal loads, flips the bits in `key`
-// (0: data unchanged) and writes them back with nontemporal stores.
+// The tile walk: a persistent grid of one 8-wave workgroup per CU walks
+// 4 KiB tiles (8 rows of 512 B) in grid-stride order; in a tile, lane c of
+// row group g reads the float4 chunks 8*i + c (i = 0..3) of row g with
+// nontemporal loads, flips the bits in `key` (0: data unchanged) and writes
+// them back with nontemporal stores.
 typedef unsigned int u4 __attribute__((ext_vector_type(4)));
 constexpr int kProbeWaves = 8;
 
@@ -62,6 +63,31 @@ __global__ __launch_bounds__(W * 64) void k_inplace_probe(const f4 *src, f4 *dst
             const u4 b = __builtin_bit_cast(u4, v[i]) ^ key;
             __builtin_nontemporal_store(__builtin_bit_cast(f4, b), dst + row + 8 * i + c);
         }
+    }
+}
+
+// The staged step kernel's memory pattern without its arithmetic: a
+// workgroup of 8 waves takes two consecutive tiles; every thread loads one
+// float4 (nontemporal, 1 KiB contiguous per wave instruction) into LDS; after
+// a barrier waves 0 and 4 read their tile back in the row layout (lane c of
+// row group g: float4 chunks 8*i + c of row g), flip the bits in `key` and
+// store the rows with nontemporal stores.
+__global__ __launch_bounds__(512) void k_staged_probe(f4 *buf, unsigned key) {
+    __shared__ f4 tile[2][256];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = lane >> 3;
+    const int c = lane & 7;
+    const int mine = wave / 4;
+    f4 *T = buf + (static_cast<int64_t>(blockIdx.x) * 2 + mine) * 256;
+    tile[mine][(wave % 4) * 64 + lane] = __builtin_nontemporal_load(T + (wave % 4) * 64 + lane);
+    __syncthreads();
+    if (wave % 4 != 0) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = grp * 32 + 8 * i + c;
+        const u4 b = __builtin_bit_cast(u4, tile[mine][q]) ^ key;
+        __builtin_nontemporal_store(__builtin_bit_cast(f4, b), T + q);
     }
 }
 
@@ -228,6 +254,20 @@ int gdn_probe_write(void *buf, size_t bytes, unsigned key, void *stream) {
     (void)hipGetLastError();
     k_write_probe<<<dim3(grid), dim3(kProbeWaves * 64), 0, static_cast<hipStream_t>(stream)>>>(
         static_cast<f4 *>(buf), tiles, key);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// Reads and rewrites `bytes` (a multiple of 8192, at most 2^35, 16-byte
+// aligned device memory) in place with the staged step kernel's pattern,
+// XOR-ing every 32-bit word with `key`.  Returns 0, -1 on bad arguments, -6
+// when the launch fails.
+int gdn_probe_inplace_staged(void *buf, size_t bytes, unsigned key, void *stream) {
+    if (!buf || bytes == 0 || bytes % 8192 != 0 || bytes > (size_t(1) << 35) ||
+        reinterpret_cast<size_t>(buf) % 16 != 0)
+        return -1;
+    (void)hipGetLastError();
+    k_staged_probe<<<dim3(static_cast<unsigned>(bytes / 8192)), dim3(512), 0,
+                     static_cast<hipStream_t>(stream)>>>(static_cast<f4 *>(buf), key);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

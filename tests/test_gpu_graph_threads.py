@@ -85,10 +85,10 @@ def test_graph_capture_step_seq_pair_tail(g):
 def test_graph_capture_large_launch_shapes(g):
     """The launch shapes that only large calls take: gdn_seq with more half
     heads than fit two per CU (the 16-token kernel held to three workgroups
-    per CU, which spills a few registers to scratch) and gdn_step beyond 64
-    passes of the tile walk (epochs, with a dynamic LDS reservation)."""
+    per CU, which spills a few registers to scratch) and gdn_step's staged
+    kernel (two tiles per workgroup through LDS)."""
     import torch
-    print("\n  graph capture: seq B=24 T=20, step B=300 (epochs)", flush=True)
+    print("\n  graph capture: seq B=24 T=20, step B=300 (staged)", flush=True)
     B = 24
     ss = {n: dev(x) for n, x in gi.step_inputs(6004, 0, B, T=20).items()}
     M = dev(gi.state(6004, 0, B))

@@ -48,12 +48,11 @@ def test_step_matches_oracle(g, orc, B, Hv, Hk):
     ref.assert_close("out", og, want, OUT_TOL)
 
 
-def test_step_epoch_launch_matches_oracle(g, orc):
-    # 257 x 33 heads = 135,696 tiles: more than 64 passes of the persistent
-    # grid, so the launch runs as 4-pass epochs; 17 of them, the last one
-    # ragged, with a head count that does not divide the walk's stride.
+def test_step_large_launch_matches_oracle(g, orc):
+    # 257 x 33 heads = 135,696 tiles in 67,848 staged workgroups of two
+    # tiles, with head counts (33 value, 11 key) that are not powers of two.
     B, Hv, Hk = 257, 33, 11
-    print(f"\n  gdn_step epoch launch B={B} Hv={Hv} Hk={Hk}", flush=True)
+    print(f"\n  gdn_step large launch B={B} Hv={Hv} Hk={Hk}", flush=True)
     si = gi.step_inputs(2600, Hv, B, Hv, Hk)
     M = gi.state(2600, Hv, B, Hv)
     Mg, og = run_step(g, si, M)
@@ -199,8 +198,8 @@ def test_nan_stays_in_its_row(g):
 
 # B = 1: one wave per tile (both policies); 64: the Infinity-Cache resident
 # decode (cached: 8 tiles per wave, 4 waves per workgroup; default: the
-# persistent walk); 17 x 33 heads: the last cached workgroup half empty;
-# 300 x 33 heads: the default launch runs as 4-pass epochs
+# staged kernel); 17 x 33 heads: the last cached workgroup half empty;
+# 300 x 33 heads: a large staged launch
 @pytest.mark.parametrize("B,Hv,Hk", [(1, 32, 16), (64, 32, 16), (17, 33, 11), (300, 33, 11)])
 def test_step_cached_policy_is_bitwise(g, orc, B, Hv, Hk):
     """gdn_step_ex with GDN_STATE_CACHED (state through the caches) gives the

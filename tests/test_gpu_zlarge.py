@@ -1,8 +1,8 @@
 """GPU: every kernel on a state past 2^31 floats (8 GiB), the size at which a
 32-bit element offset would wrap.  B = 4104 sequences of 32 value heads are
 131,328 heads of 16,384 floats, so the heads of the last 8 sequences start
-beyond float index 2^31.  (k_step at this size is covered by the flattened
-B = 9216 call of the full-size tests.)
+beyond float index 2^31; and gdn_step at B = 16400, whose 34 GB of state
+take two launches of the staged kernel.
 
 Inputs and states of G = 8 seeded sequences are tiled over the batch on the
 GPU: sequence b gets the inputs and starting state of sequence b % 8.  Each
@@ -57,22 +57,22 @@ def first(t):
     return t[:G].cpu().numpy()
 
 
-def assert_groups_bitwise(name, t):
-    """Every group of G sequences of t ([B][...]) equals the first group bit
-    for bit (compared as 32-bit patterns)."""
+def assert_groups_bitwise(name, t, ng=NG):
+    """Every group of G sequences of t ([ng * G][...]) equals the first group
+    bit for bit (compared as 32-bit patterns)."""
     import torch
-    rows = t.reshape(NG, -1).view(torch.int32)
+    rows = t.reshape(ng, -1).view(torch.int32)
     bad = 0
-    for s in range(1, NG, 32):
+    for s in range(1, ng, 32):
         bad += int((rows[s:s + 32] != rows[0]).any(dim=1).sum())
-    ref.record(name=f"{name}: {NG} groups bitwise", mismatched_groups=bad, passed=bad == 0)
-    print(f"    {name:>14s}: {NG} groups of {G} bitwise equal: {bad == 0}", flush=True)
-    assert bad == 0, f"{name}: {bad} of {NG - 1} groups differ from the first"
+    ref.record(name=f"{name}: {ng} groups bitwise", mismatched_groups=bad, passed=bad == 0)
+    print(f"    {name:>14s}: {ng} groups of {G} bitwise equal: {bad == 0}", flush=True)
+    assert bad == 0, f"{name}: {bad} of {ng - 1} groups differ from the first"
 
 
 def test_step_cached_past_2_31(g, orc):
     """gdn_step_ex with GDN_STATE_CACHED (the one-shot kernel) and the default
-    walk over the same 8.6 GB state."""
+    staged kernel over the same 8.6 GB state."""
     import torch
     print(f"\n  gdn_step_ex cached / gdn_step B={B}", flush=True)
     si = gi.step_inputs(7101, 0, G)
@@ -91,6 +91,31 @@ def test_step_cached_past_2_31(g, orc):
         ref.assert_close(f"{tag} state", first(Md), M, 1e-6)
         ref.assert_close(f"{tag} out", first(o), want, 1e-5)
         del Md
+
+
+def test_step_split_launch_past_32_gib(g, orc):
+    """gdn_step at B = 16400 (34 GB of state): the staged kernel covers 2^22
+    tile pairs (32 GiB) per launch, so this call takes two launches and its
+    last 16 sequences come from the second one."""
+    import torch
+    Bs = 16400
+    ng = Bs // G
+    assert Bs * 32 * 16 // 2 > 1 << 22
+    print(f"\n  gdn_step B={Bs} (two staged launches)", flush=True)
+    si = gi.step_inputs(7102, 0, G)
+    M0 = gi.state(7102, 0, G)
+    t = {n: dev(x).repeat((ng,) + (1,) * (x.ndim - 1)) for n, x in si.items()}
+    Md = dev(M0).repeat(ng, 1, 1, 1)
+    o = torch.empty((Bs, 32, 128), device="cuda")
+    g.step(t["q"], t["k"], t["v"], t["beta"], t["gate"], Md, o)
+    torch.cuda.synchronize()
+    assert_groups_bitwise("state", Md, ng)
+    assert_groups_bitwise("out", o, ng)
+    M = M0.copy()
+    want = orc.step_M(si["q"], si["k"], si["v"], si["beta"], si["gate"], M)
+    ref.assert_close("state", first(Md), M, 1e-6)
+    ref.assert_close("out", first(o), want, 1e-5)
+    del Md
 
 
 @pytest.mark.parametrize("T,exact", [(3, False), (20, False), (20, True), (65, False)])
