@@ -57,7 +57,8 @@ __global__ __launch_bounds__(64) void k_step_tile(StepArgs a) {
 // of the pair into LDS with a nontemporal load, so each load instruction of
 // a wave covers 1 KiB of contiguous state (four waves per tile); after a
 // barrier, waves 0 and 4 read their tile back from LDS in the row layout,
-// run k_step's arithmetic on it and store the rows straight from registers.
+// run the step's row arithmetic on it (that of k_step_tile) and store the
+// rows straight from registers.
 // Same per-row arithmetic, so the same bits.  Measured on MI355X against
 // the persistent walk (the same pattern with each wave loading its own tile
 // row by row): 5.90-5.92 against 6.19-6.21 ms for the B = 256 x 36-layer
@@ -68,7 +69,8 @@ __global__ __launch_bounds__(64) void k_step_tile(StepArgs a) {
 // not taken: one tile per 256-thread workgroup (1.5 % slower on the 36
 // layers), 4 or 8 tiles per workgroup, one or two waves per tile (slower),
 // every wave computing a share of the rows (up to 50 % slower), the stores
-// also staged through LDS behind a second barrier (6.6-6.7 ms), workgroups
+// also staged through LDS behind a second barrier (6.6-6.7 ms) or by the
+// computing wave alone (5.98 against 5.90 ms), workgroups
 // remapped so that one XCD takes a contiguous share of the tiles (2 %
 // slower), and a grid-stride loop over tile pairs inside the kernel (its
 // live values took 68 VGPRs instead of 56: three workgroups per CU instead
@@ -136,7 +138,8 @@ __global__ __launch_bounds__(kStagedThreads) void k_step_staged(StepArgs a, int 
 // Each wave takes TPW consecutive tiles of one head (every head's 16 tiles
 // split over 16 / TPW waves), issues all their state loads at once, reads
 // the head's k, q, beta and gate once, and then updates and stores its tiles
-// one after the other.  Same per-row arithmetic as k_step, so the same bits.
+// one after the other.  Same per-row arithmetic as k_step_tile and
+// k_step_staged, so the same bits.
 // Measured on MI355X, 100 calls with fresh inputs per call: B = 64 (a
 // 128 MiB state) 4.15 ms against 4.48 ms for the nontemporal walk and
 // 4.95 ms for the walk with cached state access; B = 32 2.04 against

@@ -136,7 +136,7 @@ __global__ __launch_bounds__(kGateThreads) void k_gate_transform(GateArgs a) {
 // slower.
 //
 // Every reduction keeps the order of the three-launch path (k_prestate,
-// k_step, k_gated_norm), so both paths give the same bits, and position 2
+// gdn_step's kernel, k_gated_norm), so both paths give the same bits, and position 2
 // of a pair gives the bits of a one-position call on the ring and state
 // that position 1 committed.  With kRaw the lanes also make their heads'
 // beta and gate from the raw gate inputs with beta_gate(), as
