@@ -53,7 +53,7 @@ __global__ __launch_bounds__(64) void k_step_tile(StepArgs a) {
 }
 
 // Large launches: staged tiles.  A workgroup of 8 waves takes two
-// consecutive tiles of one head per pass.  Every thread streams one float4
+// consecutive tiles of one head.  Every thread streams one float4
 // of the pair into LDS with a nontemporal load, so each load instruction of
 // a wave covers 1 KiB of contiguous state (four waves per tile); after a
 // barrier, waves 0 and 4 read their tile back from LDS in the row layout,
@@ -75,7 +75,8 @@ __global__ __launch_bounds__(64) void k_step_tile(StepArgs a) {
 // slower), and a grid-stride loop over tile pairs inside the kernel (its
 // live values took 68 VGPRs instead of 56: three workgroups per CU instead
 // of four, 25 % slower).  A launch with more tile pairs than one dispatch
-// holds (states beyond 64 GiB) is split into several launches.
+// holds (2^22 workgroups: states beyond 32 GiB) is split into several
+// launches.
 constexpr int kStagedThreads = 512;
 constexpr int kStagedTiles = 2;
 constexpr int kF4PerTile = kRowsPerTile * D / 4;   // 256
