@@ -2,8 +2,9 @@
 // four HIP runtime calls that gdn_api.cpp makes, so that the C-ABI layer can
 // be built with g++ under AddressSanitizer and UndefinedBehaviorSanitizer and
 // driven on a machine without a GPU (tests/c/gdn_api_check.c).  Every launch
-// is recorded instead of enqueued; the driver reads the records back to check
-// what the ABI layer passed on.  Test infrastructure, never part of libgdn.
+// is recorded instead of enqueued; the check program reads the records back
+// to check what the ABI layer passed on.  Test infrastructure, never part of
+// libgdn.
 
 #include <hip/hip_runtime_api.h>
 

@@ -36,7 +36,8 @@ def pytest_configure(config):
 
 def pytest_sessionfinish(session, exitstatus):
     """After a GPU session, write the parity records (one JSON object per
-    compared quantity) to gpurun_out/parity_records.jsonl."""
+    compared quantity) to parity_records.jsonl in the output folder that the
+    GPU runs return."""
     import json
     ref = sys.modules.get("ref")
     if ref is None or not ref.RECORDS:
