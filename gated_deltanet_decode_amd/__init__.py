@@ -128,7 +128,27 @@ def _check(rc: int) -> None:
         raise GdnError(rc, last_error())
 
 
+try:
+    import torch as _torch
+    _F32 = _torch.float32
+except ImportError:       # the checks below then raise the import error
+    _F32 = None
+
+
 def _ptr(t, name, shape=None, optional=False):
+    """Device address of a contiguous float32 GPU tensor of the given shape.
+    The common case is tested in one expression; anything else goes through
+    the checks one by one, which name what is wrong."""
+    try:
+        if (t.dtype is _F32 and t.is_cuda and t.is_contiguous()
+                and (shape is None or t.shape == shape)):
+            return t.data_ptr()
+    except AttributeError:
+        pass
+    return _ptr_checked(t, name, shape, optional)
+
+
+def _ptr_checked(t, name, shape, optional):
     import torch
     if t is None:
         if optional:
