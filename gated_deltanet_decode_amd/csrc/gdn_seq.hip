@@ -1,6 +1,8 @@
 // gdn_seq.hip - gdn_seq: the multi-token kernel with the state resident in
 // registers.
 
+#include <cstddef>
+
 #include "gdn_device.hpp"
 
 namespace gdn {
@@ -20,7 +22,8 @@ namespace {
 // double-buffered (97 KiB of LDS for CH = 32; gfx950 allows 160 KiB per
 // workgroup): the global loads of chunk c+1 are issued before chunk c is
 // computed and written to LDS after it, so their latency hides behind CH
-// tokens of arithmetic.  Outputs overwrite the consumed v entries in LDS (row
+// tokens of arithmetic.  With DMA, k, q and v go from global memory straight
+// into LDS (global_load_lds_dwordx4) and hold no registers meanwhile.  Outputs overwrite the consumed v entries in LDS (row
 // j's v is read only by row j's lanes, before its output exists) and are
 // flushed to HBM with coalesced 16-byte stores once per chunk.  Two barriers
 // per chunk; none per token.
@@ -62,21 +65,50 @@ struct Chunk {
     static_assert(2 * CH <= NTH, "one thread per gate and per beta");
 };
 
-template <int CH, int NTH>
+template <int CH, int NTH, bool DMA>
 struct ChunkRegs {
-    f4 f[Chunk<CH, NTH>::kFetchPer];   // k slots, then q, then v
+    f4 f[DMA ? 1 : Chunk<CH, NTH>::kFetchPer];   // k slots, then q, then v (unused with DMA)
     float s;    // gate or beta of one token (threads 0 .. 2*CH-1); with the
     float s2;   // scaled decay, thread t < CH holds token t's gate and beta
 };
+
+// Global-to-LDS load of 16 bytes per lane (global_load_lds_dwordx4): lane l's
+// bytes land at dst + 16 l.  dst must be the same in every lane of the wave;
+// the data is in LDS once the wave's vector-memory counter has drained.
+__device__ __forceinline__ void load_lds16(const float *src, float *dst) {
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)(src),
+                                     (__attribute__((address_space(3))) void *)(dst), 16, 0, 0);
+}
 
 // kClamp: the chunk may run past token T - 1 (only a sequence's last chunk
 // can); slots past the end load token T - 1 again, which nothing reads (a
 // partial chunk computes, flushes and takes the next key of its first nt
 // tokens only).  Every load is unconditional and in bounds.
-template <int CH, int NTH, bool kClamp, bool SC>
-__device__ __forceinline__ void seq_fetch(ChunkRegs<CH, NTH> &cr, const SeqArgs &a, int64_t b, int h,
-                                          int kh, int t0, int tid) {
+// DMA: token tt of the chunk is fetched by wave tt % NW straight into its
+// LDS slot (buf): k and q, adjacent there, with one instruction (lanes 0-31
+// k, 32-63 q: 1 KiB), v with a second one on lanes 0-31 (512 B).
+template <int CH, int NTH, bool kClamp, bool SC, bool DMA>
+__device__ __forceinline__ void seq_fetch(ChunkRegs<CH, NTH, DMA> &cr, TokenLds *buf, const SeqArgs &a,
+                                          int64_t b, int h, int kh, int t0, int tid) {
     using C = Chunk<CH, NTH>;
+    if constexpr (DMA) {
+        constexpr int NW = NTH / 64;
+        static_assert(CH % NW == 0, "whole tokens per wave");
+        static_assert(offsetof(TokenLds, q) == offsetof(TokenLds, k) + D * sizeof(float),
+                      "k and q adjacent: one 1 KiB transfer");
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const bool lo = lane < 32;
+        const int c4 = 4 * (lane & 31);
+#pragma unroll
+        for (int n = 0; n < CH / NW; ++n) {
+            const int tt = wave + n * NW;
+            const int t = kClamp ? min(t0 + tt, a.T - 1) : t0 + tt;
+            const int64_t bt = b * a.T + t;
+            load_lds16((lo ? a.k : a.q) + (bt * a.Hk + kh) * D + c4, buf[tt].k);
+            if (lo) load_lds16(a.v + (bt * a.Hv + h) * D + c4, buf[tt].v);
+        }
+    }
     const int col = 4 * (tid & 31);
     const int t = t0 + (tid >> 5);                      // token of slot 0
     const int64_t bt = b * a.T + t;
@@ -85,7 +117,7 @@ __device__ __forceinline__ void seq_fetch(ChunkRegs<CH, NTH> &cr, const SeqArgs 
     const int64_t ktok = static_cast<int64_t>(a.Hk) * D;   // one token apart
     const int64_t vtok = static_cast<int64_t>(a.Hv) * D;
 #pragma unroll
-    for (int n = 0; n < C::kSlots; ++n) {
+    for (int n = 0; n < (DMA ? 0 : C::kSlots); ++n) {
         const int dt = kClamp ? min(t + n * C::kTokStride, a.T - 1) - t : n * C::kTokStride;
         cr.f[n] = *reinterpret_cast<const f4 *>(a.k + koff + dt * ktok);
         cr.f[C::kSlots + n] = *reinterpret_cast<const f4 *>(a.q + koff + dt * ktok);
@@ -108,15 +140,15 @@ __device__ __forceinline__ void seq_fetch(ChunkRegs<CH, NTH> &cr, const SeqArgs 
     }
 }
 
-template <int CH, int NTH, bool SC>
-__device__ __forceinline__ void fetch_chunk(ChunkRegs<CH, NTH> &cr, const SeqArgs &a, int64_t b, int h,
-                                            int kh, int t0, int tid) {
+template <int CH, int NTH, bool SC, bool DMA>
+__device__ __forceinline__ void fetch_chunk(ChunkRegs<CH, NTH, DMA> &cr, TokenLds *buf, const SeqArgs &a,
+                                            int64_t b, int h, int kh, int t0, int tid) {
     // 8-token chunks (sequences under 16 tokens) always clamp: one code path
     // measured 1-3 % faster at T = 3..6.
     if (CH > 8 && t0 + CH <= a.T)
-        seq_fetch<CH, NTH, false, SC>(cr, a, b, h, kh, t0, tid);
+        seq_fetch<CH, NTH, false, SC, DMA>(cr, buf, a, b, h, kh, t0, tid);
     else
-        seq_fetch<CH, NTH, true, SC>(cr, a, b, h, kh, t0, tid);
+        seq_fetch<CH, NTH, true, SC, DMA>(cr, buf, a, b, h, kh, t0, tid);
 }
 
 // Scaled decay.  The decay multiplies every state element by the same
@@ -139,6 +171,8 @@ __device__ __forceinline__ void fetch_chunk(ChunkRegs<CH, NTH> &cr, const SeqArg
 // group's rounding differs from the per-token multiply, so its results are
 // not bitwise those of gdn_step.
 constexpr int kScaleGroup = 16;
+// s_waitcnt operand (gfx9 encoding) that waits for vmcnt = 0 only.
+constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr float kMinScale = 0x1p-63f;
 
 // DPP move that keeps `old` in lanes without a source (row shifts).
@@ -153,17 +187,17 @@ __device__ __forceinline__ float lane_value(float x, int lane) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
 
-// Stages a fetched chunk into LDS.  With SC, info[2 g] says whether group g
-// of the chunk may run scaled (1 or 0) and info[2 g + 1] is its decay
-// product.
-template <int CH, int NTH, bool SC>
-__device__ __forceinline__ void seq_stage(TokenLds *buf, float *info, const ChunkRegs<CH, NTH> &cr,
+// Stages a fetched chunk into LDS (with DMA, its per-token scalars only).
+// With SC, info[2 g] says whether group g of the chunk may run scaled (1 or
+// 0) and info[2 g + 1] is its decay product.
+template <int CH, int NTH, bool SC, bool DMA>
+__device__ __forceinline__ void seq_stage(TokenLds *buf, float *info, const ChunkRegs<CH, NTH, DMA> &cr,
                                           int tid) {
     using C = Chunk<CH, NTH>;
     const int col = 4 * (tid & 31);
     TokenLds *tok = buf + (tid >> 5);
 #pragma unroll
-    for (int n = 0; n < C::kSlots; ++n) {
+    for (int n = 0; n < (DMA ? 0 : C::kSlots); ++n) {
         TokenLds &tk = tok[n * C::kTokStride];
         *reinterpret_cast<f4 *>(tk.k + col) = cr.f[n];
         *reinterpret_cast<f4 *>(tk.q + col) = cr.f[C::kSlots + n];
@@ -402,8 +436,8 @@ __device__ __forceinline__ bool group_scaled(const float *info, int gi) {
 // paired row reductions (seq_token); a head's 128 rows are split over PARTS
 // workgroups of 16 / (TPW * PARTS) waves with TPW tiles each; WPS: waves per
 // SIMD the register allocation must allow (3 caps it at 168 VGPRs); SC: the
-// scaled decay.
-template <int CH, bool NT, bool PAIR, int PARTS, int WPS, int TPW = 2, bool SC = false>
+// scaled decay; DMA: chunks go from global memory straight into LDS.
+template <int CH, bool NT, bool PAIR, int PARTS, int WPS, int TPW = 2, bool SC = false, bool DMA = false>
 __global__ __launch_bounds__(64 * 16 / (TPW * PARTS), WPS) void k_seq(SeqArgs a) {
     constexpr int NTH = 64 * 16 / (TPW * PARTS);
     constexpr int R = D / PARTS;                  // rows of this workgroup
@@ -452,15 +486,16 @@ __global__ __launch_bounds__(64 * 16 / (TPW * PARTS), WPS) void k_seq(SeqArgs a)
         }
     }
 
-    ChunkRegs<CH, NTH> cr;
-    fetch_chunk<CH, NTH, SC>(cr, a, b, h, kh, 0, tid);
-    seq_stage<CH, NTH, SC>(lds[0], info[0], cr, tid);
+    ChunkRegs<CH, NTH, DMA> cr;
+    fetch_chunk<CH, NTH, SC, DMA>(cr, lds[0], a, b, h, kh, 0, tid);
+    seq_stage<CH, NTH, SC, DMA>(lds[0], info[0], cr, tid);
+    if constexpr (DMA) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's transfers are in LDS
     __syncthreads();
 
     const int n_chunks = (a.T + CH - 1) / CH;
     for (int ch = 0; ch < n_chunks; ++ch) {
         const bool more = ch + 1 < n_chunks;
-        if (more) fetch_chunk<CH, NTH, SC>(cr, a, b, h, kh, (ch + 1) * CH, tid);
+        if (more) fetch_chunk<CH, NTH, SC, DMA>(cr, lds[(ch + 1) & 1], a, b, h, kh, (ch + 1) * CH, tid);
 
         TokenLds *buf = lds[ch & 1];
         const int t0 = ch * CH;
@@ -524,7 +559,8 @@ __global__ __launch_bounds__(64 * 16 / (TPW * PARTS), WPS) void k_seq(SeqArgs a)
                 *reinterpret_cast<f4 *>(a.out + o) = *reinterpret_cast<const f4 *>(buf[tt].v + col);
             }
         }
-        if (more) seq_stage<CH, NTH, SC>(lds[(ch + 1) & 1], info[(ch + 1) & 1], cr, tid);
+        if (more) seq_stage<CH, NTH, SC, DMA>(lds[(ch + 1) & 1], info[(ch + 1) & 1], cr, tid);
+        if constexpr (DMA) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // chunk ch+1's transfers
         __syncthreads();                 // chunk ch+1 staged; chunk ch flushed
     }
     if constexpr (TPW == 2) {
@@ -557,12 +593,17 @@ __global__ __launch_bounds__(64 * 16 / (TPW * PARTS), WPS) void k_seq(SeqArgs a)
 //   tokens, 16-token chunks from there.  Whole heads are 3-30 % slower here
 //   except at B = 6..8 and T near 64 (up to 4 % faster; not special-cased).
 //   With few heads, paired reductions: fewer instructions, and occupancy
-//   does not matter.  With many, unpaired reductions and registers for three
-//   workgroups per CU: the 8-token kernel needs 168 VGPRs unpaired, 181
-//   paired (two per CU); the 16-token kernel is held to 168 (a few spill).
+//   does not matter.  With many, registers for three workgroups per CU
+//   (168 VGPRs): the 8-token kernel unpaired (164; 180 paired), the
+//   16-token kernel paired with its chunks fetched straight into LDS (DMA:
+//   168 VGPRs, no spill; 194 with the chunk in registers).
 //   Thresholds: T < 16, paired up to `CUs` heads (2-5 % faster at B <= 8,
-//   5-25 % slower from B = 32); T >= 16, paired up to 2 x CUs heads (best
-//   up to B = 16; from B = 24 unpaired is 1-20 % faster).
+//   5-25 % slower from B = 32); T >= 16, DMA and three per CU beyond `CUs`
+//   heads: 5-14 % faster than the unpaired register-staged kernel held to
+//   168 VGPRs (which spilled 28 bytes per lane) from B = 12 to 512, equal
+//   or up to 3 % slower at B <= 8, where two per CU with the chunk in
+//   registers stays.  DMA measured equal or slower for T < 16 and for long
+//   sequences (1.72 against 1.67 ms at B = 8, T = 4096).
 // - Longer sequences: whole heads, one 8-wave workgroup per head, 32-token
 //   chunks, plain state access, paired reductions.  They are VALU-bound, and
 //   half heads would duplicate the staging (40 % slower at B = 8, T = 4096).
@@ -617,10 +658,10 @@ hipError_t launch_seq_as(const SeqArgs &a, hipStream_t s) {
         else
             k_seq<8, true, false, 2, 1><<<split, dim3(256), 0, s>>>(a);
     } else if (a.T <= 64) {
-        if (heads <= 2 * cus)
+        if (heads <= cus)
             k_seq<16, true, true, 2, 1, 2, SC><<<split, dim3(256), 0, s>>>(a);
         else
-            k_seq<16, true, false, 2, 3, 2, SC><<<split, dim3(256), 0, s>>>(a);
+            k_seq<16, true, true, 2, 3, 2, SC, true><<<split, dim3(256), 0, s>>>(a);
     } else if (2 * heads <= cus) {
         k_seq<32, false, true, 2, 1, 2, SC><<<split, dim3(256), 0, s>>>(a);
     } else {
