@@ -43,8 +43,9 @@ def token(si, t):
 # tokens and 16-token chunks from there; otherwise T < 16 (half heads,
 # 8-token chunks, full and partial) paired up to 256 heads (B = 4, 8) and
 # unpaired beyond (B = 12: 384 heads); 16 <= T <= 64 (half heads, 16-token
-# chunks) paired up to 512 heads (B = 8) and unpaired beyond (B = 24: 768
-# heads); beyond 64 tokens, 2 parts per head while they fit the CUs (B = 3)
+# chunks, paired) with the chunk staged through registers up to 256 heads
+# (B = 8) and fetched straight into LDS beyond (B = 12: 384 heads, B = 24:
+# 768); beyond 64 tokens, 2 parts per head while they fit the CUs (B = 3)
 # and whole heads (B = 8).
 @pytest.mark.parametrize("B,T,Hv,Hk", [(1, 1, 32, 16), (2, 5, 32, 16), (2, 8, 32, 16),
                                        (1, 17, 32, 16), (1, 24, 32, 16), (2, 32, 32, 16),
@@ -52,7 +53,7 @@ def token(si, t):
                                        (1, 64, 32, 16), (2, 65, 32, 16), (8, 24, 32, 16),
                                        (12, 9, 32, 16), (24, 20, 32, 16), (1, 70, 32, 16),
                                        (3, 70, 32, 16), (8, 66, 32, 16), (1, 7, 32, 16),
-                                       (4, 5, 32, 16), (8, 40, 32, 16)])
+                                       (4, 5, 32, 16), (8, 40, 32, 16), (12, 33, 32, 16)])
 def test_seq_matches_oracle(g, orc, B, T, Hv, Hk):
     print(f"\n  gdn_seq B={B} T={T} Hv={Hv} Hk={Hk}", flush=True)
     si = gi.step_inputs(3000 + T, 0, B, Hv, Hk, T=T)
@@ -115,7 +116,7 @@ def test_seq_is_bitwise_repeated_step(g, B, T):
 
 
 @pytest.mark.parametrize("B,T", [(2, 24), (2, 32), (2, 37), (2, 65), (24, 20), (1, 70), (3, 70),
-                                 (8, 66), (1, 24), (8, 32), (4, 64), (1, 16)])
+                                 (8, 66), (1, 24), (8, 32), (4, 64), (1, 16), (12, 33)])
 def test_seq_exact_is_bitwise_repeated_step(g, B, T):
     """gdn_seq_exact: T tokens == T gdn_step calls, bit for bit, at any T and
     with ordinary gates (no scaled groups), in every launch shape that takes
