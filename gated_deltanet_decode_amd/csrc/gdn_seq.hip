@@ -599,16 +599,28 @@ __global__ __launch_bounds__(64 * 16 / (TPW * PARTS), WPS) void k_seq(SeqArgs a)
 //   168 VGPRs, no spill; 194 with the chunk in registers).
 //   Thresholds: T < 16, paired up to `CUs` heads (2-5 % faster at B <= 8,
 //   5-25 % slower from B = 32); T >= 16, DMA and three per CU beyond `CUs`
-//   heads: 5-14 % faster than the unpaired register-staged kernel held to
-//   168 VGPRs (which spilled 28 bytes per lane) from B = 12 to 512, equal
-//   or up to 3 % slower at B <= 8, where two per CU with the chunk in
-//   registers stays.  DMA measured equal or slower for T < 16 and for long
-//   sequences (1.72 against 1.67 ms at B = 8, T = 4096).
-// - Longer sequences: whole heads, one 8-wave workgroup per head, 32-token
-//   chunks, plain state access, paired reductions.  They are VALU-bound, and
-//   half heads would duplicate the staging (40 % slower at B = 8, T = 4096).
-//   With fewer heads than CUs, though, whole heads leave CUs idle, and a
-//   head is split while the parts still fit the CUs:
+//   heads (next item), two per CU with the chunk in registers up to `CUs`
+//   heads (the DMA kernel measured equal or up to 3 % slower at B <= 8).
+//   DMA measured equal or slower for T < 16.
+// - 16 tokens or more with more heads than CUs, at any length: the DMA
+//   half-head kernel, three workgroups (12 waves) per CU.  Against the
+//   unpaired register-staged kernel held to 168 VGPRs (28 bytes of spill per
+//   lane) at T <= 64: 5-14 % faster from B = 12 to 512.  Against whole heads
+//   (next item, 8 waves per CU) beyond 64 tokens: 7-10 % faster where both
+//   fill their rounds of workgroups alike (B = 24 T = 512 665 -> 596 us,
+//   B = 40 T = 1024 2083 -> 1916), 20-31 % where whole heads leave most of a
+//   round empty (B = 9 T = 4096 3383 -> 2347 us, B = 12 T = 2048 1643 ->
+//   1192, B = 20 T = 2048 2490 -> 1989).  Whole heads stay where they fill
+//   every round and the half heads do not (heads a multiple of CUs, twice
+//   the heads not of 3 x CUs) beyond 1024 tokens: B = 16 T = 4096 3303
+//   against 3560 us (at T = 1024 the half heads are 3 % ahead there).
+// - Longer sequences with at most `CUs` heads: whole heads, one 8-wave
+//   workgroup per head, 32-token chunks, plain state access, paired
+//   reductions.  They are VALU-bound; half heads at two per CU duplicate the
+//   staging without adding waves (40 % slower at B = 8, T = 4096; 1.72
+//   against 1.67 ms with the DMA kernel).
+//   With fewer heads than CUs, whole heads leave CUs idle, and a head is
+//   split while the parts still fit the CUs:
 //   - B = 1, 2: the one-tile splits above.  A lone wave on its SIMD issues
 //     one instruction per 4 cycles, so halving its rows nearly halves its
 //     instruction stream: 1.74 -> 1.07 ms at B = 1, T = 4096 (1.39 ms with
@@ -629,6 +641,10 @@ static_assert(2 * 256 == kSeqThreadsPerHead && 512 == kSeqThreadsPerHead,
               "the API bounds B * Hv by this launch's work-items per head");
 
 namespace {
+
+// Workgroups of the DMA half-head kernel that fit on a CU: 168 VGPRs (three
+// waves per SIMD) and 49 KiB of LDS.
+constexpr int kDmaWgsPerCu = 3;
 
 // SC: the 16- and 32-token kernels run qualifying groups scaled.
 template <bool SC>
@@ -657,11 +673,11 @@ hipError_t launch_seq_as(const SeqArgs &a, hipStream_t s) {
             k_seq<8, true, true, 2, 1><<<split, dim3(256), 0, s>>>(a);
         else
             k_seq<8, true, false, 2, 1><<<split, dim3(256), 0, s>>>(a);
+    } else if (heads > cus && !(a.T > 1024 && heads % cus == 0 &&
+                                  (2 * heads) % (kDmaWgsPerCu * cus) != 0)) {
+        k_seq<16, true, true, 2, kDmaWgsPerCu, 2, SC, true><<<split, dim3(256), 0, s>>>(a);
     } else if (a.T <= 64) {
-        if (heads <= cus)
-            k_seq<16, true, true, 2, 1, 2, SC><<<split, dim3(256), 0, s>>>(a);
-        else
-            k_seq<16, true, true, 2, 3, 2, SC, true><<<split, dim3(256), 0, s>>>(a);
+        k_seq<16, true, true, 2, 1, 2, SC><<<split, dim3(256), 0, s>>>(a);
     } else if (2 * heads <= cus) {
         k_seq<32, false, true, 2, 1, 2, SC><<<split, dim3(256), 0, s>>>(a);
     } else {

@@ -45,8 +45,8 @@ def token(si, t):
 # unpaired beyond (B = 12: 384 heads); 16 <= T <= 64 (half heads, 16-token
 # chunks, paired) with the chunk staged through registers up to 256 heads
 # (B = 8) and fetched straight into LDS beyond (B = 12: 384 heads, B = 24:
-# 768); beyond 64 tokens, 2 parts per head while they fit the CUs (B = 3)
-# and whole heads (B = 8).
+# 768, at any length); beyond 64 tokens with at most 256 heads, 2 parts per
+# head while they fit the CUs (B = 3) and whole heads (B = 8).
 @pytest.mark.parametrize("B,T,Hv,Hk", [(1, 1, 32, 16), (2, 5, 32, 16), (2, 8, 32, 16),
                                        (1, 17, 32, 16), (1, 24, 32, 16), (2, 32, 32, 16),
                                        (3, 33, 4, 2), (2, 16, 1, 1), (1, 48, 64, 16),
@@ -116,7 +116,7 @@ def test_seq_is_bitwise_repeated_step(g, B, T):
 
 
 @pytest.mark.parametrize("B,T", [(2, 24), (2, 32), (2, 37), (2, 65), (24, 20), (1, 70), (3, 70),
-                                 (8, 66), (1, 24), (8, 32), (4, 64), (1, 16), (12, 33)])
+                                 (8, 66), (1, 24), (8, 32), (4, 64), (1, 16), (12, 33), (12, 70)])
 def test_seq_exact_is_bitwise_repeated_step(g, B, T):
     """gdn_seq_exact: T tokens == T gdn_step calls, bit for bit, at any T and
     with ordinary gates (no scaled groups), in every launch shape that takes
@@ -168,8 +168,11 @@ def mixed_groups(si):
 # sequence 0 of each batch size below runs through a different launch shape
 # (B = 1: 16 one-tile parts, 16-token chunks; B = 2: 8 parts; B = 3: 2 parts,
 # 32-token chunks; B = 8: whole heads, 32-token chunks; T <= 64 with B = 4:
-# paired half heads; B = 24: unpaired half heads, 16-token chunks)
-@pytest.mark.parametrize("T,Bs", [(100, (1, 2, 3, 8)), (64, (1, 2, 4, 24)), (37, (1, 4, 24))])
+# half heads with the chunk in registers; B = 12, 24: half heads with the
+# chunk fetched straight into LDS, 16-token chunks; T = 1040 with B = 16:
+# whole heads, kept beyond 1024 tokens where they fill their rounds)
+@pytest.mark.parametrize("T,Bs", [(100, (1, 2, 3, 8, 12)), (64, (1, 2, 4, 24)), (37, (1, 4, 24)),
+                                  (1040, (1, 12, 16))])
 def test_seq_bits_do_not_depend_on_launch_shape(g, orc, T, Bs):
     """The scaled groups are counted from the call's first token in every
     launch shape, and a fold inside a 32-token chunk (pipelined with the next

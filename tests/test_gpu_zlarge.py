@@ -120,9 +120,9 @@ def test_step_split_launch_past_32_gib(g, orc):
 
 @pytest.mark.parametrize("T,exact", [(3, False), (20, False), (20, True), (65, False)])
 def test_seq_past_2_31(g, orc, T, exact):
-    """The many-heads gdn_seq routes: 8-token chunks (T < 16), the capped
-    half-head kernel (16 <= T <= 64, scaled and exact) and whole heads with
-    32-token chunks (T > 64)."""
+    """The many-heads gdn_seq routes: 8-token chunks (T < 16) and the
+    half-head kernel with its chunks fetched straight into LDS (16-token
+    chunks; T = 20 scaled and exact, T = 65 with a partial last chunk)."""
     import torch
     print(f"\n  gdn_seq{'_exact' if exact else ''} B={B} T={T}", flush=True)
     si = gi.step_inputs(7200 + T, 0, G, T=T)
