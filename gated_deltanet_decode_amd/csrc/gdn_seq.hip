@@ -10,7 +10,7 @@ namespace {
 
 // -------------------------------------------------------------- gdn_seq
 // One workgroup per (sequence, value head), or per half head for short
-// sequences, of waves holding 2 tiles each: the head's state lives in VGPRs
+// sequences and for more heads than CUs, of waves holding 2 tiles each: the head's state lives in VGPRs
 // (32 floats per lane) for all T tokens and is read and written once per
 // call.  Rows never exchange data, so a head splits across workgroups
 // freely; each part stages the head's k and q and flushes only its own rows'
@@ -23,10 +23,11 @@ namespace {
 // workgroup): the global loads of chunk c+1 are issued before chunk c is
 // computed and written to LDS after it, so their latency hides behind CH
 // tokens of arithmetic.  With DMA, k, q and v go from global memory straight
-// into LDS (global_load_lds_dwordx4) and hold no registers meanwhile.  Outputs overwrite the consumed v entries in LDS (row
-// j's v is read only by row j's lanes, before its output exists) and are
-// flushed to HBM with coalesced 16-byte stores once per chunk.  Two barriers
-// per chunk; none per token.
+// into LDS (global_load_lds_dwordx4) and hold no registers meanwhile.
+// Outputs overwrite the consumed v entries in LDS (row j's v is read only by
+// row j's lanes, before its output exists) and are flushed to HBM with
+// coalesced 16-byte stores once per chunk.  Two barriers per chunk; none per
+// token.
 //
 // Within a chunk the row update is software-pipelined (pass()): the update
 // and output of token t share one sweep over the registers with the decay and
