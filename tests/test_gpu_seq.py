@@ -87,7 +87,7 @@ def repeated_steps(g, si, M):
     outs = []
     for t in range(T):
         tk = {n: dev(x) for n, x in token(si, t).items()}
-        o = torch.empty((B, 32, 128), device="cuda")
+        o = torch.empty(tk["v"].shape, device="cuda")
         g.step(tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], Md, o)
         outs.append(o)
     torch.cuda.synchronize()
@@ -124,6 +124,23 @@ def test_seq_exact_is_bitwise_repeated_step(g, B, T):
     print(f"\n  gdn_seq_exact == repeated gdn_step, B={B} T={T}", flush=True)
     si = gi.step_inputs(3150, 0, B, T=T)
     M = gi.state(3150, 0, B)
+    Ms, os_ = run_seq(g, si, M, exact=True)
+    Md, od = repeated_steps(g, si, M)
+    assert np.array_equal(Md, Ms), "state differs"
+    assert np.array_equal(od, os_), "outputs differ"
+
+
+# other head counts on the many-heads routes (more heads than CUs): 64 value
+# heads per key head group of 16, one head of each kind, 4 value heads per
+# key head
+@pytest.mark.parametrize("B,T,Hv,Hk", [(5, 80, 64, 16), (300, 16, 1, 1), (64, 20, 32, 8)])
+def test_seq_exact_other_head_counts(g, B, T, Hv, Hk):
+    """gdn_seq_exact == T gdn_step calls, bit for bit, with head counts other
+    than the page's on the half-head kernel that fetches its chunks into
+    LDS."""
+    print(f"\n  gdn_seq_exact == repeated gdn_step, B={B} T={T} Hv={Hv} Hk={Hk}", flush=True)
+    si = gi.step_inputs(3170, 0, B, Hv, Hk, T=T)
+    M = gi.state(3170, 0, B, Hv)
     Ms, os_ = run_seq(g, si, M, exact=True)
     Md, od = repeated_steps(g, si, M)
     assert np.array_equal(Md, Ms), "state differs"
