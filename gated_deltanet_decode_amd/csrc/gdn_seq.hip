@@ -10,9 +10,9 @@ namespace {
 
 // -------------------------------------------------------------- gdn_seq
 // One workgroup per (sequence, value head), or per half head for short
-// sequences and for more heads than CUs, of waves holding 2 tiles each: the head's state lives in VGPRs
-// (32 floats per lane) for all T tokens and is read and written once per
-// call.  Rows never exchange data, so a head splits across workgroups
+// sequences and for more heads than CUs, of waves holding 2 tiles each: the
+// head's state lives in VGPRs (32 floats per lane) for all T tokens and is
+// read and written once per call.  Rows never exchange data, so a head splits across workgroups
 // freely; each part stages the head's k and q and flushes only its own rows'
 // outputs.
 //
@@ -75,7 +75,9 @@ struct ChunkRegs {
 
 // Global-to-LDS load of 16 bytes per lane (global_load_lds_dwordx4): lane l's
 // bytes land at dst + 16 l.  dst must be the same in every lane of the wave;
-// the data is in LDS once the wave's vector-memory counter has drained.
+// the data is in LDS once the wave's vector-memory counter has drained
+// (s_waitcnt with kWaitVmcnt0, the gfx9 encoding of vmcnt(0) alone).
+constexpr int kWaitVmcnt0 = 0x0F70;
 __device__ __forceinline__ void load_lds16(const float *src, float *dst) {
     __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)(src),
                                      (__attribute__((address_space(3))) void *)(dst), 16, 0, 0);
@@ -172,8 +174,6 @@ __device__ __forceinline__ void fetch_chunk(ChunkRegs<CH, NTH, DMA> &cr, TokenLd
 // group's rounding differs from the per-token multiply, so its results are
 // not bitwise those of gdn_step.
 constexpr int kScaleGroup = 16;
-// s_waitcnt operand (gfx9 encoding) that waits for vmcnt = 0 only.
-constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr float kMinScale = 0x1p-63f;
 
 // DPP move that keeps `old` in lanes without a source (row shifts).
