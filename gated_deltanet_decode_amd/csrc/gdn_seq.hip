@@ -12,9 +12,9 @@ namespace {
 // One workgroup per (sequence, value head), or per half head for short
 // sequences and for more heads than CUs, of waves holding 2 tiles each: the
 // head's state lives in VGPRs (32 floats per lane) for all T tokens and is
-// read and written once per call.  Rows never exchange data, so a head splits across workgroups
-// freely; each part stages the head's k and q and flushes only its own rows'
-// outputs.
+// read and written once per call.  Rows never exchange data, so a head splits
+// across workgroups freely; each part stages the head's k and q and flushes
+// only its own rows' outputs.
 //
 // The per-token inputs (k, q, v, exp(gate), beta, and for the scaled decay
 // below two per-token factors: 1.5 KiB per token) are
