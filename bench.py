@@ -69,7 +69,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--workload", default="step_b256_x36",
                    choices=["step_b1", "step_b64_x100", "step_b256_x36", "seq_b8_t4096",
-                            "seq_b256_t64", "tail_b32"],
+                            "seq_b256_t64", "seq_b40_t1024", "tail_b32"],
                    help="step_b256_x36 (default): the headline run; the others run only that "
                         "workload's secondary measurement (for profiling)")
     return p.parse_args()
@@ -609,10 +609,13 @@ def extra_measurements(torch, g, stream, only=None):
                                "exact_TFLOPs": upd * D * D * 7 / (ms_exact / 1e3) / 1e12}
 
     # seq_b256_t64: gdn_seq with many heads and a short sequence (B=256 x
-    # T=64 from a seeded state, 4 states in rotation): the half-head route
-    # with 16-token chunks, 3 workgroups per CU
-    if want("seq_b256_t64"):
-        c5 = gi.WORKLOADS["seq_b256_t64"]
+    # T=64 from a seeded state, 4 states in rotation), and seq_b40_t1024:
+    # more heads than CUs and a longer sequence (B=40 x T=1024); both take
+    # the half-head route with 16-token chunks, 3 workgroups per CU
+    for name in ("seq_b256_t64", "seq_b40_t1024"):
+        if not want(name):
+            continue
+        c5 = gi.WORKLOADS[name]
         B, T = c5["B"], c5["T"]
         si = {n: torch.from_numpy(x).cuda() for n, x in gi.step_inputs(c5["seed"], 0, B, T=T).items()}
         sts = [torch.from_numpy(gi.state(c5["seed"], s_, B)).cuda() for s_ in range(4)]
@@ -624,17 +627,20 @@ def extra_measurements(torch, g, stream, only=None):
             k[0] += 1
             g.seq(si["q"], si["k"], si["v"], si["beta"], si["gate"], sts[i], o, stream=stream,
                   exact=exact)
-        ms = min(timeit(lambda: rot(False), 8) for _ in range(3))
-        ms_x = min(timeit(lambda: rot(True), 8) for _ in range(3))
+        reps = 8 if T <= 64 else 3
+        ms = min(timeit(lambda: rot(False), reps) for _ in range(3))
+        ms_x = min(timeit(lambda: rot(True), reps) for _ in range(3))
         upd = B * T * HV
         tf = upd * D * D * 7 / (ms / 1e3) / 1e12
-        res["seq_b256_t64"] = {"ms": ms, "state_updates_per_s": upd / (ms / 1e3),
-                               "TFLOPs": tf, "flop_per_element": 7,
-                               "frac_fp32_vector_nonpacked_78.6": tf / 78.6,
-                               "state_GBps": B * HV * 2 * D * D * 4 / (ms / 1e3) / 1e9,
-                               "exact_ms": ms_x,
-                               "exact_TFLOPs": upd * D * D * 7 / (ms_x / 1e3) / 1e12}
-        del sts
+        res[name] = {"ms": ms, "state_updates_per_s": upd / (ms / 1e3),
+                     "TFLOPs": tf, "flop_per_element": 7,
+                     "frac_fp32_vector_nonpacked_78.6": tf / 78.6,
+                     # executed with the scaled decay: 6 flop per element
+                     "executed_TFLOPs_6_flop_per_element": tf * 6 / 7,
+                     "state_GBps": B * HV * 2 * D * D * 4 / (ms / 1e3) / 1e9,
+                     "exact_ms": ms_x,
+                     "exact_TFLOPs": upd * D * D * 7 / (ms_x / 1e3) / 1e12}
+        del sts, si, o
 
     # tail_b32: layer tail B=32
     if want("tail_b32"):

@@ -71,6 +71,9 @@ WORKLOADS = {
     # gdn_seq with many heads and a short sequence: 256 sequences x 64 tokens
     # from seeded states (a secondary line, not one of the five configs)
     "seq_b256_t64": dict(B=256, T=64, seed=1005),
+    # gdn_seq with more heads than compute units and a longer sequence: 40
+    # sequences x 1024 tokens from seeded states (a secondary line)
+    "seq_b40_t1024": dict(B=40, T=1024, seed=1006),
 }
 
 

@@ -10,6 +10,8 @@ by layer).
   seq_b8_t4096:  gdn_seq B=8 x T=4096 from a zero state
   seq_b256_t64:  gdn_seq B=256 x T=64 from seeded states (the benchmark's
                  many-heads short-sequence line)
+  seq_b40_t1024: gdn_seq B=40 x T=1024 from seeded states (the benchmark's
+                 many-heads long-sequence line; 8 of the sequences checked)
 """
 import numpy as np
 import pytest
@@ -231,3 +233,41 @@ def test_seq_b256_t64(g, orc, workload):
         ref.assert_close(f"{tag} out", og, want, 1e-5)
         ref.assert_vs_f64(f"{tag} state[:8]", Mg[:8], Mo8, M64)
         ref.assert_vs_f64(f"{tag} out[:8]", og[:8], want8, out64)
+
+
+@pytest.mark.timeout(600)
+def test_seq_b40_t1024(g, orc, workload):
+    """gdn_seq at the benchmark's B=40 x T=1024 (1280 heads: half heads with
+    their chunks fetched into LDS, three workgroups per CU), the whole batch
+    in one launch; sequences 0-3 and 36-39 against the oracle, every element,
+    and the binary64 yardstick on two of them; gdn_seq_exact likewise."""
+    import torch
+    workload("seq_b40_t1024")
+    c = gi.WORKLOADS["seq_b40_t1024"]
+    B, T = c["B"], c["T"]
+    print(f"\n  seq_b40_t1024: gdn_seq and gdn_seq_exact B={B} T={T}", flush=True)
+    si = gi.step_inputs(c["seed"], 0, B, T=T)
+    M = gi.state(c["seed"], 0, B)
+    t = {n: dev(x) for n, x in si.items()}
+    res = {}
+    for exact in (False, True):
+        Md = dev(M)
+        out = torch.empty((B, T, 32, 128), device="cuda")
+        g.seq(t["q"], t["k"], t["v"], t["beta"], t["gate"], Md, out, exact=exact)
+        torch.cuda.synchronize()
+        res[exact] = (Md.cpu().numpy(), out.cpu().numpy())
+        del Md, out
+    del t
+    pick = np.r_[0:4, B - 4:B]
+    sp = {n: np.ascontiguousarray(x[pick]) for n, x in si.items()}
+    Mo = M[pick].copy()
+    want = ref.seq_mt(orc, sp, Mo)
+    s2 = {n: np.ascontiguousarray(x[[0, B - 1]]) for n, x in si.items()}
+    M64 = M[[0, B - 1]].astype(np.float64)
+    out64 = ref.seq_f64_mt(orc, s2, M64)
+    for exact, tag in ((False, "seq"), (True, "seq_exact")):
+        Mg, og = res[exact]
+        ref.assert_close(f"{tag} state", Mg[pick], Mo, 1e-4)
+        ref.assert_close(f"{tag} out", og[pick], want, 1e-4)
+        ref.assert_vs_f64(f"{tag} state[0,-1]", Mg[[0, B - 1]], Mo[[0, -1]], M64)
+        ref.assert_vs_f64(f"{tag} out[0,-1]", og[[0, B - 1]], want[[0, -1]], out64)
