@@ -602,6 +602,7 @@ def extra_measurements(torch, g, stream, only=None):
                                "frac_fp32_vector_nonpacked_78.6": tf / 78.6,
                                "frac_fp32_vector_157.3": tf / 157.3,
                                "executed_TFLOPs_6_flop_per_element": tf6,
+                               "executed_frac_fp32_vector_nonpacked_78.6": tf6 / 78.6,
                                "fma_probe_TFLOPs_8_waves_per_cu": probe8,
                                "fma_probe_TFLOPs_16_waves_per_cu": probe16,
                                "executed_frac_of_fma_probe_same_occupancy": tf6 / probe8,
@@ -637,6 +638,7 @@ def extra_measurements(torch, g, stream, only=None):
                      "frac_fp32_vector_nonpacked_78.6": tf / 78.6,
                      # executed with the scaled decay: 6 flop per element
                      "executed_TFLOPs_6_flop_per_element": tf * 6 / 7,
+                     "executed_frac_fp32_vector_nonpacked_78.6": tf * 6 / 7 / 78.6,
                      "state_GBps": B * HV * 2 * D * D * 4 / (ms / 1e3) / 1e9,
                      "exact_ms": ms_x,
                      "exact_TFLOPs": upd * D * D * 7 / (ms_x / 1e3) / 1e12}
